@@ -1,0 +1,301 @@
+"""Python binding of the drafting-step library (``libdflash.so``, C ABI in ``include/dflash.h``).
+
+Thin by design: the functions below carry the C calls' names and do argument
+marshalling only (tensors -> device pointers, the current torch stream -> a HIP
+stream, status codes -> exceptions).  Every step of the computation runs in the
+library's HIP kernels.  PyTorch provides device memory and streams.
+
+The library must have been built (``python -m block_diffusion_drafter_feature_amd.build``
+or ``__graft_entry__.build()``); importing this package does not build it and
+there is no fallback: without the library every call raises.
+
+Helpers ``Drafter`` (device weights + the config/weights structs), ``KVCache`` and
+``Workspace`` only allocate and lay out memory.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libdflash.so")
+
+DFLASH_OK = 0
+DFLASH_E_INVAL = -1
+DFLASH_E_UNSUPPORTED = -2
+DFLASH_E_WORKSPACE = -3
+DFLASH_E_CAPACITY = -4
+DFLASH_E_HIP = -5
+DFLASH_F32 = 0
+DFLASH_BF16 = 1
+DFLASH_PATH_GREEDY = 0
+DFLASH_PATH_EXACT = 1
+MAX_LAYERS = 16
+CONV_SITES = 4
+
+EXPORTED = (
+    "dflash_inject_context", "dflash_draft_block", "dflash_select_path", "dflash_verify",
+    "dflash_inject_workspace_bytes", "dflash_draft_workspace_bytes", "dflash_path_workspace_bytes",
+    "dflash_verify_workspace_bytes", "dflash_check_config", "dflash_status_string",
+)
+
+
+class DflashError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: status {status} ({status_string(status)})")
+        self.status = status
+
+
+# ------------------------------------------------------------------ C structs
+
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+
+
+class dflash_config(ctypes.Structure):
+    _fields_ = [("dtype", _i32), ("d_model", _i32), ("n_heads", _i32), ("n_kv_heads", _i32),
+                ("head_dim", _i32), ("d_ffn", _i32), ("n_layers", _i32), ("n_feat_layers", _i32),
+                ("d_target", _i32), ("vocab", _i32), ("ps_dim", _i32), ("ps_rank", _i32),
+                ("use_conv", _i32), ("use_gate", _i32), ("rms_eps", ctypes.c_float),
+                ("rope_theta", ctypes.c_float)]
+
+
+class dflash_layer_weights(ctypes.Structure):
+    _fields_ = [("w_q", _vp), ("w_k", _vp), ("w_v", _vp), ("w_o", _vp), ("w_gate", _vp), ("w_up", _vp),
+                ("w_down", _vp), ("g_attn", _vp), ("g_ffn", _vp), ("conv_gen", _vp * CONV_SITES),
+                ("conv_w0", _vp * CONV_SITES), ("conv_w1", _vp * CONV_SITES)]
+
+
+class dflash_weights(ctypes.Structure):
+    _fields_ = [("embed", _vp), ("lm_head", _vp), ("w_fc", _vp), ("g_fc", _vp), ("g_final", _vp),
+                ("ps_left", _vp), ("ps_right", _vp), ("ps_gate", _vp), ("ps_u", _vp), ("ps_v", _vp),
+                ("layers", dflash_layer_weights * MAX_LAYERS)]
+
+
+class dflash_kv(ctypes.Structure):
+    _fields_ = [("k", _vp * MAX_LAYERS), ("vt", _vp * MAX_LAYERS), ("batch", _i32), ("cap", _i32)]
+
+
+# ------------------------------------------------------------------ library loading
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises when it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_diffusion_drafter_feature_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, PC = ctypes.POINTER, ctypes.c_size_t
+        cfgp, wp, kvp = P(dflash_config), P(dflash_weights), P(dflash_kv)
+        sig = {
+            "dflash_inject_context": ([cfgp, wp, kvp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, PC, _vp], ctypes.c_int),
+            "dflash_draft_block": ([cfgp, wp, kvp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
+            "dflash_select_path": ([cfgp, wp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, PC, _vp],
+                                   ctypes.c_int),
+            "dflash_verify": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
+            "dflash_inject_workspace_bytes": ([cfgp, _i32], PC),
+            "dflash_draft_workspace_bytes": ([cfgp, _i32, _i32], PC),
+            "dflash_path_workspace_bytes": ([cfgp, _i32], PC),
+            "dflash_verify_workspace_bytes": ([_i32, _i32, _i32], PC),
+            "dflash_check_config": ([cfgp], ctypes.c_int),
+            "dflash_status_string": ([ctypes.c_int], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+def _ptr(x) -> Optional[int]:
+    """Device pointer of a tensor (or an int / None passed through)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, status: int) -> None:
+    if status != DFLASH_OK:
+        raise DflashError(fn, status)
+
+
+def status_string(status: int) -> str:
+    return lib().dflash_status_string(status).decode()
+
+
+# ------------------------------------------------------------------ the calls (same names as the C ABI)
+
+def dflash_check_config(cfg: dflash_config) -> int:
+    return lib().dflash_check_config(ctypes.byref(cfg))
+
+
+def dflash_inject_workspace_bytes(cfg: dflash_config, n_rows: int) -> int:
+    return lib().dflash_inject_workspace_bytes(ctypes.byref(cfg), n_rows)
+
+
+def dflash_draft_workspace_bytes(cfg: dflash_config, batch: int, cap: int) -> int:
+    return lib().dflash_draft_workspace_bytes(ctypes.byref(cfg), batch, cap)
+
+
+def dflash_path_workspace_bytes(cfg: dflash_config, batch: int) -> int:
+    return lib().dflash_path_workspace_bytes(ctypes.byref(cfg), batch)
+
+
+def dflash_verify_workspace_bytes(batch: int, n_draft: int, vocab: int) -> int:
+    return lib().dflash_verify_workspace_bytes(batch, n_draft, vocab)
+
+
+def dflash_inject_context(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, workspace_bytes,
+                          stream=None) -> None:
+    _check("dflash_inject_context", lib().dflash_inject_context(
+        ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), _ptr(hidden), n_rows, _ptr(row_off), _ptr(pos0),
+        _ptr(n_new), batch, _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def dflash_draft_block(cfg, w, kv, ctx_len, block_ids, batch, cand_ids, cand_logits, final_hidden, logits,
+                       workspace, workspace_bytes, stream=None) -> None:
+    _check("dflash_draft_block", lib().dflash_draft_block(
+        ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), _ptr(ctx_len), _ptr(block_ids), batch,
+        _ptr(cand_ids), _ptr(cand_logits), _ptr(final_hidden), _ptr(logits), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def dflash_select_path(cfg, w, cand_ids, cand_logits, final_hidden, block_ids, n_fixed, mode, batch, path_idx,
+                       path_ids, pair_scores, workspace, workspace_bytes, stream=None) -> None:
+    _check("dflash_select_path", lib().dflash_select_path(
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(cand_ids), _ptr(cand_logits), _ptr(final_hidden), _ptr(block_ids),
+        n_fixed, mode, batch, _ptr(path_idx), _ptr(path_ids), _ptr(pair_scores), _ptr(workspace), workspace_bytes,
+        _stream(stream)))
+
+
+def dflash_verify(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_len, bonus, workspace,
+                  workspace_bytes, stream=None) -> None:
+    _check("dflash_verify", lib().dflash_verify(
+        _ptr(draft), _ptr(tgt_logits), tgt_dtype, batch, n_draft, vocab, _ptr(accept_len), _ptr(bonus),
+        _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+# ------------------------------------------------------------------ memory helpers (allocation / layout only)
+
+def make_config(dims) -> dflash_config:
+    """A ``dflash_config`` from an object with the attributes of ``synth.Dims``."""
+    return dflash_config(
+        dtype=DFLASH_BF16 if dims.dtype == "bf16" else DFLASH_F32, d_model=dims.d, n_heads=dims.n_heads,
+        n_kv_heads=dims.n_kv_heads, head_dim=dims.head_dim, d_ffn=dims.d_ffn, n_layers=dims.n_layers,
+        n_feat_layers=dims.n_feat_layers, d_target=dims.d_target, vocab=dims.vocab, ps_dim=dims.ps_dim,
+        ps_rank=dims.ps_rank, use_conv=int(dims.use_conv), use_gate=int(dims.use_gate),
+        rms_eps=dims.rms_eps, rope_theta=dims.rope_theta)
+
+
+def torch_dtype(dims):
+    import torch
+    return torch.bfloat16 if dims.dtype == "bf16" else torch.float32
+
+
+def to_device(arr, dims, device="cuda"):
+    """Upload a stored array (bf16 bit patterns as uint16, or float32) as a device tensor."""
+    import numpy as np
+    import torch
+    a = np.ascontiguousarray(arr)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(a).to(device)
+
+
+class Drafter:
+    """Device copies of a drafter's weights and the structs that point at them."""
+
+    def __init__(self, dims, weights: Dict[str, "object"], device: str = "cuda"):
+        self.dims = dims
+        self.t = {k: to_device(v, dims, device) for k, v in weights.items()}
+        self.cfg = make_config(dims)
+        st = dflash_check_config(self.cfg)
+        if st != DFLASH_OK:
+            raise DflashError("dflash_check_config", st)
+        w = dflash_weights()
+        p = lambda k: self.t[k].data_ptr() if k in self.t else None  # noqa: E731
+        for k in ("embed", "lm_head", "w_fc", "g_fc", "g_final", "ps_left", "ps_right", "ps_gate", "ps_u", "ps_v"):
+            setattr(w, k, p(k))
+        for l in range(dims.n_layers):
+            L = w.layers[l]
+            for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down", "g_attn", "g_ffn"):
+                setattr(L, k, p(f"l{l}.{k}"))
+            if dims.use_conv:
+                for s in range(CONV_SITES):
+                    L.conv_gen[s] = p(f"l{l}.conv{s}.gen")
+                    L.conv_w0[s] = p(f"l{l}.conv{s}.w0")
+                    L.conv_w1[s] = p(f"l{l}.conv{s}.w1")
+        self.w = w
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.t.values())
+
+
+class KVCache:
+    """Per-layer key cache ``[B][Hkv][cap][hd]`` and transposed value cache ``[B][Hkv][hd][cap]``."""
+
+    def __init__(self, dims, batch: int, cap: int, device: str = "cuda", fill: Optional[float] = 0.0):
+        import torch
+        if cap % 32:
+            raise ValueError("cap must be a multiple of 32")
+        dt = torch_dtype(dims)
+        shp = (batch, dims.n_kv_heads, cap, dims.head_dim)
+        shpt = (batch, dims.n_kv_heads, dims.head_dim, cap)
+        if fill is None:
+            self.k = [torch.empty(shp, dtype=dt, device=device) for _ in range(dims.n_layers)]
+            self.vt = [torch.empty(shpt, dtype=dt, device=device) for _ in range(dims.n_layers)]
+        else:
+            self.k = [torch.full(shp, fill, dtype=dt, device=device) for _ in range(dims.n_layers)]
+            self.vt = [torch.full(shpt, fill, dtype=dt, device=device) for _ in range(dims.n_layers)]
+        self.dims, self.batch, self.cap = dims, batch, cap
+        kv = dflash_kv(batch=batch, cap=cap)
+        for l in range(dims.n_layers):
+            kv.k[l] = self.k[l].data_ptr()
+            kv.vt[l] = self.vt[l].data_ptr()
+        self.kv = kv
+
+    def load_logical(self, K, V) -> None:
+        """Copy caches given as ``[L][B][Hkv][cap][hd]`` stored arrays into the device layout."""
+        for l in range(self.dims.n_layers):
+            self.k[l].copy_(to_device(K[l], self.dims))
+            self.vt[l].copy_(to_device(V[l], self.dims).transpose(-1, -2))
+
+    def logical(self, layer: int):
+        """(K, V) of one layer as ``[B][Hkv][cap][hd]`` device tensors (V transposed back)."""
+        return self.k[layer], self.vt[layer].transpose(-1, -2)
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in self.k + self.vt)
+
+
+class Workspace:
+    """A device byte buffer that grows to the largest size asked for."""
+
+    def __init__(self, device: str = "cuda"):
+        self.device = device
+        self.buf = None
+
+    def get(self, nbytes: int):
+        import torch
+        if nbytes <= 0:
+            raise DflashError("workspace size query", DFLASH_E_INVAL)
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
+        return self.buf

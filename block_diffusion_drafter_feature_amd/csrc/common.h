@@ -1,0 +1,171 @@
+// Device-side building blocks shared by the gfx950 kernels of the drafting step.
+//
+// Storage types: bf16 (bit patterns in uint16_t) or fp32.  GEMM operands are fed
+// to the CDNA4 matrix cores as "fragments": 8 consecutive K elements per lane.
+// A 64-lane wave therefore covers 4 lane groups x 8 = 32 K elements per
+// fragment.  For bf16 one fragment is one v_mfma_f32_16x16x32_bf16; for fp32 it
+// is eight v_mfma_f32_16x16x4_f32, fragment element j of lane group g being the
+// K slot g of the j-th instruction.  Both A and B operands use the same
+// (group, element) -> K mapping, so any consistent assignment of K indices to
+// (group, element) gives the same contraction.
+//
+// Output layout of a 16x16 MFMA tile: lane l holds rows 4*(l/16)+i (i=0..3) of
+// column l%16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dflash {
+
+typedef uint16_t bf16_t;
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------------ conversions
+
+__device__ __forceinline__ float bf2f(bf16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// float -> bf16, round to nearest, ties to even (NaN kept quiet).
+__device__ __forceinline__ bf16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float to_f(T v);
+template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ float to_f<bf16_t>(bf16_t v) { return bf2f(v); }
+
+template <typename T> __device__ __forceinline__ T from_f(float v);
+template <> __device__ __forceinline__ float from_f<float>(float v) { return v; }
+template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f2bf(v); }
+
+// round-trip through the storage type (identity for fp32)
+template <typename T> __device__ __forceinline__ float round_to(float v) { return to_f<T>(from_f<T>(v)); }
+
+// ------------------------------------------------------------------ fragments
+
+template <typename T> struct Frag;
+
+template <> struct Frag<bf16_t> {
+  typedef bf16x8_t type;
+  __device__ __forceinline__ static type zero() {
+    u32x4_t z = {0u, 0u, 0u, 0u};
+    return __builtin_bit_cast(type, z);
+  }
+  __device__ __forceinline__ static type load(const bf16_t* p) {
+    return __builtin_bit_cast(type, *reinterpret_cast<const u32x4_t*>(p));
+  }
+  // load 8 floats and round them to bf16
+  __device__ __forceinline__ static type load_f32(const float* p) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+    u32x4_t r;
+    r[0] = static_cast<uint32_t>(f2bf(a[0])) | (static_cast<uint32_t>(f2bf(a[1])) << 16);
+    r[1] = static_cast<uint32_t>(f2bf(a[2])) | (static_cast<uint32_t>(f2bf(a[3])) << 16);
+    r[2] = static_cast<uint32_t>(f2bf(b[0])) | (static_cast<uint32_t>(f2bf(b[1])) << 16);
+    r[3] = static_cast<uint32_t>(f2bf(b[2])) | (static_cast<uint32_t>(f2bf(b[3])) << 16);
+    return __builtin_bit_cast(type, r);
+  }
+  __device__ __forceinline__ static type from_floats(const float* v) {
+    u32x4_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      r[j] = static_cast<uint32_t>(f2bf(v[2 * j])) | (static_cast<uint32_t>(f2bf(v[2 * j + 1])) << 16);
+    return __builtin_bit_cast(type, r);
+  }
+  __device__ __forceinline__ static f32x4_t mma(f32x4_t acc, type a, type b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+  }
+  // zero element j (0..7) when !keep
+  __device__ __forceinline__ static type mask(type v, uint32_t keep_bits) {
+    u32x4_t r = __builtin_bit_cast(u32x4_t, v);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      uint32_t m = ((keep_bits >> (2 * j)) & 1u ? 0x0000ffffu : 0u) | ((keep_bits >> (2 * j + 1)) & 1u ? 0xffff0000u : 0u);
+      r[j] &= m;
+    }
+    return __builtin_bit_cast(type, r);
+  }
+};
+
+template <> struct Frag<float> {
+  typedef f32x8_t type;
+  __device__ __forceinline__ static type zero() {
+    type z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    return z;
+  }
+  __device__ __forceinline__ static type load(const float* p) {
+    const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
+    const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
+    type r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return r;
+  }
+  __device__ __forceinline__ static type load_f32(const float* p) { return load(p); }
+  __device__ __forceinline__ static type from_floats(const float* v) {
+    type r = {v[0], v[1], v[2], v[3], v[4], v[5], v[6], v[7]};
+    return r;
+  }
+  __device__ __forceinline__ static f32x4_t mma(f32x4_t acc, type a, type b) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], acc, 0, 0, 0);
+    return acc;
+  }
+  __device__ __forceinline__ static type mask(type v, uint32_t keep_bits) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = ((keep_bits >> j) & 1u) ? v[j] : 0.f;
+    return v;
+  }
+};
+
+// ------------------------------------------------------------------ rotary encoding
+
+// cos/sin of the rotary angle pos * theta^(-2i/hd).  The angle is formed and
+// reduced to [-pi, pi] in double precision (context positions reach 10^5 and a
+// float angle would be off by ~1e-2 rad there), then evaluated in float.
+__device__ __forceinline__ void rope_cs(int pos, int i, int hd, float theta, float* c, float* s) {
+  const double inv = exp(-(2.0 * i / hd) * log(static_cast<double>(theta)));
+  double a = static_cast<double>(pos) * inv;
+  const double two_pi = 6.283185307179586476925286766559;
+  a -= two_pi * rint(a / two_pi);
+  sincosf(static_cast<float>(a), s, c);
+}
+
+// ------------------------------------------------------------------ wave reductions
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// deterministic block-wide sum (fixed reduction tree); `red` holds >= nwaves floats
+__device__ __forceinline__ float block_sum(float v, float* red) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += red[i];
+  return t;
+}
+
+// (value, index) order used by every selection: larger value first, then lower index
+__device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+}  // namespace dflash

@@ -1,0 +1,513 @@
+// C ABI of the drafting step: argument checks, workspace carving and the launch
+// sequence of each call.  Every call validates all of its arguments before the
+// first launch, then enqueues its kernels on the caller's stream and returns.
+#include "dflash.h"
+
+#include "attention.h"
+#include "common.h"
+#include "elementwise.h"
+#include "epilogues.h"
+#include "gemm.h"
+#include "select.h"
+
+using namespace dflash;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kTopkChunk = 4096;     // vocabulary columns per top-k work-group
+constexpr int kArgmaxChunk = 8192;   // vocabulary columns per argmax work-group
+
+size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
+
+// Carves typed slices out of the caller's workspace; with base == nullptr it only
+// adds up the sizes (the *_workspace_bytes queries use the same code).
+struct Carver {
+  char* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <typename X>
+  X* take(size_t n) {
+    X* p = base ? reinterpret_cast<X*>(base + off) : nullptr;
+    off += align_up(n * sizeof(X));
+    return p;
+  }
+};
+
+size_t esize(const dflash_config* c) { return c->dtype == DFLASH_BF16 ? 2 : 4; }
+
+int check_config(const dflash_config* c) {
+  if (!c) return DFLASH_E_INVAL;
+  if (c->dtype != DFLASH_BF16 && c->dtype != DFLASH_F32) return DFLASH_E_INVAL;
+  if (c->d_model <= 0 || c->n_heads <= 0 || c->n_kv_heads <= 0 || c->head_dim <= 0 || c->d_ffn <= 0 ||
+      c->n_layers <= 0 || c->n_feat_layers <= 0 || c->d_target <= 0 || c->vocab <= 0 || c->ps_dim <= 0 ||
+      c->ps_rank <= 0)
+    return DFLASH_E_INVAL;
+  if (!(c->rms_eps >= 0.f) || !(c->rope_theta > 0.f) || (c->use_conv != 0 && c->use_conv != 1) ||
+      (c->use_gate != 0 && c->use_gate != 1))
+    return DFLASH_E_INVAL;
+  if (c->n_layers > DFLASH_MAX_LAYERS) return DFLASH_E_UNSUPPORTED;
+  if (c->d_model % 64 || c->d_ffn % 64) return DFLASH_E_UNSUPPORTED;
+  if (static_cast<int64_t>(c->n_feat_layers) * c->d_target % 64) return DFLASH_E_UNSUPPORTED;
+  if (static_cast<int64_t>(c->n_feat_layers) * c->d_target > (1 << 28)) return DFLASH_E_UNSUPPORTED;
+  if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_E_UNSUPPORTED;
+  if (c->n_heads % c->n_kv_heads) return DFLASH_E_UNSUPPORTED;
+  const int G = c->n_heads / c->n_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return DFLASH_E_UNSUPPORTED;
+  if (c->vocab % 16 || c->vocab < 16) return DFLASH_E_UNSUPPORTED;
+  if (c->ps_dim % 64 || c->ps_rank > 256) return DFLASH_E_UNSUPPORTED;
+  return DFLASH_OK;
+}
+
+int check_weights(const dflash_config* c, const dflash_weights* w, bool draft, bool inject, bool path) {
+  if (!w) return DFLASH_E_INVAL;
+  if (draft && (!w->embed || !w->lm_head || !w->g_final)) return DFLASH_E_INVAL;
+  if (inject && (!w->w_fc || !w->g_fc)) return DFLASH_E_INVAL;
+  if (path && (!w->embed || !w->ps_left || !w->ps_right || !w->ps_u || !w->ps_v)) return DFLASH_E_INVAL;
+  if (path && c->use_gate && !w->ps_gate) return DFLASH_E_INVAL;
+  for (int l = 0; l < c->n_layers; ++l) {
+    const dflash_layer_weights& L = w->layers[l];
+    if ((draft || inject) && (!L.w_k || !L.w_v)) return DFLASH_E_INVAL;
+    if (draft && (!L.w_q || !L.w_o || !L.w_gate || !L.w_up || !L.w_down || !L.g_attn || !L.g_ffn))
+      return DFLASH_E_INVAL;
+    if (draft && c->use_conv)
+      for (int s = 0; s < DFLASH_CONV_SITES; ++s)
+        if (!L.conv_gen[s] || !L.conv_w0[s] || !L.conv_w1[s]) return DFLASH_E_INVAL;
+  }
+  return DFLASH_OK;
+}
+
+int check_kv(const dflash_config* c, const dflash_kv* kv, int batch) {
+  if (!kv || kv->cap <= 0 || kv->batch <= 0) return DFLASH_E_INVAL;
+  if (kv->cap % 32) return DFLASH_E_UNSUPPORTED;
+  if (batch > kv->batch) return DFLASH_E_CAPACITY;
+  for (int l = 0; l < c->n_layers; ++l)
+    if (!kv->k[l] || !kv->vt[l]) return DFLASH_E_INVAL;
+  return DFLASH_OK;
+}
+
+// ------------------------------------------------------------------ workspace layouts
+
+template <typename T>
+struct InjectWs {
+  float* hf;   // [rows][d] fused feature before its norm
+  T* f;        // [rows][d] fused feature, storage type
+};
+template <typename T>
+InjectWs<T> carve_inject(Carver& cv, const dflash_config* c, int rows) {
+  InjectWs<T> w;
+  w.hf = cv.take<float>(static_cast<size_t>(rows) * c->d_model);
+  w.f = cv.take<T>(static_cast<size_t>(rows) * c->d_model);
+  return w;
+}
+
+int attn_splits(const dflash_config* c, int batch, int cap) {
+  const int want = (512 + batch * c->n_kv_heads - 1) / (batch * c->n_kv_heads);
+  const int maxs = (cap + 255) / 256;
+  int s = want < maxs ? want : maxs;
+  return s < 1 ? 1 : (s > 64 ? 64 : s);
+}
+
+template <typename T>
+struct DraftWs {
+  float* x;       // [M][d] residual stream
+  float* uf;      // [M][max(d)] normed (or post-GEMM) rows before the conv, fp32
+  T* ut;          // [M][d] GEMM operand
+  T* q;           // [M][H*hd]
+  T* kb;          // [B][Hkv][16][hd]
+  T* vbt;         // [B][Hkv][hd][16]
+  float* part_o;  // [B][Hkv][S][G][16][hd]
+  float* part_ml;
+  T* o;           // [M][H*hd]
+  float* delta;   // [M][2*d/16]
+  T* h;           // [M][d_ffn]
+  float* logits;  // [M][V] (when the caller passes none)
+  float* tk_v;    // [M][n_chunks][16]
+  int32_t* tk_i;
+  int S;
+};
+template <typename T>
+DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
+  DraftWs<T> w;
+  const size_t M = 16 * static_cast<size_t>(B), d = c->d_model, hq = static_cast<size_t>(c->n_heads) * c->head_dim;
+  const int G = c->n_heads / c->n_kv_heads;
+  w.S = attn_splits(c, B, cap);
+  const int nch = (c->vocab + kTopkChunk - 1) / kTopkChunk;
+  w.x = cv.take<float>(M * d);
+  w.uf = cv.take<float>(M * d);
+  w.ut = cv.take<T>(M * d);
+  w.q = cv.take<T>(M * hq);
+  w.kb = cv.take<T>(static_cast<size_t>(B) * c->n_kv_heads * 16 * c->head_dim);
+  w.vbt = cv.take<T>(static_cast<size_t>(B) * c->n_kv_heads * 16 * c->head_dim);
+  w.part_o = cv.take<float>(static_cast<size_t>(B) * c->n_kv_heads * w.S * G * 16 * c->head_dim);
+  w.part_ml = cv.take<float>(static_cast<size_t>(B) * c->n_kv_heads * w.S * G * 16 * 2);
+  w.o = cv.take<T>(M * hq);
+  w.delta = cv.take<float>(M * 2 * (d / 16));
+  w.h = cv.take<T>(M * c->d_ffn);
+  w.logits = cv.take<float>(M * c->vocab);
+  w.tk_v = cv.take<float>(M * nch * 16);
+  w.tk_i = cv.take<int32_t>(M * nch * 16);
+  return w;
+}
+
+constexpr int kPathSlots = 16 * 16 + 1;
+
+struct PathWs {
+  int32_t* tokens;  // [B][T]
+  float* z;         // [B][T][2*PD]
+  float* gamma;     // [B*16][PD]
+  float* lam;       // [B][T][r]
+  float* rho;       // [B][T][r]
+};
+PathWs carve_path(Carver& cv, const dflash_config* c, int B) {
+  PathWs w;
+  const size_t T = kPathSlots;
+  w.tokens = cv.take<int32_t>(B * T);
+  w.z = cv.take<float>(B * T * 2 * c->ps_dim);
+  w.gamma = cv.take<float>(static_cast<size_t>(B) * 16 * c->ps_dim);
+  w.lam = cv.take<float>(B * T * c->ps_rank);
+  w.rho = cv.take<float>(B * T * c->ps_rank);
+  return w;
+}
+
+struct VerifyWs {
+  float* pv;
+  int32_t* pi;
+};
+VerifyWs carve_verify(Carver& cv, int B, int n_draft, int V) {
+  VerifyWs w;
+  const size_t nch = (V + kArgmaxChunk - 1) / kArgmaxChunk;
+  w.pv = cv.take<float>(static_cast<size_t>(B) * (n_draft + 1) * nch);
+  w.pi = cv.take<int32_t>(static_cast<size_t>(B) * (n_draft + 1) * nch);
+  return w;
+}
+
+#define LAUNCH_CHECK()                             \
+  do {                                             \
+    if (hipGetLastError() != hipSuccess) return DFLASH_E_HIP; \
+  } while (0)
+#define GEMM_CHECK(expr)                           \
+  do {                                             \
+    if ((expr) != hipSuccess) return DFLASH_E_HIP; \
+  } while (0)
+
+template <typename T>
+SegW<T> seg1(const void* p, int rows, int K) {
+  SegW<T> s{};
+  s.p[0] = static_cast<const T*>(p);
+  s.off[0] = 0;
+  s.off[1] = rows;
+  s.n_seg = 1;
+  s.K = K;
+  return s;
+}
+
+// ------------------------------------------------------------------ inject
+
+template <typename T>
+int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv* kv, const void* hidden,
+                int rows, const int32_t* row_off, const int32_t* pos0, const int32_t* n_new, int B, void* ws,
+                hipStream_t s) {
+  Carver cv(ws);
+  InjectWs<T> W = carve_inject<T>(cv, c, rows);
+  const int d = c->d_model, dcat = c->n_feat_layers * c->d_target;
+  {
+    EpiStore<T> e{seg1<T>(w->w_fc, d, dcat), W.hf, d, STORE};
+    GEMM_CHECK((run_gemm<T, T>(static_cast<const T*>(hidden), dcat, nullptr, rows, dcat, (d + 15) / 16, e, s)));
+  }
+  rmsnorm_kernel<T><<<rows, 256, 0, s>>>(W.hf, static_cast<const T*>(w->g_fc), d, c->rms_eps, W.f, nullptr);
+  LAUNCH_CHECK();
+  EpiInject<T> e{};
+  for (int l = 0; l < c->n_layers; ++l) {
+    e.wk[l] = static_cast<const T*>(w->layers[l].w_k);
+    e.wv[l] = static_cast<const T*>(w->layers[l].w_v);
+    e.kc[l] = static_cast<T*>(kv->k[l]);
+    e.vtc[l] = static_cast<T*>(kv->vt[l]);
+  }
+  e.K = d;
+  e.L = c->n_layers;
+  e.Hkv = c->n_kv_heads;
+  e.hd = c->head_dim;
+  e.B = B;
+  e.cap = kv->cap;
+  e.theta = c->rope_theta;
+  e.row_off = row_off;
+  e.pos0 = pos0;
+  e.n_new = n_new;
+  const int nvt = c->n_layers * 2 * c->n_kv_heads * c->head_dim / 16;
+  GEMM_CHECK((run_gemm<T, T>(W.f, d, nullptr, rows, d, nvt, e, s)));
+  return DFLASH_OK;
+}
+
+// ------------------------------------------------------------------ draft
+
+template <typename T, int HD, int G>
+hipError_t launch_attn(const AttnArgs<T>& a, int B, hipStream_t s) {
+  constexpr int HW = G < 2 ? G : 2;
+  dim3 grid(a.S, a.Hkv, B);
+  block_attn_kernel<T, HD, G, HW><<<grid, 64 * (G / HW), 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <typename T>
+hipError_t run_attention(const dflash_config* c, const AttnArgs<T>& a, int B, T* out, hipStream_t s) {
+  const int G = c->n_heads / c->n_kv_heads;
+  hipError_t e;
+  if (c->head_dim == 64) {
+    e = G == 1 ? launch_attn<T, 64, 1>(a, B, s) : G == 2 ? launch_attn<T, 64, 2>(a, B, s) : launch_attn<T, 64, 4>(a, B, s);
+  } else {
+    e = G == 1 ? launch_attn<T, 128, 1>(a, B, s) : G == 2 ? launch_attn<T, 128, 2>(a, B, s) : launch_attn<T, 128, 4>(a, B, s);
+  }
+  if (e != hipSuccess) return e;
+  dim3 grid(c->n_heads, B);
+  if (c->head_dim == 64) attn_combine_kernel<T, 64><<<grid, 256, 0, s>>>(a.part_o, a.part_ml, out, c->n_heads, c->n_kv_heads, a.S);
+  else attn_combine_kernel<T, 128><<<grid, 256, 0, s>>>(a.part_o, a.part_ml, out, c->n_heads, c->n_kv_heads, a.S);
+  return hipGetLastError();
+}
+
+// pre-sublayer input: u = RMSNorm(x; g), conv'd when enabled, rounded to T into W.ut
+template <typename T>
+int pre_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site, const void* gain, int M,
+                 DraftWs<T>& W, hipStream_t s) {
+  const int d = c->d_model;
+  if (!c->use_conv) {
+    rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, W.ut, nullptr);
+    LAUNCH_CHECK();
+    return DFLASH_OK;
+  }
+  rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, nullptr, W.uf);
+  LAUNCH_CHECK();
+  EpiStore<T> e{seg1<T>(L.conv_gen[site], 2 * (d / 16), d), W.delta, 2 * (d / 16), STORE};
+  GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, e, s)));
+  conv_apply_kernel<T><<<M, 256, 0, s>>>(W.uf, W.delta, static_cast<const T*>(L.conv_w0[site]),
+                                         static_cast<const T*>(L.conv_w1[site]), d, 0, W.ut, nullptr);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+// post-sublayer: x += A W^T, through the conv when enabled
+template <typename T, typename AS>
+int post_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site, const void* wmat, const AS* A,
+                  int K, int M, DraftWs<T>& W, hipStream_t s) {
+  const int d = c->d_model;
+  if (!c->use_conv) {
+    EpiStore<T> e{seg1<T>(wmat, d, K), W.x, d, ADD};
+    GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s)));
+    return DFLASH_OK;
+  }
+  EpiStore<T> e{seg1<T>(wmat, d, K), W.uf, d, STORE};
+  GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s)));
+  EpiStore<T> g{seg1<T>(L.conv_gen[site], 2 * (d / 16), d), W.delta, 2 * (d / 16), STORE};
+  GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, g, s)));
+  conv_apply_kernel<T><<<M, 256, 0, s>>>(W.uf, W.delta, static_cast<const T*>(L.conv_w0[site]),
+                                         static_cast<const T*>(L.conv_w1[site]), d, 1, nullptr, W.x);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+template <typename T>
+int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv* kv, const int32_t* ctx_len,
+               const int32_t* block_ids, int B, int32_t* cand_ids, float* cand_logits, float* final_hidden,
+               float* logits, void* ws, hipStream_t s) {
+  Carver cv(ws);
+  DraftWs<T> W = carve_draft<T>(cv, c, B, kv->cap);
+  const int M = 16 * B, d = c->d_model, H = c->n_heads, Hkv = c->n_kv_heads, hd = c->head_dim;
+  const int hq = H * hd, F = c->d_ffn, V = c->vocab;
+  int rc;
+  embed_kernel<T><<<M, 256, 0, s>>>(static_cast<const T*>(w->embed), block_ids, d, W.x);
+  LAUNCH_CHECK();
+  for (int l = 0; l < c->n_layers; ++l) {
+    const dflash_layer_weights& L = w->layers[l];
+    // attention sublayer
+    if ((rc = pre_sublayer<T>(c, L, 0, L.g_attn, M, W, s))) return rc;
+    EpiQKV<T> eq{static_cast<const T*>(L.w_q), static_cast<const T*>(L.w_k), static_cast<const T*>(L.w_v),
+                 d, H, Hkv, hd, c->rope_theta, ctx_len, W.q, W.kb, W.vbt};
+    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, (hq + 2 * Hkv * hd) / 16, eq, s)));
+    AttnArgs<T> aa{W.q, W.kb, W.vbt, static_cast<const T*>(kv->k[l]), static_cast<const T*>(kv->vt[l]), ctx_len,
+                   W.part_o, W.part_ml, H, Hkv, kv->cap, W.S, 1.4426950408889634f / sqrtf(static_cast<float>(hd))};
+    GEMM_CHECK(run_attention<T>(c, aa, B, W.o, s));
+    if ((rc = post_sublayer<T, T>(c, L, 1, L.w_o, W.o, hq, M, W, s))) return rc;
+    // feed-forward sublayer
+    if ((rc = pre_sublayer<T>(c, L, 2, L.g_ffn, M, W, s))) return rc;
+    EpiSwiGLU<T> ef{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), d, F, W.h};
+    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, 2 * (F / 16), ef, s)));
+    if ((rc = post_sublayer<T, T>(c, L, 3, L.w_down, W.h, F, M, W, s))) return rc;
+  }
+  rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(w->g_final), d, c->rms_eps, W.ut, final_hidden);
+  LAUNCH_CHECK();
+  float* lg = logits ? logits : W.logits;
+  EpiStore<T> el{seg1<T>(w->lm_head, V, d), lg, V, STORE};
+  GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, V / 16, el, s)));
+  const int nch = (V + kTopkChunk - 1) / kTopkChunk;
+  topk_partial_kernel<<<dim3(nch, M), 256, 0, s>>>(lg, V, V, kTopkChunk, W.tk_v, W.tk_i);
+  LAUNCH_CHECK();
+  topk_final_kernel<<<M, 64, 0, s>>>(W.tk_v, W.tk_i, nch, cand_ids, cand_logits);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+// ------------------------------------------------------------------ path
+
+template <typename T>
+int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* cand_ids, const float* cand_logits,
+              const float* final_hidden, const int32_t* block_ids, int n_fixed, int mode, int B, int32_t* path_idx,
+              int32_t* path_ids, float* pair_scores, void* ws, hipStream_t s) {
+  Carver cv(ws);
+  PathWs W = carve_path(cv, c, B);
+  const int d = c->d_model, PD = c->ps_dim, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
+  path_tokens_kernel<<<B, 256, 0, s>>>(cand_ids, block_ids, n_fixed, W.tokens);
+  LAUNCH_CHECK();
+  {
+    SegW<T> sw{};
+    sw.p[0] = static_cast<const T*>(w->ps_left);
+    sw.p[1] = static_cast<const T*>(w->ps_right);
+    sw.off[0] = 0;
+    sw.off[1] = PD;
+    sw.off[2] = 2 * PD;
+    sw.n_seg = 2;
+    sw.K = d;
+    EpiStore<T> e{sw, W.z, 2 * PD, STORE};
+    GEMM_CHECK((run_gemm<T, T>(static_cast<const T*>(w->embed), d, W.tokens, B * Tn, d, 2 * PD / 16, e, s)));
+  }
+  if (c->use_gate) {
+    EpiStore<T> e{seg1<T>(w->ps_gate, PD, d), W.gamma, PD, SIGMOID};
+    GEMM_CHECK((run_gemm<T, float>(final_hidden, d, nullptr, 16 * B, d, PD / 16, e, s)));
+  }
+  path_factors_kernel<T><<<B, 256, 0, s>>>(W.z, c->use_gate ? W.gamma : nullptr, static_cast<const T*>(w->ps_u),
+                                           static_cast<const T*>(w->ps_v), PD, c->ps_rank, n_fixed, W.lam, W.rho);
+  LAUNCH_CHECK();
+  path_walk_kernel<<<B, 256, 0, s>>>(W.lam, W.rho, c->ps_rank, cand_ids, cand_logits, n_fixed, mode, path_idx,
+                                     path_ids, pair_scores);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+// =====================================================================================
+// exported C ABI
+// =====================================================================================
+
+extern "C" {
+
+int dflash_check_config(const dflash_config* cfg) { return check_config(cfg); }
+
+const char* dflash_status_string(int status) {
+  switch (status) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_E_INVAL: return "invalid argument";
+    case DFLASH_E_UNSUPPORTED: return "unsupported shape";
+    case DFLASH_E_WORKSPACE: return "workspace too small";
+    case DFLASH_E_CAPACITY: return "KV cache capacity exceeded";
+    case DFLASH_E_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t dflash_inject_workspace_bytes(const dflash_config* cfg, int32_t n_rows) {
+  if (check_config(cfg) != DFLASH_OK || n_rows <= 0) return 0;
+  Carver cv(nullptr);
+  if (cfg->dtype == DFLASH_BF16) carve_inject<bf16_t>(cv, cfg, n_rows);
+  else carve_inject<float>(cv, cfg, n_rows);
+  return cv.off;
+}
+
+size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t cap) {
+  if (check_config(cfg) != DFLASH_OK || batch <= 0 || cap <= 0) return 0;
+  Carver cv(nullptr);
+  if (cfg->dtype == DFLASH_BF16) carve_draft<bf16_t>(cv, cfg, batch, cap);
+  else carve_draft<float>(cv, cfg, batch, cap);
+  return cv.off;
+}
+
+size_t dflash_path_workspace_bytes(const dflash_config* cfg, int32_t batch) {
+  if (check_config(cfg) != DFLASH_OK || batch <= 0) return 0;
+  Carver cv(nullptr);
+  carve_path(cv, cfg, batch);
+  return cv.off;
+}
+
+size_t dflash_verify_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab) {
+  if (batch <= 0 || n_draft < 0 || n_draft > 64 || vocab <= 0) return 0;
+  Carver cv(nullptr);
+  carve_verify(cv, batch, n_draft, vocab);
+  return cv.off;
+}
+
+int dflash_inject_context(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, const void* hidden,
+                          int32_t n_rows, const int32_t* row_off, const int32_t* pos0, const int32_t* n_new,
+                          int32_t batch, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_weights(cfg, w, false, true, false))) return rc;
+  if (batch <= 0 || n_rows <= 0) return DFLASH_E_INVAL;
+  if ((rc = check_kv(cfg, kv, batch))) return rc;
+  if (!hidden || !row_off || !pos0 || !n_new || !workspace) return DFLASH_E_INVAL;
+  if (workspace_bytes < dflash_inject_workspace_bytes(cfg, n_rows)) return DFLASH_E_WORKSPACE;
+  if (cfg->dtype == DFLASH_BF16)
+    return inject_impl<bf16_t>(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, stream);
+  return inject_impl<float>(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, stream);
+}
+
+int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, const int32_t* ctx_len,
+                       const int32_t* block_ids, int32_t batch, int32_t* cand_ids, float* cand_logits,
+                       float* final_hidden, float* logits, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_weights(cfg, w, true, false, false))) return rc;
+  if (batch <= 0) return DFLASH_E_INVAL;
+  if ((rc = check_kv(cfg, kv, batch))) return rc;
+  if (!ctx_len || !block_ids || !cand_ids || !cand_logits || !final_hidden || !workspace) return DFLASH_E_INVAL;
+  if (workspace_bytes < dflash_draft_workspace_bytes(cfg, batch, kv->cap)) return DFLASH_E_WORKSPACE;
+  if (cfg->dtype == DFLASH_BF16)
+    return draft_impl<bf16_t>(cfg, w, kv, ctx_len, block_ids, batch, cand_ids, cand_logits, final_hidden, logits,
+                              workspace, stream);
+  return draft_impl<float>(cfg, w, kv, ctx_len, block_ids, batch, cand_ids, cand_logits, final_hidden, logits,
+                           workspace, stream);
+}
+
+int dflash_select_path(const dflash_config* cfg, const dflash_weights* w, const int32_t* cand_ids,
+                       const float* cand_logits, const float* final_hidden, const int32_t* block_ids, int32_t n_fixed,
+                       int32_t mode, int32_t batch, int32_t* path_idx, int32_t* path_ids, float* pair_scores,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_weights(cfg, w, false, false, true))) return rc;
+  if (batch <= 0 || (n_fixed != 0 && n_fixed != 1)) return DFLASH_E_INVAL;
+  if (mode != DFLASH_PATH_GREEDY && mode != DFLASH_PATH_EXACT) return DFLASH_E_INVAL;
+  if (!cand_ids || !cand_logits || !block_ids || !path_idx || !path_ids || !workspace) return DFLASH_E_INVAL;
+  if (cfg->use_gate && !final_hidden) return DFLASH_E_INVAL;
+  if (workspace_bytes < dflash_path_workspace_bytes(cfg, batch)) return DFLASH_E_WORKSPACE;
+  if (cfg->dtype == DFLASH_BF16)
+    return path_impl<bf16_t>(cfg, w, cand_ids, cand_logits, final_hidden, block_ids, n_fixed, mode, batch, path_idx,
+                             path_ids, pair_scores, workspace, stream);
+  return path_impl<float>(cfg, w, cand_ids, cand_logits, final_hidden, block_ids, n_fixed, mode, batch, path_idx,
+                          path_ids, pair_scores, workspace, stream);
+}
+
+int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch, int32_t n_draft,
+                  int32_t vocab, int32_t* accept_len, int32_t* bonus, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream) {
+  if (batch <= 0 || n_draft < 0 || vocab <= 0) return DFLASH_E_INVAL;
+  if (n_draft > 64) return DFLASH_E_UNSUPPORTED;
+  if (tgt_dtype != DFLASH_BF16 && tgt_dtype != DFLASH_F32) return DFLASH_E_INVAL;
+  if ((n_draft > 0 && !draft) || !tgt_logits || !accept_len || !bonus || !workspace) return DFLASH_E_INVAL;
+  if (workspace_bytes < dflash_verify_workspace_bytes(batch, n_draft, vocab)) return DFLASH_E_WORKSPACE;
+  Carver cv(workspace);
+  VerifyWs W = carve_verify(cv, batch, n_draft, vocab);
+  const int nch = (vocab + kArgmaxChunk - 1) / kArgmaxChunk;
+  dim3 grid(nch, batch * (n_draft + 1));
+  if (tgt_dtype == DFLASH_BF16)
+    argmax_partial_kernel<bf16_t><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(tgt_logits), vocab,
+                                                            kArgmaxChunk, W.pv, W.pi);
+  else
+    argmax_partial_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(tgt_logits), vocab,
+                                                           kArgmaxChunk, W.pv, W.pi);
+  LAUNCH_CHECK();
+  accept_kernel<<<batch, 64, 0, stream>>>(W.pv, W.pi, nch, draft, n_draft, accept_len, bonus);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+}  // extern "C"

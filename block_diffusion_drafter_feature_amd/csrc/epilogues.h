@@ -1,0 +1,178 @@
+// Epilogue functors of the GEMMs: where W rows come from and what happens to each
+// output element.  Interface used by gemm.h:
+//   PX, PC            partner of (virtual tile vt, column c) is (vt ^ PX, c ^ PC)
+//   wrow(vt, c)       pointer to the W row feeding column c of virtual tile vt (nullptr: zero)
+//   apply(vt, m, c, v, partner)
+#pragma once
+
+#include "common.h"
+
+namespace dflash {
+
+// Up to 16 weight matrices stacked along N.
+template <typename T>
+struct SegW {
+  const T* p[16];
+  int off[17];   // row offsets, off[n_seg] = total rows
+  int n_seg;
+  int K;
+  __device__ __forceinline__ int find(int n) const {
+    int s = 0;
+    while (s + 1 < n_seg && n >= off[s + 1]) ++s;
+    return s;
+  }
+};
+
+// Rotary-pair column layout: the 16 columns of a tile are 8 dims of the first half
+// of a head and their 8 partners of the second half.
+__device__ __forceinline__ int rope_dim(int tt, int c, int hd) {
+  return (c < 8) ? 8 * tt + c : hd / 2 + 8 * tt + (c - 8);
+}
+
+// ------------------------------------------------------------------ plain store / residual / sigmoid
+
+enum StoreMode { STORE = 0, ADD = 1, SIGMOID = 2 };
+
+template <typename T>
+struct EpiStore {
+  SegW<T> w;
+  float* out;
+  int ldo;
+  int mode;
+  static constexpr int PX = 0, PC = 0;
+  __device__ __forceinline__ const T* wrow(int vt, int c) const {
+    const int n = vt * 16 + c;
+    if (n >= w.off[w.n_seg]) return nullptr;
+    const int s = w.find(n);
+    return w.p[s] + static_cast<size_t>(n - w.off[s]) * w.K;
+  }
+  __device__ __forceinline__ void apply(int vt, int m, int c, float v, float) const {
+    const int n = vt * 16 + c;
+    if (n >= w.off[w.n_seg]) return;
+    float* o = out + static_cast<size_t>(m) * ldo + n;
+    if (mode == ADD) *o += v;
+    else if (mode == SIGMOID) *o = 1.f / (1.f + expf(-v));
+    else *o = v;
+  }
+};
+
+// ------------------------------------------------------------------ block Q/K/V with RoPE
+
+template <typename T>
+struct EpiQKV {
+  const T* wq;
+  const T* wk;
+  const T* wv;
+  int K, H, Hkv, hd;
+  float theta;
+  const int32_t* ctx_len;  // [B]
+  T* q;                    // [M][H][hd]
+  T* kb;                   // [B][Hkv][16][hd]
+  T* vbt;                  // [B][Hkv][hd][16]
+  static constexpr int PX = 0, PC = 8;
+  // virtual tiles: H*hd/16 query tiles, Hkv*hd/16 key tiles (both RoPE-paired), Hkv*hd/16 value tiles
+  __device__ __forceinline__ const T* wrow(int vt, int c) const {
+    const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
+    if (vt < tq) return wq + static_cast<size_t>((vt / tph) * hd + rope_dim(vt % tph, c, hd)) * K;
+    vt -= tq;
+    if (vt < tk) return wk + static_cast<size_t>((vt / tph) * hd + rope_dim(vt % tph, c, hd)) * K;
+    vt -= tk;
+    if (vt < tk) return wv + static_cast<size_t>(vt * 16 + c) * K;
+    return nullptr;
+  }
+  __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
+    const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
+    const int b = m >> 4, j = m & 15;
+    if (vt < tq + tk) {
+      const bool isq = vt < tq;
+      const int t = isq ? vt : vt - tq;
+      const int head = t / tph, tt = t % tph;
+      const int dim = rope_dim(tt, c, hd);
+      float cs, sn;
+      rope_cs(ctx_len[b] + j, 8 * tt + (c & 7), hd, theta, &cs, &sn);
+      const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
+      if (isq) q[(static_cast<size_t>(m) * H + head) * hd + dim] = from_f<T>(r);
+      else kb[((static_cast<size_t>(b) * Hkv + head) * 16 + j) * hd + dim] = from_f<T>(r);
+    } else {
+      const int t = vt - tq - tk;
+      if (t >= tk) return;
+      const int n = t * 16 + c, head = n / hd, dim = n % hd;
+      vbt[((static_cast<size_t>(b) * Hkv + head) * hd + dim) * 16 + j] = from_f<T>(v);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ context K/V injection
+
+template <typename T>
+struct EpiInject {
+  const T* wk[16];
+  const T* wv[16];
+  T* kc[16];
+  T* vtc[16];
+  int K, L, Hkv, hd, B, cap;
+  float theta;
+  const int32_t* row_off;  // [B+1]
+  const int32_t* pos0;     // [B]
+  const int32_t* n_new;    // [B]
+  static constexpr int PX = 0, PC = 8;
+  // virtual tiles per layer: Hkv*hd/16 key tiles (RoPE-paired) then Hkv*hd/16 value tiles
+  __device__ __forceinline__ const T* wrow(int vt, int c) const {
+    const int tk = Hkv * hd / 16, tph = hd / 16;
+    const int l = vt / (2 * tk), t = vt % (2 * tk);
+    if (l >= L) return nullptr;
+    if (t < tk) return wk[l] + static_cast<size_t>((t / tph) * hd + rope_dim(t % tph, c, hd)) * K;
+    return wv[l] + static_cast<size_t>((t - tk) * 16 + c) * K;
+  }
+  __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
+    const int tk = Hkv * hd / 16, tph = hd / 16;
+    const int l = vt / (2 * tk), t = vt % (2 * tk);
+    if (l >= L) return;
+    // sequence owning row m: row_off[b] <= m < row_off[b+1]
+    int lo = 0, hi = B;
+    if (m < row_off[0] || m >= row_off[B]) return;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (row_off[mid] <= m) lo = mid; else hi = mid;
+    }
+    const int b = lo, i = m - row_off[b];
+    if (i >= n_new[b]) return;
+    const int pos = pos0[b] + i;
+    if (pos < 0 || pos >= cap) return;
+    if (t < tk) {
+      const int head = t / tph, tt = t % tph, dim = rope_dim(tt, c, hd);
+      float cs, sn;
+      rope_cs(pos, 8 * tt + (c & 7), hd, theta, &cs, &sn);
+      const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
+      kc[l][((static_cast<size_t>(b) * Hkv + head) * cap + pos) * hd + dim] = from_f<T>(r);
+    } else {
+      const int n = (t - tk) * 16 + c, head = n / hd, dim = n % hd;
+      vtc[l][((static_cast<size_t>(b) * Hkv + head) * hd + dim) * cap + pos] = from_f<T>(v);
+    }
+  }
+};
+
+// ------------------------------------------------------------------ SwiGLU (gate/up pair)
+
+template <typename T>
+struct EpiSwiGLU {
+  const T* wg;
+  const T* wu;
+  int K, Fd;
+  T* h;  // [M][Fd]
+  static constexpr int PX = 1, PC = 0;
+  __device__ __forceinline__ const T* wrow(int vt, int c) const {
+    const int n = (vt >> 1) * 16 + c;
+    if (n >= Fd) return nullptr;
+    return ((vt & 1) ? wu : wg) + static_cast<size_t>(n) * K;
+  }
+  __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
+    if (vt & 1) return;
+    const int n = (vt >> 1) * 16 + c;
+    if (n >= Fd) return;
+    const float s = v / (1.f + expf(-v));
+    h[static_cast<size_t>(m) * Fd + n] = from_f<T>(s * pv);
+  }
+};
+
+}  // namespace dflash

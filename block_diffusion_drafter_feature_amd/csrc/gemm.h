@@ -1,0 +1,292 @@
+// GEMMs of the drafting step on the gfx950 matrix cores:  C[m, n] = sum_k A[m, k] W[n, k].
+//
+// A is an activation matrix (row-major, optional row gather, given either in the
+// storage type T or in fp32 and rounded to T as it is loaded).  W rows are looked
+// up through the epilogue functor, which maps a "virtual 16-column tile" and a
+// column inside it to a weight row.  That indirection lets one launch cover
+// several weight matrices (Q|K|V, the K/V projections of every layer) and lets a
+// tile hold columns that belong together (a RoPE pair d, d+hd/2; a gate/up pair)
+// so the epilogue can combine them without another pass.
+//
+// Two kernels:
+//  * gemm_skinny : M <= 64 (the drafted block of 1..4 sequences).  Weight
+//    streaming: each work-group owns NT virtual tiles over the whole K; its NW
+//    waves split K, stream their slice of W straight from HBM into registers
+//    (16 B per lane per fragment) and reduce through LDS in a fixed order.
+//  * gemm_tiled  : M > 64.  128x128 output tile per work-group, A and W tiles
+//    staged through LDS (register prefetch of the next K slab while the matrix
+//    cores work on the current one), 2x2 waves of 64x64.
+// Both are deterministic (no atomics).
+#pragma once
+
+#include "common.h"
+#include <type_traits>
+
+namespace dflash {
+
+template <typename T, typename AS>
+__device__ __forceinline__ typename Frag<T>::type load_a(const AS* p) {
+  if constexpr (std::is_same<AS, T>::value) return Frag<T>::load(p);
+  else return Frag<T>::load_f32(p);
+}
+
+// ---------------------------------------------------------------------------------
+// skinny GEMM
+// ---------------------------------------------------------------------------------
+
+template <typename T, typename AS, int MT, int NT, int NW, class Epi>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restrict__ A, int lda,
+                                                              const int32_t* __restrict__ arows, int M, int K,
+                                                              Epi epi) {
+  typedef Frag<T> F;
+  typedef typename F::type frag_t;
+  constexpr int ROWS = 16 * MT;
+  constexpr int TW = 16 * NT;
+  constexpr int U = (MT <= 2) ? 8 : 4;
+  __shared__ float red[NW][MT * NT * 256];
+  __shared__ float tile[ROWS][TW + 1];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int vt0 = blockIdx.x * NT;
+
+  const T* wp[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) wp[nt] = epi.wrow(vt0 + nt, r16);
+  const AS* ap[MT];
+  bool av[MT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) {
+    const int m = mt * 16 + r16;
+    av[mt] = m < M;
+    const int ar = av[mt] ? (arows ? arows[m] : m) : 0;
+    ap[mt] = A + static_cast<size_t>(ar) * lda;
+  }
+
+  f32x4_t acc[MT][NT];
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // wave-uniform K loop over this wave's slice [k0, k0 + kw); lane group g reads K offset +8g
+  const int kw = K / NW;
+  const int k0 = wave * kw, kend = k0 + kw;
+  int kb = k0;
+  for (; kb + 32 * U <= kend; kb += 32 * U) {
+    const int k = kb + g * 8;
+    frag_t w[U][NT], a[U][MT];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) w[u][nt] = wp[nt] ? F::load(wp[nt] + k + 32 * u) : F::zero();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? load_a<T, AS>(ap[mt] + k + 32 * u) : F::zero();
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = F::mma(acc[mt][nt], a[u][mt], w[u][nt]);
+  }
+  for (; kb < kend; kb += 32) {
+    const int k = kb + g * 8;
+    frag_t w[NT], a[MT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) w[nt] = wp[nt] ? F::load(wp[nt] + k) : F::zero();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) a[mt] = av[mt] ? load_a<T, AS>(ap[mt] + k) : F::zero();
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = F::mma(acc[mt][nt], a[mt], w[nt]);
+  }
+
+  // fixed-order reduction of the NW partial tiles
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][((mt * NT + nt) * 64 + lane) * 4 + i] = acc[mt][nt][i];
+  __syncthreads();
+  for (int e = threadIdx.x; e < MT * NT * 256; e += 64 * NW) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += red[w][e];
+    const int i = e & 3, l = (e >> 2) & 63, t = e >> 8;
+    const int mt = t / NT, nt = t % NT;
+    tile[mt * 16 + 4 * (l >> 4) + i][nt * 16 + (l & 15)] = s;
+  }
+  __syncthreads();
+  for (int e = threadIdx.x; e < ROWS * TW; e += 64 * NW) {
+    const int m = e / TW, c = e % TW;
+    if (m >= M) continue;
+    const int pc = (((c >> 4) ^ Epi::PX) << 4) | ((c & 15) ^ Epi::PC);
+    epi.apply(vt0 + (c >> 4), m, c & 15, tile[m][c], tile[m][pc]);
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// tiled GEMM (M > 64)
+// ---------------------------------------------------------------------------------
+
+template <typename T> struct TiledCfg;
+template <> struct TiledCfg<bf16_t> { static constexpr int BK = 64; };
+template <> struct TiledCfg<float> { static constexpr int BK = 32; };
+
+template <typename T, typename AS, class Epi>
+__global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ A, int lda,
+                                                         const int32_t* __restrict__ arows, int M, int K,
+                                                         Epi epi) {
+  typedef Frag<T> F;
+  typedef typename F::type frag_t;
+  constexpr int BM = 128, BN = 128, BK = TiledCfg<T>::BK;
+  constexpr int EPB = 16 / sizeof(T);           // elements per 16-byte chunk
+  constexpr int CPR = BK / EPB;                 // chunks per tile row (8)
+  constexpr int LD = BK + EPB;                  // padded LDS row (elements)
+  constexpr int CH = BM * CPR / 256;            // chunks per thread per operand (4)
+  constexpr int SMEM_AB = 2 * BM * LD * sizeof(T);
+  constexpr int SMEM_EP = 64 * (BN + 1) * sizeof(float);
+  constexpr int SMEM = SMEM_AB > SMEM_EP ? SMEM_AB : SMEM_EP;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  T* As = reinterpret_cast<T*>(smem);
+  T* Bs = As + BM * LD;
+  float* Ct = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int m0 = blockIdx.y * BM;
+  const int vt0 = blockIdx.x * (BN / 16);
+
+  // global->register staging: chunk q of this thread covers row (tid*CH+q)/CPR, chunk (tid*CH+q)%CPR
+  const AS* agp[CH];
+  const T* bgp[CH];
+  bool aok[CH];
+#pragma unroll
+  for (int q = 0; q < CH; ++q) {
+    const int idx = tid * CH + q, r = idx / CPR, ck = idx % CPR;
+    const int m = m0 + r;
+    aok[q] = m < M;
+    const int ar = aok[q] ? (arows ? arows[m] : m) : 0;
+    agp[q] = A + static_cast<size_t>(ar) * lda + ck * EPB;
+    const T* wr = epi.wrow(vt0 + r / 16, r % 16);
+    bgp[q] = wr ? wr + ck * EPB : nullptr;
+  }
+  u32x4_t ra[CH], rb[CH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      if (aok[q]) {
+        if constexpr (std::is_same<AS, T>::value) {
+          ra[q] = *reinterpret_cast<const u32x4_t*>(agp[q] + k0);
+        } else {  // fp32 source rounded to bf16: 8 values -> one 16 B chunk
+          ra[q] = __builtin_bit_cast(u32x4_t, Frag<T>::load_f32(reinterpret_cast<const float*>(agp[q]) + k0));
+        }
+      } else {
+        ra[q] = u32x4_t{0u, 0u, 0u, 0u};
+      }
+      rb[q] = bgp[q] ? *reinterpret_cast<const u32x4_t*>(bgp[q] + k0) : u32x4_t{0u, 0u, 0u, 0u};
+    }
+  };
+  auto sstore = [&]() {
+#pragma unroll
+    for (int q = 0; q < CH; ++q) {
+      const int idx = tid * CH + q, r = idx / CPR, ck = idx % CPR;
+      *reinterpret_cast<u32x4_t*>(As + r * LD + ck * EPB) = ra[q];
+      *reinterpret_cast<u32x4_t*>(Bs + r * LD + ck * EPB) = rb[q];
+    }
+  };
+
+  f32x4_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int KT = K / BK;
+  gload(0);
+  sstore();
+  __syncthreads();
+  for (int kt = 0; kt < KT; ++kt) {
+    if (kt + 1 < KT) gload((kt + 1) * BK);
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      frag_t af[4], bfr[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = F::load(As + (wm * 64 + i * 16 + r16) * LD + ks * 32 + g * 8);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) bfr[j] = F::load(Bs + (wn * 64 + j * 16 + r16) * LD + ks * 32 + g * 8);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = F::mma(acc[i][j], af[i], bfr[j]);
+    }
+    __syncthreads();
+    if (kt + 1 < KT) {
+      sstore();
+      __syncthreads();
+    }
+  }
+
+  // epilogue, one 64-row half at a time through LDS
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    if (wm == half) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            Ct[(i * 16 + 4 * g + e) * (BN + 1) + wn * 64 + j * 16 + r16] = acc[i][j][e];
+    }
+    __syncthreads();
+    for (int e = tid; e < 64 * BN; e += 256) {
+      const int r = e / BN, c = e % BN;
+      const int m = m0 + half * 64 + r;
+      if (m < M) {
+        const int pc = (((c >> 4) ^ Epi::PX) << 4) | ((c & 15) ^ Epi::PC);
+        epi.apply(vt0 + (c >> 4), m, c & 15, Ct[r * (BN + 1) + c], Ct[r * (BN + 1) + pc]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------
+// launcher
+// ---------------------------------------------------------------------------------
+
+template <typename T, typename AS, int MT, int NT, class Epi>
+static hipError_t launch_skinny_nw(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
+                                   const Epi& epi, hipStream_t s) {
+  const int grid = n_vtiles / NT;
+  if (K % (8 * 32) == 0)
+    gemm_skinny_kernel<T, AS, MT, NT, 8, Epi><<<grid, 64 * 8, 0, s>>>(A, lda, arows, M, K, epi);
+  else if (K % (4 * 32) == 0)
+    gemm_skinny_kernel<T, AS, MT, NT, 4, Epi><<<grid, 64 * 4, 0, s>>>(A, lda, arows, M, K, epi);
+  else
+    gemm_skinny_kernel<T, AS, MT, NT, 2, Epi><<<grid, 64 * 2, 0, s>>>(A, lda, arows, M, K, epi);
+  return hipGetLastError();
+}
+
+// n_vtiles: number of virtual 16-column tiles (multiple of 2 when Epi::PX == 1).
+// K: multiple of 64.
+template <typename T, typename AS, class Epi>
+static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
+                           hipStream_t s) {
+  if (M <= 0 || n_vtiles <= 0) return hipSuccess;
+  constexpr int NT = Epi::PX ? 2 : 1;
+  if (M <= 16) return launch_skinny_nw<T, AS, 1, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (M <= 32) return launch_skinny_nw<T, AS, 2, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (M <= 64) return launch_skinny_nw<T, AS, 4, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
+  dim3 grid((n_vtiles + 7) / 8, (M + 127) / 128);
+  gemm_tiled_kernel<T, AS, Epi><<<grid, 256, 0, s>>>(A, lda, arows, M, K, epi);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,364 @@
+// Selection kernels: top-16 over the vocabulary, greedy verification, the Path
+// Selector's pair scores and path walk.  All reductions use the total order
+// (value descending, index ascending), so results are unique and deterministic.
+#pragma once
+
+#include "common.h"
+#include <limits.h>
+
+namespace dflash {
+
+// ------------------------------------------------------------------ register top-16 lists
+
+struct Top16 {
+  float v[16];
+  int i[16];
+  __device__ __forceinline__ void init() {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      v[k] = -INFINITY;
+      i[k] = INT_MAX;
+    }
+  }
+  __device__ __forceinline__ void cswap(int a, int b) {   // keep the better of (a, b) at a
+    const bool sw = better(v[b], i[b], v[a], i[a]);
+    const float tv = sw ? v[b] : v[a];
+    const int ti = sw ? i[b] : i[a];
+    v[b] = sw ? v[a] : v[b];
+    i[b] = sw ? i[a] : i[b];
+    v[a] = tv;
+    i[a] = ti;
+  }
+  // insert one candidate into the sorted list
+  __device__ __forceinline__ void push(float x, int id) {
+    if (!better(x, id, v[15], i[15])) return;
+    v[15] = x;
+    i[15] = id;
+#pragma unroll
+    for (int k = 15; k > 0; --k) cswap(k - 1, k);
+  }
+  // sort a bitonic sequence into descending order
+  __device__ __forceinline__ void bitonic_merge() {
+#pragma unroll
+    for (int st = 8; st > 0; st >>= 1)
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if ((k & st) == 0) cswap(k, k + st);
+  }
+  // this <- top 16 of (this U other); both sorted descending
+  __device__ __forceinline__ void merge(const float* ov, const int* oi) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bool take = better(ov[15 - k], oi[15 - k], v[k], i[k]);
+      v[k] = take ? ov[15 - k] : v[k];
+      i[k] = take ? oi[15 - k] : i[k];
+    }
+    bitonic_merge();
+  }
+  // all 64 lanes of the wave end with the wave's top 16
+  __device__ __forceinline__ void wave_merge() {
+    // the level loop stays rolled: unrolling its six bitonic stages makes the
+    // compiler's select-chain optimisations run for tens of minutes
+#pragma unroll 1
+    for (int s = 1; s < 64; s <<= 1) {
+      float ov[16];
+      int oi[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        ov[k] = __shfl_xor(v[k], s, 64);
+        oi[k] = __shfl_xor(i[k], s, 64);
+      }
+      merge(ov, oi);
+    }
+  }
+};
+
+// Work-group top-16 of its lanes' lists; result valid in wave 0 (all its lanes).
+__device__ __forceinline__ void block_top16(Top16& t, float* sv, int* si) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  t.wave_merge();
+  if (lane < 16) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k == lane) {
+        sv[w * 16 + k] = t.v[k];
+        si[w * 16 + k] = t.i[k];
+      }
+  }
+  __syncthreads();
+  if (w == 0) {
+    t.init();
+    if (lane < nw) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        t.v[k] = sv[lane * 16 + k];
+        t.i[k] = si[lane * 16 + k];
+      }
+    }
+    t.wave_merge();
+  }
+}
+
+// Stage 1: top-16 of each (row, column chunk).  grid (n_chunks, rows), 256 threads.
+__global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restrict__ logits, int V, int ld,
+                                                           int chunk, float* __restrict__ pv,
+                                                           int32_t* __restrict__ pi) {
+  __shared__ float sv[4 * 16];
+  __shared__ int si[4 * 16];
+  const int c = blockIdx.x, m = blockIdx.y, nch = gridDim.x;
+  const int c0 = c * chunk, c1 = min(V, c0 + chunk);
+  const float* row = logits + static_cast<size_t>(m) * ld;
+  Top16 t;
+  t.init();
+  for (int j = c0 + threadIdx.x; j < c1; j += 256) t.push(row[j], j);
+  block_top16(t, sv, si);
+  if (threadIdx.x < 16) {
+    const size_t o = (static_cast<size_t>(m) * nch + c) * 16;
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k == threadIdx.x) {
+        pv[o + k] = t.v[k];
+        pi[o + k] = t.i[k];
+      }
+  }
+}
+
+// Stage 2: merge the per-chunk lists of each row.  grid (rows), 64 threads.
+__global__ __launch_bounds__(64) void topk_final_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
+                                                        int n_chunks, int32_t* __restrict__ out_ids,
+                                                        float* __restrict__ out_vals) {
+  const int m = blockIdx.x, lane = threadIdx.x;
+  Top16 t;
+  t.init();
+  for (int c = lane; c < n_chunks; c += 64) {
+    const size_t o = (static_cast<size_t>(m) * n_chunks + c) * 16;
+    float ov[16];
+    int oi[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      ov[k] = pv[o + k];
+      oi[k] = pi[o + k];
+    }
+    t.merge(ov, oi);
+  }
+  t.wave_merge();
+  if (lane < 16) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k)
+      if (k == lane) {
+        out_ids[static_cast<size_t>(m) * 16 + k] = t.i[k];
+        out_vals[static_cast<size_t>(m) * 16 + k] = t.v[k];
+      }
+  }
+}
+
+// ------------------------------------------------------------------ greedy verification
+
+__device__ __forceinline__ void argmax_step(float& bv, int& bi, float v, int i) {
+  if (better(v, i, bv, bi)) {
+    bv = v;
+    bi = i;
+  }
+}
+
+// Stage 1: argmax of each (target row, column chunk).  grid (n_chunks, rows), 256 threads.
+template <typename TL>
+__global__ __launch_bounds__(256) void argmax_partial_kernel(const TL* __restrict__ x, int V, int chunk,
+                                                             float* __restrict__ pv, int32_t* __restrict__ pi) {
+  __shared__ float sv[4];
+  __shared__ int si[4];
+  const int c = blockIdx.x, r = blockIdx.y, nch = gridDim.x;
+  const int c0 = c * chunk, c1 = min(V, c0 + chunk);
+  const TL* row = x + static_cast<size_t>(r) * V;
+  float bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int j = c0 + threadIdx.x; j < c1; j += 256) argmax_step(bv, bi, to_f<TL>(row[j]), j);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = __shfl_xor(bv, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    argmax_step(bv, bi, ov, oi);
+  }
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) {
+    sv[w] = bv;
+    si[w] = bi;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < 4; ++k) argmax_step(bv, bi, sv[k], si[k]);
+    pv[static_cast<size_t>(r) * nch + c] = bv;
+    pi[static_cast<size_t>(r) * nch + c] = bi;
+  }
+}
+
+// Stage 2: per sequence, the greedy token of every row, then the accepted prefix and
+// the bonus token.  grid (batch), 64 threads; n_draft <= 64.
+__global__ __launch_bounds__(64) void accept_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
+                                                    int n_chunks, const int32_t* __restrict__ draft, int n_draft,
+                                                    int32_t* __restrict__ accept_len, int32_t* __restrict__ bonus) {
+  __shared__ int tok[65];
+  const int b = blockIdx.x, lane = threadIdx.x;
+  const int R = n_draft + 1;
+  for (int r = lane; r < R; r += 64) {
+    const size_t o = (static_cast<size_t>(b) * R + r) * n_chunks;
+    float bv = -INFINITY;
+    int bi = INT_MAX;
+    for (int c = 0; c < n_chunks; ++c) argmax_step(bv, bi, pv[o + c], pi[o + c]);
+    tok[r] = bi;
+  }
+  __syncthreads();
+  if (lane == 0) {
+    int a = 0;
+    while (a < n_draft && draft[static_cast<size_t>(b) * n_draft + a] == tok[a]) ++a;
+    accept_len[b] = a;
+    bonus[b] = tok[a];
+  }
+}
+
+// ------------------------------------------------------------------ Path Selector
+
+// Tokens whose 256-d embeddings are needed, per sequence: the 16 candidates of each
+// drafted position p (slot 16p + j), then the anchor (slot 16P) when n_fixed = 1.
+__global__ void path_tokens_kernel(const int32_t* __restrict__ cand_ids, const int32_t* __restrict__ block_ids,
+                                   int n_fixed, int32_t* __restrict__ tokens) {
+  const int b = blockIdx.x, P = 16 - n_fixed, T = 16 * P + n_fixed;
+  for (int t = threadIdx.x; t < T; t += blockDim.x) {
+    const int v = t < 16 * P ? cand_ids[(static_cast<size_t>(b) * 16 + n_fixed + t / 16) * 16 + (t % 16)]
+                             : block_ids[static_cast<size_t>(b) * 16];
+    tokens[static_cast<size_t>(b) * T + t] = v;
+  }
+}
+
+// Low-rank factors: lam[t] = U z_l(t) for left-neighbour tokens, rho[t] = V (gamma (.) z_r(t))
+// for right tokens.  grid (batch), 256 threads.  z: [B][T][2*PD] fp32 (left | right).
+template <typename T>
+__global__ __launch_bounds__(256) void path_factors_kernel(const float* __restrict__ z, const float* __restrict__ gamma,
+                                                           const T* __restrict__ U, const T* __restrict__ Vf, int PD,
+                                                           int r, int n_fixed, float* __restrict__ lam,
+                                                           float* __restrict__ rho) {
+  const int b = blockIdx.x, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
+  const float* zb = z + static_cast<size_t>(b) * Tn * 2 * PD;
+  for (int e = threadIdx.x; e < Tn * r; e += blockDim.x) {
+    const int t = e / r, k = e % r;
+    const int p = t < 16 * P ? t / 16 : -1;                   // drafted position of slot t (-1: anchor)
+    const bool is_left = (p >= 0 && p < P - 1) || (p < 0);
+    const bool is_right = p >= 0 && (p > 0 || n_fixed == 1);
+    const float* zl = zb + static_cast<size_t>(t) * 2 * PD;
+    const float* zr = zl + PD;
+    if (is_left) {
+      const T* u = U + static_cast<size_t>(k) * PD;
+      float s = 0.f;
+      for (int i = 0; i < PD; ++i) s += to_f<T>(u[i]) * zl[i];
+      lam[(static_cast<size_t>(b) * Tn + t) * r + k] = s;
+    }
+    if (is_right) {
+      const T* v = Vf + static_cast<size_t>(k) * PD;
+      const float* gm = gamma ? gamma + (static_cast<size_t>(b) * 16 + n_fixed + p) * PD : nullptr;
+      float s = 0.f;
+      if (gm) for (int i = 0; i < PD; ++i) s += to_f<T>(v[i]) * (gm[i] * zr[i]);
+      else for (int i = 0; i < PD; ++i) s += to_f<T>(v[i]) * zr[i];
+      rho[(static_cast<size_t>(b) * Tn + t) * r + k] = s;
+    }
+  }
+}
+
+// Pair scores and the walk.  grid (batch), 256 threads.
+//   S[p][a][j] = lam(cand[p-1][a]) . rho(cand[p][j])   (p >= 1)
+//   S[0][0][j] = lam(anchor) . rho(cand[0][j])          (anchor only)
+// Greedy: c_0 = argmax_j (l_0[j] + S[0][0][j]), c_p = argmax_j (l_p[j] + S[p][c_{p-1}][j]).
+// Exact:  best_0[j] = l_0[j] + S[0][0][j]; best_p[j] = l_p[j] + max_a (best_{p-1}[a] + S[p][a][j]).
+// All sums in fp32 in exactly this order; ties to the lowest index.
+__global__ __launch_bounds__(256) void path_walk_kernel(const float* __restrict__ lam, const float* __restrict__ rho,
+                                                        int r, const int32_t* __restrict__ cand_ids,
+                                                        const float* __restrict__ cand_logits, int n_fixed, int mode,
+                                                        int32_t* __restrict__ path_idx, int32_t* __restrict__ path_ids,
+                                                        float* __restrict__ pair_scores) {
+  __shared__ float S[16][16][16];
+  __shared__ float best[16];
+  __shared__ int back[16][16];
+  const int b = blockIdx.x, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
+  const float* lb = lam + static_cast<size_t>(b) * Tn * r;
+  const float* rb = rho + static_cast<size_t>(b) * Tn * r;
+  for (int e = threadIdx.x; e < P * 256; e += blockDim.x) {
+    const int p = e / 256, a = (e / 16) % 16, j = e % 16;
+    float s = 0.f;
+    int lt = -1;
+    if (p >= 1) lt = (p - 1) * 16 + a;
+    else if (n_fixed == 1 && a == 0) lt = 16 * P;   // anchor slot
+    if (lt >= 0) {
+      const float* x = lb + static_cast<size_t>(lt) * r;
+      const float* y = rb + static_cast<size_t>(p * 16 + j) * r;
+      for (int k = 0; k < r; ++k) s += x[k] * y[k];
+    }
+    S[p][a][j] = s;
+    if (pair_scores) pair_scores[((static_cast<size_t>(b) * P + p) * 16 + a) * 16 + j] = s;
+  }
+  __syncthreads();
+  if (threadIdx.x >= 16) return;
+  // one candidate per lane (lanes 0..15 of wave 0)
+  const int j = threadIdx.x;
+  const float* lg = cand_logits + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
+  const int32_t* ci = cand_ids + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
+  auto argmax16 = [&](float v, int& bi) {   // lanes 0..15: index of the best v, lowest on ties
+    float bv = v;
+    bi = j;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+      const float ov = __shfl_xor(bv, o, 16);
+      const int oi = __shfl_xor(bi, o, 16);
+      if (better(ov, oi, bv, bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    return bv;
+  };
+  if (mode == 0) {
+    float sc = lg[j] + (n_fixed == 1 ? S[0][0][j] : 0.f);
+    int c;
+    argmax16(sc, c);
+    if (j == 0) path_idx[static_cast<size_t>(b) * P] = c;
+    for (int p = 1; p < P; ++p) {
+      sc = lg[p * 16 + j] + S[p][c][j];
+      argmax16(sc, c);
+      if (j == 0) path_idx[static_cast<size_t>(b) * P + p] = c;
+    }
+  } else {
+    float bj = lg[j] + (n_fixed == 1 ? S[0][0][j] : 0.f);
+    best[j] = bj;
+    for (int p = 1; p < P; ++p) {
+      float bv = -INFINITY;
+      int ba = 0;
+      for (int a = 0; a < 16; ++a) {
+        const float v = best[a] + S[p][a][j];
+        if (v > bv) {
+          bv = v;
+          ba = a;
+        }
+      }
+      back[p][j] = ba;
+      bj = lg[p * 16 + j] + bv;
+      __builtin_amdgcn_wave_barrier();
+      best[j] = bj;
+      __builtin_amdgcn_wave_barrier();
+    }
+    int c;
+    argmax16(bj, c);
+    if (j == 0) {
+      for (int p = P - 1; p >= 0; --p) {
+        path_idx[static_cast<size_t>(b) * P + p] = c;
+        if (p > 0) c = back[p][c];
+      }
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  if (j == 0) {
+    for (int p = 0; p < P; ++p) {
+      const int c = path_idx[static_cast<size_t>(b) * P + p];
+      path_ids[static_cast<size_t>(b) * P + p] = ci[p * 16 + c];
+    }
+  }
+}
+
+}  // namespace dflash

@@ -1,0 +1,235 @@
+/*
+ * dflash.h -- C ABI of one DFlash-style block-diffusion drafting step on an
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The step follows the method as the public descriptions state it:
+ *   - "DFlash – Difusión de Bloques para Decodificación Especulativa en Flash"
+ *     (gist.science 2602.06036), section 2.2 "Diseño de Inferencia": target hidden
+ *     states from several layers are concatenated, projected to one context
+ *     feature, pushed through every drafter layer's K/V projections into the
+ *     drafter's KV cache; the drafter predicts a whole block of mask tokens in one
+ *     forward pass.  Section 2.3: the drafter shares embedding and LM head with
+ *     the target; a block starts with a clean anchor token.
+ *   - "DFlash 2: optimización de la decodificación especulativa para inferencia
+ *     paralela de LLMs" (kerneldigest.dev), "Arquitectura del Sistema": item 1,
+ *     the Path Selector (top-16 candidates per position, low-rank bilinear
+ *     scoring of adjacent pairs on 256-d embeddings under a context gate, greedy
+ *     walk); item 2, the dynamic short convolution (two taps, depthwise,
+ *     content-dependent, one correction per 16 channels, before and after every
+ *     attention and FFN sublayer); "Flujo de Inferencia con DFlash 2": the target
+ *     verifies the chosen block in one pass, accepted tokens are kept.
+ *   - "FlexDraft" (gist.science 2605.20022), "Metodología" item 1: mask tokens
+ *     attend bidirectionally inside their block and to the clean prefix.
+ *
+ * Conventions (all calls):
+ *   - Every pointer argument named as device memory must point to memory of the
+ *     current HIP device; the caller owns it.  The library keeps no pointer after
+ *     a call returns and holds no global state; calls on different streams may run
+ *     concurrently if they do not share output or workspace memory.
+ *   - Struct arguments (dflash_config, dflash_weights, dflash_kv) are host memory,
+ *     read during the call only.
+ *   - All device work is enqueued on `stream`; no call synchronises the host or
+ *     copies device -> host.  Outputs are valid once the stream reaches them.
+ *   - Arguments are validated before anything is enqueued: on a non-zero return
+ *     nothing was launched and outputs are untouched.  DFLASH_E_HIP means a launch
+ *     failed part-way; outputs are then undefined.
+ *   - Linear weights are [out, in] row-major.  Matrices are in the storage type
+ *     `cfg->dtype` (bf16 bit patterns or fp32); GEMMs accumulate in fp32.
+ *   - Workspace: caller-provided device memory of at least the size the matching
+ *     *_workspace_bytes() query returns, 256-byte aligned.  Its content on entry is
+ *     irrelevant.
+ */
+#ifndef DFLASH_H
+#define DFLASH_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define DFLASH_OK              0
+#define DFLASH_E_INVAL        -1   /* null pointer, non-positive size, bad enum value     */
+#define DFLASH_E_UNSUPPORTED  -2   /* a shape the kernels do not handle (see each call)   */
+#define DFLASH_E_WORKSPACE    -3   /* workspace smaller than the size query returns       */
+#define DFLASH_E_CAPACITY     -4   /* host-known sizes exceed the KV cache capacity       */
+#define DFLASH_E_HIP          -5   /* a HIP launch failed                                 */
+
+/* storage types */
+#define DFLASH_F32   0
+#define DFLASH_BF16  1
+
+/* path choice */
+#define DFLASH_PATH_GREEDY 0       /* greedy walk over the pair scores (the method's rule) */
+#define DFLASH_PATH_EXACT  1       /* maximum total score (dynamic programming)             */
+
+#define DFLASH_MAX_LAYERS 16
+#define DFLASH_BLOCK 16            /* rows of a drafted block                               */
+#define DFLASH_TOPK  16            /* candidates kept per position                          */
+#define DFLASH_CONV_SITES 4        /* conv sites per layer: pre-attn, post-attn, pre-FFN, post-FFN */
+
+typedef struct dflash_config {
+  int32_t dtype;          /* DFLASH_BF16 or DFLASH_F32                                        */
+  int32_t d_model;        /* drafter width d; multiple of 64                                  */
+  int32_t n_heads;        /* query heads H                                                    */
+  int32_t n_kv_heads;     /* key/value heads Hkv; H / Hkv in {1, 2, 4}                        */
+  int32_t head_dim;       /* 64 or 128                                                        */
+  int32_t d_ffn;          /* SwiGLU width; multiple of 64                                     */
+  int32_t n_layers;       /* 1 .. DFLASH_MAX_LAYERS                                           */
+  int32_t n_feat_layers;  /* sampled target layers n_s                                        */
+  int32_t d_target;       /* target width d_t; n_s * d_t multiple of 64                       */
+  int32_t vocab;          /* V; multiple of 16, >= 16                                         */
+  int32_t ps_dim;         /* Path Selector embedding width; 256                               */
+  int32_t ps_rank;        /* rank r of the bilinear form; 1 .. 256                            */
+  int32_t use_conv;       /* 0/1: dynamic short conv around every sublayer                    */
+  int32_t use_gate;       /* 0/1: context gate in the Path Selector                           */
+  float   rms_eps;        /* RMSNorm epsilon (1e-6)                                           */
+  float   rope_theta;     /* rotary base (1e6)                                                */
+} dflash_config;
+
+typedef struct dflash_layer_weights {
+  const void* w_q;        /* [H*hd, d]                                                        */
+  const void* w_k;        /* [Hkv*hd, d]  (used by both inject and draft)                      */
+  const void* w_v;        /* [Hkv*hd, d]                                                      */
+  const void* w_o;        /* [d, H*hd]                                                        */
+  const void* w_gate;     /* [d_ffn, d]                                                       */
+  const void* w_up;       /* [d_ffn, d]                                                       */
+  const void* w_down;     /* [d, d_ffn]                                                       */
+  const void* g_attn;     /* [d] RMSNorm gain before attention                                */
+  const void* g_ffn;      /* [d] RMSNorm gain before the FFN                                  */
+  const void* conv_gen[DFLASH_CONV_SITES];  /* [2*d/16, d] correction generator (use_conv)    */
+  const void* conv_w0[DFLASH_CONV_SITES];   /* [d] static tap on the current row (use_conv)   */
+  const void* conv_w1[DFLASH_CONV_SITES];   /* [d] static tap on the previous row (use_conv)  */
+} dflash_layer_weights;
+
+typedef struct dflash_weights {
+  const void* embed;      /* [V, d] token embedding shared with the target                    */
+  const void* lm_head;    /* [V, d] LM head shared with the target                            */
+  const void* w_fc;       /* [d, n_s*d_t] context-feature projection                          */
+  const void* g_fc;       /* [d] RMSNorm gain of the context feature                          */
+  const void* g_final;    /* [d] final RMSNorm gain                                           */
+  const void* ps_left;    /* [ps_dim, d] left-role projection of token embeddings             */
+  const void* ps_right;   /* [ps_dim, d] right-role projection                                 */
+  const void* ps_gate;    /* [ps_dim, d] context gate (use_gate)                              */
+  const void* ps_u;       /* [r, ps_dim] left factor of the bilinear form                      */
+  const void* ps_v;       /* [r, ps_dim] right factor                                          */
+  dflash_layer_weights layers[DFLASH_MAX_LAYERS];
+} dflash_weights;
+
+/* The drafter's KV cache of injected context, one pair of arrays per layer.
+ *   k[l]  : [batch][Hkv][cap][hd]   keys after RoPE, position-major
+ *   vt[l] : [batch][Hkv][hd][cap]   values, transposed (position contiguous)
+ * cap is a multiple of 32.  Row p of sequence b holds context position p.  Rows at
+ * or beyond a sequence's context length are never read by dflash_draft_block. */
+typedef struct dflash_kv {
+  void*   k[DFLASH_MAX_LAYERS];
+  void*   vt[DFLASH_MAX_LAYERS];
+  int32_t batch;
+  int32_t cap;
+} dflash_kv;
+
+/* Context-feature fusion + KV injection ("DFlash ...", section 2.2).
+ *
+ * For every new context row r of sequence b (rows row_off[b] .. row_off[b]+n_new[b]-1
+ * of `hidden`, i = r - row_off[b] < n_new[b]):
+ *   F_r = RMSNorm(hidden_r * w_fc^T; g_fc)            (rounded to the storage type)
+ *   k[l][b][:, pos0[b]+i, :]  = RoPE(F_r * w_k^T, pos0[b]+i)   for every layer l
+ *   vt[l][b][:, :, pos0[b]+i] = F_r * w_v^T
+ *
+ * hidden  : device [n_rows, n_s*d_t] storage type, row-major.
+ * row_off : device int32 [batch+1], non-decreasing, row_off[batch] <= n_rows.
+ * pos0    : device int32 [batch], first cache position written for each sequence.
+ * n_new   : device int32 [batch], rows injected; rows of a sequence past n_new[b] are
+ *           computed but not written (lets a caller inject accept_len+1 rows of a
+ *           fixed 16-row buffer without a host round trip).
+ * Rows whose position would reach kv->cap are skipped (never written).
+ * n_rows > 0.  Workspace: dflash_inject_workspace_bytes(cfg, n_rows).
+ */
+int dflash_inject_context(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv,
+                          const void* hidden, int32_t n_rows, const int32_t* row_off,
+                          const int32_t* pos0, const int32_t* n_new, int32_t batch,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* One parallel forward pass of the drafter over a 16-row block per sequence
+ * ("DFlash ...", sections 2.2-2.3; "DFlash 2 ...", item 2 for the conv).
+ *
+ * ctx_len   : device int32 [batch], context rows in the cache (0 .. kv->cap).  Block
+ *             row j sits at position ctx_len[b] + j.
+ * block_ids : device int32 [batch, 16] token ids of the block (anchor and mask ids).
+ * Block attention: each block row attends to cache rows 0 .. ctx_len[b]-1 and to all
+ * 16 block rows (bidirectional in the block); nothing else.
+ * Outputs (device):
+ *   cand_ids     int32 [batch, 16, 16]  top-16 token ids per row, best first
+ *   cand_logits  float [batch, 16, 16]  their logits (fp32)
+ *   final_hidden float [batch, 16, d]   final RMSNorm output (input of the gate)
+ *   logits       float [batch, 16, V]   optional (NULL to skip): all logits
+ * Order of the top-16: larger logit first, lower id on equal logits.
+ * Workspace: dflash_draft_workspace_bytes(cfg, batch, kv->cap).
+ */
+int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv,
+                       const int32_t* ctx_len, const int32_t* block_ids, int32_t batch,
+                       int32_t* cand_ids, float* cand_logits, float* final_hidden, float* logits,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Path Selector ("DFlash 2 ...", "Arquitectura del Sistema", item 1).
+ *
+ * Drafted positions are block rows n_fixed..15 (P = 16 - n_fixed); n_fixed is 0 (all
+ * rows are mask tokens) or 1 (row 0 is the anchor block_ids[b][0]).  With
+ *   z_l(t) = ps_left * E[t],  z_r(t) = ps_right * E[t]                (256-d)
+ *   gamma_i = sigmoid(ps_gate * xhat_i)  (use_gate; else 1), xhat_i = final_hidden row i
+ *   phi_i(a, t) = (ps_u * z_l(a)) . (ps_v * (gamma_i (.) z_r(t)))
+ * the score of candidate j at drafted position p given left token a is
+ *   cand_logits[p][j] + phi_{row p}(a, cand_ids[p][j])
+ * (no left term at p = 0 without an anchor).  GREEDY walks left to right taking the
+ * best score; EXACT maximises the sum over the block.  Ties: lowest candidate index.
+ *
+ * Inputs: cand_ids int32 [batch,16,16], cand_logits float [batch,16,16],
+ *         final_hidden float [batch,16,d], block_ids int32 [batch,16] (device).
+ * Outputs: path_idx int32 [batch, P] candidate index per drafted position,
+ *          path_ids int32 [batch, P] the chosen token ids,
+ *          pair_scores float [batch, P, 16, 16] optional (NULL to skip): phi of every
+ *          adjacent candidate pair, [p][a][j] = phi(cand[p-1][a], cand[p][j]); at p = 0
+ *          row 0 holds phi(anchor, cand[0][j]) (zeros without anchor), rows 1.. zero.
+ * Workspace: dflash_path_workspace_bytes(cfg, batch).
+ */
+int dflash_select_path(const dflash_config* cfg, const dflash_weights* w,
+                       const int32_t* cand_ids, const float* cand_logits, const float* final_hidden,
+                       const int32_t* block_ids, int32_t n_fixed, int32_t mode, int32_t batch,
+                       int32_t* path_idx, int32_t* path_ids, float* pair_scores,
+                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Greedy verification ("DFlash 2 ...", "Flujo de Inferencia con DFlash 2").
+ *
+ * draft       : device int32 [batch, n_draft]
+ * tgt_logits  : device [batch, n_draft+1, vocab], DFLASH_BF16 or DFLASH_F32 (tgt_dtype);
+ *               row i is the target's next-token logits after the draft prefix through i-1.
+ * accept_len  : device int32 [batch]: a = number of leading drafts equal to the target's
+ *               greedy token of their row.
+ * bonus       : device int32 [batch]: the target's greedy token of row a.
+ * Greedy token = largest logit, lowest id among equal logits.  n_draft in 0..64.
+ * Workspace: dflash_verify_workspace_bytes(batch, n_draft, vocab).
+ */
+int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch,
+                  int32_t n_draft, int32_t vocab, int32_t* accept_len, int32_t* bonus,
+                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace sizes in bytes (0 when the arguments are invalid). */
+size_t dflash_inject_workspace_bytes(const dflash_config* cfg, int32_t n_rows);
+size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t cap);
+size_t dflash_path_workspace_bytes(const dflash_config* cfg, int32_t batch);
+size_t dflash_verify_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab);
+
+/* Check a configuration against what the kernels support: DFLASH_OK, DFLASH_E_INVAL
+ * or DFLASH_E_UNSUPPORTED. */
+int dflash_check_config(const dflash_config* cfg);
+
+/* Static text for a status code. */
+const char* dflash_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DFLASH_H */

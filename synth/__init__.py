@@ -275,7 +275,9 @@ def make_weights(dims: Dims, seed: int, ps_scale: str = "config", conv_scale: st
     ``ps_scale="stress"`` draws the Path Selector at a scale where its pair
     scores are of the order of the logit gaps (at N(0, 0.02^2) they are ~1e-4
     and the chosen path is always the top-1 candidate, which tests nothing).
-    ``conv_scale="stress"`` likewise makes the conv corrections O(0.1).
+    ``conv_scale="stress"`` likewise makes the conv taps and their content-dependent
+    corrections O(0.2) (at the config scale they are ~1e-2 and the conv is nearly the
+    identity).
     Names listed in ``zero`` are returned as all-zero tensors.
     """
     shapes = weight_shapes(dims)
@@ -298,7 +300,7 @@ def make_weights(dims: Dims, seed: int, ps_scale: str = "config", conv_scale: st
             elif name == "ps_gate":
                 std = 1.0 / np.sqrt(d)
         if conv_scale == "stress" and base == "gen":
-            std = 2.0 / np.sqrt(d)
+            std = 0.2 / np.sqrt(d)          # corrections ~N(0, 0.2^2) on unit-RMS rows
         if conv_scale == "stress" and base in ("w0", "w1"):
             std = 0.2
         out[name] = normal(shp, std, seed, 100 + idx, dims.dtype)

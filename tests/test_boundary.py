@@ -1,0 +1,121 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and rejects bad
+arguments before anything reaches the GPU (no compute calls are made here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import block_diffusion_drafter_feature_amd as D
+import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+FAKE = 0x10000          # a non-null pointer value; the rejected calls never dereference it
+
+
+def declared_functions():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:int|size_t|const char\*)\s+(dflash_\w+)\s*\(", txt, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 10
+    lib = ctypes.CDLL(D.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(D.EXPORTED)
+
+
+def test_status_strings():
+    assert D.status_string(0) == "ok"
+    assert "workspace" in D.status_string(D.DFLASH_E_WORKSPACE)
+    assert D.status_string(12345) == "unknown status"
+
+
+@pytest.mark.parametrize("name", synth.WORKLOADS + synth.TEST_WORKLOADS)
+def test_named_configs_are_supported(name):
+    cfg = D.make_config(synth.workload(name).dims)
+    assert D.dflash_check_config(cfg) == D.DFLASH_OK
+    assert D.dflash_draft_workspace_bytes(cfg, 4, 1024) > 0
+    assert D.dflash_inject_workspace_bytes(cfg, 16) > 0
+    assert D.dflash_path_workspace_bytes(cfg, 4) > 0
+
+
+def test_bad_configs_rejected():
+    base = synth.workload("t_small").dims
+    def with_(**kw):
+        c = D.make_config(base)
+        for k, v in kw.items():
+            setattr(c, k, v)
+        return D.dflash_check_config(c)
+    assert with_(dtype=7) == D.DFLASH_E_INVAL
+    assert with_(d_model=0) == D.DFLASH_E_INVAL
+    assert with_(head_dim=96) == D.DFLASH_E_UNSUPPORTED
+    assert with_(n_heads=6, n_kv_heads=4) == D.DFLASH_E_UNSUPPORTED
+    assert with_(n_heads=16, n_kv_heads=2) == D.DFLASH_E_UNSUPPORTED     # GQA group 8
+    assert with_(vocab=1000) == D.DFLASH_E_UNSUPPORTED
+    assert with_(n_layers=17) == D.DFLASH_E_UNSUPPORTED
+    assert with_(d_model=100) == D.DFLASH_E_UNSUPPORTED
+    assert with_(use_conv=2) == D.DFLASH_E_INVAL
+    assert D.dflash_draft_workspace_bytes(D.make_config(base), 0, 64) == 0
+    assert D.dflash_verify_workspace_bytes(1, 65, 100) == 0
+
+
+def _fake_structs(dims, batch=2, cap=64):
+    cfg = D.make_config(dims)
+    w = D.dflash_weights()
+    for k in ("embed", "lm_head", "w_fc", "g_fc", "g_final", "ps_left", "ps_right", "ps_gate", "ps_u", "ps_v"):
+        setattr(w, k, FAKE)
+    for l in range(dims.n_layers):
+        L = w.layers[l]
+        for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down", "g_attn", "g_ffn"):
+            setattr(L, k, FAKE)
+        for s in range(4):
+            L.conv_gen[s] = L.conv_w0[s] = L.conv_w1[s] = FAKE
+    kv = D.dflash_kv(batch=batch, cap=cap)
+    for l in range(dims.n_layers):
+        kv.k[l] = kv.vt[l] = FAKE
+    return cfg, w, kv
+
+
+def _status(fn, *args):
+    with pytest.raises(D.DflashError) as e:
+        fn(*args)
+    return e.value.status
+
+
+def test_calls_validate_before_launch():
+    dims = synth.workload("t_conv").dims
+    cfg, w, kv = _fake_structs(dims)
+    ws_d = D.dflash_draft_workspace_bytes(cfg, 2, 64)
+    ws_i = D.dflash_inject_workspace_bytes(cfg, 8)
+    ws_p = D.dflash_path_workspace_bytes(cfg, 2)
+    S = 1  # any stream value: nothing is enqueued on the error paths
+    # draft
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d - 1, S) == D.DFLASH_E_WORKSPACE
+    assert _status(D.dflash_draft_block, cfg, w, kv, None, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None, FAKE, ws_d * 2, S) == D.DFLASH_E_CAPACITY
+    w.layers[1].conv_w1[3] = None
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, S) == D.DFLASH_E_INVAL
+    w.layers[1].conv_w1[3] = FAKE
+    kv.cap = 48
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, S) == D.DFLASH_E_UNSUPPORTED
+    kv.cap = 64
+    # inject
+    assert _status(D.dflash_inject_context, cfg, w, kv, FAKE, 8, FAKE, FAKE, FAKE, 2, FAKE, ws_i - 1, S) == D.DFLASH_E_WORKSPACE
+    assert _status(D.dflash_inject_context, cfg, w, kv, FAKE, 0, FAKE, FAKE, FAKE, 2, FAKE, ws_i, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_inject_context, cfg, w, kv, None, 8, FAKE, FAKE, FAKE, 2, FAKE, ws_i, S) == D.DFLASH_E_INVAL
+    # path
+    assert _status(D.dflash_select_path, cfg, w, FAKE, FAKE, FAKE, FAKE, 2, 0, 2, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_select_path, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 5, 2, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_select_path, cfg, w, FAKE, FAKE, None, FAKE, 1, 0, 2, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_select_path, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 0, 2, FAKE, FAKE, None, FAKE, ws_p - 1, S) == D.DFLASH_E_WORKSPACE
+    # verify
+    ws_v = D.dflash_verify_workspace_bytes(2, 15, 1024)
+    assert _status(D.dflash_verify, FAKE, FAKE, D.DFLASH_BF16, 2, 65, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_UNSUPPORTED
+    assert _status(D.dflash_verify, FAKE, FAKE, 9, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_verify, FAKE, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v - 1, S) == D.DFLASH_E_WORKSPACE
+    assert _status(D.dflash_verify, None, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_INVAL
