@@ -1,0 +1,297 @@
+#!/usr/bin/env python3
+"""Throughput of one DFlash-style drafting step on one MI355X: drafted 16-token blocks/s.
+
+A step is one pass of the whole hot path over one batch of synthetic inputs already
+resident in HBM:
+  1. dflash_inject_context : inject 16 new context rows per sequence (positions L-16..L-1)
+  2. dflash_draft_block    : one parallel forward pass over the 16-row block
+  3. dflash_select_path    : Path Selector pair scores + greedy path
+  4. dflash_verify         : greedy acceptance against the target logits
+blocks/s = batch x steps/s.  The default workload is the Qwen3-8B-shaped drafter at
+batch 1, context 4096 (``--workload c2``); c1, c3, c4, c5 select the other shapes.
+
+Prints ONE JSON line (rank 0): the metric, a roofline object for the dominant kernel
+(algorithmic bytes or flops per launch over its event-timed duration inside the timed
+region), the per-kernel breakdown, and the CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK = 8.0e12            # MI355X HBM3E, bytes/s
+MFMA_PEAK = {"bf16": 2.5e15, "f32": 157.3e12}   # dense matrix-core peaks (fp32: vector/matrix fp32)
+METRIC = "drafted 16-token blocks/sec at 1 GPU; attention HBM GB/s and GEMM MFMA % of peak"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 to skip)")
+    ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel breakdown pass")
+    return ap.parse_args()
+
+
+# ------------------------------------------------------------------ algorithmic work per probed kernel
+
+def kernel_work(dims, batch, ctx_lens):
+    """(bytes, flops) each probed kernel must move / compute at minimum, per launch."""
+    e = 2 if dims.dtype == "bf16" else 4
+    d, H, Hkv, hd, F, V = dims.d, dims.n_heads, dims.n_kv_heads, dims.head_dim, dims.d_ffn, dims.vocab
+    M = 16 * batch
+    hq, hk = H * hd, Hkv * hd
+    kv_rows = sum(ctx_lens)
+    w = {
+        "lm_head": (V * d * e + M * d * e + M * V * 4, 2 * M * V * d),
+        "qkv": ((hq + 2 * hk) * d * e + M * d * e + M * (hq + 2 * hk) * e, 2 * M * (hq + 2 * hk) * d),
+        "o": (d * hq * e + M * hq * e + 2 * M * d * 4, 2 * M * d * hq),
+        "gate_up": (2 * F * d * e + M * d * e + M * F * e, 2 * M * 2 * F * d),
+        "down": (d * F * e + M * F * e + 2 * M * d * 4, 2 * M * d * F),
+        # block attention of one layer: every context K and V row once, plus q, block k/v, o
+        "attn": (2 * kv_rows * hk * e + M * hq * e * 2 + 2 * M * hk * e,
+                 2 * 2 * batch * 16 * H * hd * (sum(ctx_lens) / max(batch, 1) + 16)),
+        "topk": (M * V * 4, 0),
+        "inject_fc": (d * dims.d_cat * e + M * dims.d_cat * e + M * d * 4, 2 * M * d * dims.d_cat),
+        "inject_kv": (dims.n_layers * 2 * hk * d * e + M * d * e + M * dims.n_layers * 2 * hk * e,
+                      2 * M * dims.n_layers * 2 * hk * d),
+    }
+    return w
+
+
+def step_bytes(dims, batch, ctx_lens):
+    """Algorithmic HBM bytes of one whole step (weights once, KV once per layer, target logits)."""
+    e = 2 if dims.dtype == "bf16" else 4
+    d, H, Hkv, hd, F, V, L = dims.d, dims.n_heads, dims.n_kv_heads, dims.head_dim, dims.d_ffn, dims.vocab, dims.n_layers
+    per_layer = ((H + 2 * Hkv) * hd * d + d * H * hd + 3 * F * d) * e
+    conv = (4 * (2 * (d // 16) * d + 2 * d) * e) if dims.use_conv else 0
+    weights = L * (per_layer + conv) + V * d * e + d * dims.d_cat * e + (3 * dims.ps_dim * d + 2 * dims.ps_rank * dims.ps_dim) * e
+    kv = L * 2 * sum(ctx_lens) * Hkv * hd * e
+    tgt = batch * 16 * V * e
+    return weights + kv + tgt
+
+
+# ------------------------------------------------------------------ CPU oracle baseline
+
+def cpu_baseline(wl, W, seconds):
+    import numpy as np
+
+    import oracle
+    import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    dims = wl.dims
+    L = int(wl.ctx_lens[0])
+    cap = ((L + 16 + 31) // 32) * 32
+    K, V = synth.make_cache(dims, [L], cap, wl.seed)
+    kc = [oracle.decode(K[l, 0], dims.dtype) for l in range(dims.n_layers)]
+    vc = [oracle.decode(V[l, 0], dims.dtype) for l in range(dims.n_layers)]
+    hid = synth.make_hidden(dims, 16, wl.seed, key=2)
+    ids = synth.make_block_ids(dims, 1, wl.seed, 1)[0]
+    T = oracle.decode(synth.make_target_logits(dims, 1, 15, wl.seed, planted="random" if wl.planted else "none")[0],
+                      dims.dtype)
+    m = oracle.Model(dims, W)
+    pos = np.arange(L - 16, L) if L >= 16 else np.arange(0)
+    t0 = time.perf_counter()
+    oracle.drafting_step(m, kc, vc, L, hid[:len(pos)], pos, ids, T)        # warm-up: decodes the weights
+    warm = time.perf_counter() - t0
+    n, t0 = 0, time.perf_counter()
+    while True:
+        oracle.drafting_step(m, kc, vc, L, hid[:len(pos)], pos, ids, T)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or (n >= 1 and el + el / n > 3 * seconds):
+            break
+    return {"value": n / el, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
+            "host_cpus": len(os.sched_getaffinity(0)),
+            "sample": f"{n} full drafting step(s) of sequence 0 (inject 16 rows, draft, path, verify) at the "
+                      f"{wl.name} shapes, context {L}, float64 NumPy oracle; {el:.1f} s timed after a "
+                      f"{warm:.1f} s warm-up that decodes the weights"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the drafting step is built and "
+              "measured on a single MI355X. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import block_diffusion_drafter_feature_amd as D
+    import synth
+
+    def log(*a):
+        print(*a, file=sys.stderr, flush=True)
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    D.lib()
+    wl = synth.workload(args.workload)
+    dims = wl.dims
+    B, cap = wl.batch, wl.cap
+    ctx = np.asarray(wl.ctx_lens, dtype=np.int32)
+    t0 = time.time()
+    W = synth.make_weights(dims, wl.seed)
+    dr = D.Drafter(dims, W)
+    log(f"[bench] {wl.name}: weights {dr.nbytes() / 1e9:.2f} GB on device ({time.time() - t0:.1f} s)")
+    if args.cpu_seconds <= 0:
+        del W
+        W = None
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()  # noqa: E731
+    dt_t = D.torch_dtype(dims)
+
+    # ---- prefill: inject every context row (device-generated target hiddens, in chunks)
+    cache = D.KVCache(dims, B, cap)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(wl.seed)
+    chunk = 16384
+    ws_inj = D.Workspace()
+    t0 = time.time()
+    for b in range(B):
+        for r0 in range(0, int(ctx[b]), chunk):
+            n = min(chunk, int(ctx[b]) - r0)
+            hid = torch.randn((n, dims.d_cat), generator=gen, device="cuda", dtype=torch.float32).to(dt_t)
+            nb = D.dflash_inject_workspace_bytes(dr.cfg, n)
+            sub = D.dflash_kv(batch=1, cap=cap)
+            for l in range(dims.n_layers):
+                sub.k[l] = cache.k[l][b].data_ptr()
+                sub.vt[l] = cache.vt[l][b].data_ptr()
+            D.dflash_inject_context(dr.cfg, dr.w, sub, hid, n, i32([0, n]), i32([r0]), i32([n]), 1,
+                                    ws_inj.get(nb), nb)
+    torch.cuda.synchronize()
+    log(f"[bench] prefill of {int(ctx.sum())} context rows ({time.time() - t0:.1f} s)")
+
+    # ---- step inputs (resident in HBM before timing)
+    new_hid = D.to_device(synth.make_hidden(dims, 16 * B, wl.seed, key=2), dims)
+    row_off = i32(np.arange(B + 1) * 16)
+    pos0 = i32(np.maximum(ctx - 16, 0))
+    n_new = i32(np.minimum(ctx, 16))
+    ctx_t = i32(ctx)
+    ids = synth.make_block_ids(dims, B, wl.seed, 1)
+    ids_t = i32(ids)
+    T = D.to_device(synth.make_target_logits(dims, B, 15, wl.seed, planted="random" if wl.planted else "none"), dims)
+    tdt = D.DFLASH_BF16 if dims.dtype == "bf16" else D.DFLASH_F32
+    ci = torch.zeros((B, 16, 16), dtype=torch.int32, device="cuda")
+    cl = torch.zeros((B, 16, 16), dtype=torch.float32, device="cuda")
+    fh = torch.zeros((B, 16, dims.d), dtype=torch.float32, device="cuda")
+    pidx = torch.zeros((B, 15), dtype=torch.int32, device="cuda")
+    pids = torch.zeros((B, 15), dtype=torch.int32, device="cuda")
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    bon = torch.zeros(B, dtype=torch.int32, device="cuda")
+    nb_i = D.dflash_inject_workspace_bytes(dr.cfg, 16 * B)
+    nb_d = D.dflash_draft_workspace_bytes(dr.cfg, B, cap)
+    nb_p = D.dflash_path_workspace_bytes(dr.cfg, B)
+    nb_v = D.dflash_verify_workspace_bytes(B, 15, dims.vocab)
+    ws_i, ws_d, ws_p, ws_v = (torch.empty(n, dtype=torch.uint8, device="cuda") for n in (nb_i, nb_d, nb_p, nb_v))
+
+    def step(probes=None):
+        D.dflash_inject_context(dr.cfg, dr.w, cache.kv, new_hid, 16 * B, row_off, pos0, n_new, B, ws_i, nb_i,
+                                probes=probes.struct if probes else None)
+        D.dflash_draft_block(dr.cfg, dr.w, cache.kv, ctx_t, ids_t, B, ci, cl, fh, None, ws_d, nb_d,
+                             probes=probes.struct if probes else None)
+        D.dflash_select_path(dr.cfg, dr.w, ci, cl, fh, ids_t, 1, D.DFLASH_PATH_GREEDY, B, pidx, pids, None,
+                             ws_p, nb_p)
+        D.dflash_verify(pids, T, tdt, B, 15, dims.vocab, acc, bon, ws_v, nb_v)
+
+    work = kernel_work(dims, B, wl.ctx_lens)
+    dominant = "lm_head"
+    live = [D.Probes(("lm_head", "attn")) for _ in range(args.steps)]
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for k in range(args.steps):
+        step(live[k])
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / args.steps
+    value = B * 1000.0 / ms
+    log(f"[bench] {args.steps} steps: {ms:.3f} ms/step, {value:.1f} blocks/s")
+
+    def avg_ms(probes, name):
+        return float(np.mean([p.ms(name) for p in probes]))
+
+    def roof(name, t_ms):
+        by, fl = work[name]
+        peak_mf = MFMA_PEAK[dims.dtype]
+        bound = "mfma" if fl / max(by, 1) > peak_mf / HBM_PEAK else "hbm"
+        if bound == "hbm":
+            a = by / (t_ms * 1e-3)
+            return {"bound": "hbm", "achieved": round(a / 1e9, 1), "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                    "frac": round(a / HBM_PEAK, 4), "algorithmic_bytes": int(by), "ms": round(t_ms, 4)}
+        a = fl / (t_ms * 1e-3)
+        return {"bound": "mfma", "achieved": round(a / 1e12, 1), "peak": peak_mf / 1e12, "unit": "TFLOP/s",
+                "frac": round(a / peak_mf, 4), "algorithmic_flops": int(fl), "ms": round(t_ms, 4)}
+
+    dom = roof(dominant, avg_ms(live, dominant))
+    attn = roof("attn", avg_ms(live, "attn"))
+    traffic = None
+    tpath = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
+    if os.path.exists(tpath):
+        try:
+            import hashlib
+            tr = json.load(open(tpath))
+            src = hashlib.sha256(open(os.path.join(ROOT, "block_diffusion_drafter_feature_amd", "csrc",
+                                                   tr["source"]), "rb").read()).hexdigest()
+            if tr.get("kernel") == dominant and tr.get("source_sha256") == src:
+                traffic = tr["bytes_per_launch"]
+        except Exception:
+            traffic = None
+    roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
+    roofline.update({"traffic": traffic, "kernel": f"{dominant} GEMM (gemm_skinny_kernel<..., EpiLogits>)",
+                     "algorithmic_bytes_per_launch": dom.get("algorithmic_bytes"), "ms_per_launch": dom["ms"]})
+
+    breakdown = {}
+    if not args.no_breakdown:
+        pr = [D.Probes() for _ in range(5)]
+        for p in pr:
+            step(p)
+        torch.cuda.synchronize()
+        for n in ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv"):
+            breakdown[n] = roof(n, avg_ms(pr, n)) if n != "topk" else {"ms": round(avg_ms(pr, n), 4)}
+
+    cpu = None
+    if W is not None:
+        log(f"[bench] CPU oracle sample ({args.cpu_seconds:.0f} s budget) ...")
+        cpu = cpu_baseline(wl, W, args.cpu_seconds)
+        log(f"[bench] CPU oracle: {cpu['value']:.4f} blocks/s on {cpu['cores']} BLAS threads")
+
+    sb = step_bytes(dims, B, wl.ctx_lens)
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "blocks/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dims.dtype, "data": "synthetic (seeded random-init weights, N(0,1) hiddens/logits)",
+        "config": {"workload": f"{wl.name}: {wl.description}", "batch": B,
+                   "context": list(map(int, wl.ctx_lens)) if B <= 4 else {"min": int(ctx.min()), "max": int(ctx.max()),
+                                                                          "sum": int(ctx.sum())},
+                   "block": 16, "d_model": dims.d, "heads": f"{dims.n_heads}q/{dims.n_kv_heads}kv x {dims.head_dim}",
+                   "d_ffn": dims.d_ffn, "layers": dims.n_layers, "fusion": f"{dims.d_cat}->{dims.d}",
+                   "vocab": dims.vocab, "topk": 16, "conv": bool(dims.use_conv), "gate": bool(dims.use_gate),
+                   "path": "greedy", "parallelism": "single GPU"},
+        "roofline": roofline,
+        "attention": {k: attn[k] for k in ("bound", "achieved", "peak", "unit", "frac", "ms")},
+        "step_roofline": {"algorithmic_bytes": int(sb), "hbm_bound_ms": round(sb / HBM_PEAK * 1e3, 4),
+                          "frac": round(sb / HBM_PEAK * 1e3 / ms, 4)},
+        "breakdown": breakdown,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -33,6 +33,8 @@ DFLASH_PATH_GREEDY = 0
 DFLASH_PATH_EXACT = 1
 MAX_LAYERS = 16
 CONV_SITES = 4
+PROBES = ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv")
+N_PROBES = len(PROBES)
 
 EXPORTED = (
     "dflash_inject_context", "dflash_draft_block", "dflash_select_path", "dflash_verify",
@@ -73,6 +75,10 @@ class dflash_weights(ctypes.Structure):
                 ("layers", dflash_layer_weights * MAX_LAYERS)]
 
 
+class dflash_probes(ctypes.Structure):
+    _fields_ = [("begin", _vp * N_PROBES), ("end", _vp * N_PROBES)]
+
+
 class dflash_kv(ctypes.Structure):
     _fields_ = [("k", _vp * MAX_LAYERS), ("vt", _vp * MAX_LAYERS), ("batch", _i32), ("cap", _i32)]
 
@@ -91,10 +97,11 @@ def lib() -> ctypes.CDLL:
                                "`python -m block_diffusion_drafter_feature_amd.build`")
         L = ctypes.CDLL(LIB_PATH)
         P, PC = ctypes.POINTER, ctypes.c_size_t
-        cfgp, wp, kvp = P(dflash_config), P(dflash_weights), P(dflash_kv)
+        cfgp, wp, kvp, pp = P(dflash_config), P(dflash_weights), P(dflash_kv), P(dflash_probes)
         sig = {
-            "dflash_inject_context": ([cfgp, wp, kvp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, PC, _vp], ctypes.c_int),
-            "dflash_draft_block": ([cfgp, wp, kvp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
+            "dflash_inject_context": ([cfgp, wp, kvp, _vp, _i32, _vp, _vp, _vp, _i32, _vp, PC, pp, _vp], ctypes.c_int),
+            "dflash_draft_block": ([cfgp, wp, kvp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, PC, pp, _vp],
+                                   ctypes.c_int),
             "dflash_select_path": ([cfgp, wp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, PC, _vp],
                                    ctypes.c_int),
             "dflash_verify": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
@@ -162,19 +169,23 @@ def dflash_verify_workspace_bytes(batch: int, n_draft: int, vocab: int) -> int:
     return lib().dflash_verify_workspace_bytes(batch, n_draft, vocab)
 
 
+def _probes(p):
+    return None if p is None else ctypes.byref(p)
+
+
 def dflash_inject_context(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, workspace_bytes,
-                          stream=None) -> None:
+                          probes=None, stream=None) -> None:
     _check("dflash_inject_context", lib().dflash_inject_context(
         ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), _ptr(hidden), n_rows, _ptr(row_off), _ptr(pos0),
-        _ptr(n_new), batch, _ptr(workspace), workspace_bytes, _stream(stream)))
+        _ptr(n_new), batch, _ptr(workspace), workspace_bytes, _probes(probes), _stream(stream)))
 
 
 def dflash_draft_block(cfg, w, kv, ctx_len, block_ids, batch, cand_ids, cand_logits, final_hidden, logits,
-                       workspace, workspace_bytes, stream=None) -> None:
+                       workspace, workspace_bytes, probes=None, stream=None) -> None:
     _check("dflash_draft_block", lib().dflash_draft_block(
         ctypes.byref(cfg), ctypes.byref(w), ctypes.byref(kv), _ptr(ctx_len), _ptr(block_ids), batch,
         _ptr(cand_ids), _ptr(cand_logits), _ptr(final_hidden), _ptr(logits), _ptr(workspace), workspace_bytes,
-        _stream(stream)))
+        _probes(probes), _stream(stream)))
 
 
 def dflash_select_path(cfg, w, cand_ids, cand_logits, final_hidden, block_ids, n_fixed, mode, batch, path_idx,
@@ -190,6 +201,64 @@ def dflash_verify(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_le
     _check("dflash_verify", lib().dflash_verify(
         _ptr(draft), _ptr(tgt_logits), tgt_dtype, batch, n_draft, vocab, _ptr(accept_len), _ptr(bonus),
         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+_hip = None
+
+
+def hip() -> ctypes.CDLL:
+    """The HIP runtime (for events the library records on the caller's stream)."""
+    global _hip
+    if _hip is None:
+        lib()                     # the library links the runtime; load it first
+        for name in ("libamdhip64.so", "libamdhip64.so.7", "libamdhip64.so.6"):
+            try:
+                _hip = ctypes.CDLL(name)
+                break
+            except OSError:
+                continue
+        if _hip is None:
+            raise RuntimeError("HIP runtime (libamdhip64.so) not found")
+        _hip.hipEventCreate.argtypes = [ctypes.POINTER(_vp)]
+        _hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), _vp, _vp]
+        _hip.hipEventDestroy.argtypes = [_vp]
+    return _hip
+
+
+class Probes:
+    """HIP events for the timing probes of inject/draft calls (see dflash_probes)."""
+
+    def __init__(self, names=PROBES):
+        H = hip()
+        self.struct = dflash_probes()
+        self.ev = {}
+        for n in names:
+            pair = []
+            for _ in range(2):
+                e = _vp()
+                if H.hipEventCreate(ctypes.byref(e)) != 0:
+                    raise RuntimeError("hipEventCreate failed")
+                pair.append(e)
+            i = PROBES.index(n)
+            self.struct.begin[i] = pair[0]
+            self.struct.end[i] = pair[1]
+            self.ev[n] = pair
+
+    def ms(self, name: str) -> float:
+        b, e = self.ev[name]
+        out = ctypes.c_float()
+        st = hip().hipEventElapsedTime(ctypes.byref(out), b, e)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({st}) for probe {name}")
+        return float(out.value)
+
+    def __del__(self):
+        try:
+            for b, e in self.ev.values():
+                hip().hipEventDestroy(b)
+                hip().hipEventDestroy(e)
+        except Exception:
+            pass
 
 
 # ------------------------------------------------------------------ memory helpers (allocation / layout only)

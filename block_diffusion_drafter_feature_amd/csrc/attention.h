@@ -181,28 +181,39 @@ __global__ __launch_bounds__(64 * (G / HW)) void block_attn_kernel(AttnArgs<T> a
   }
 }
 
-// Merge the S split partials of every (sequence, head) in split order; write the
-// attention output rounded to the storage type, [B*16][H*hd].
+// Merge the S split partials of one query row (sequence b, head, block row q) in split
+// order; write the attention output rounded to the storage type, [B*16][H*hd].
+// grid (16, H, B), HD threads (one per output dim).
 template <typename T, int HD>
-__global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
-                                                           const float* __restrict__ part_ml, T* __restrict__ out,
-                                                           int H, int Hkv, int S) {
-  const int head = blockIdx.x, b = blockIdx.y;
+__global__ __launch_bounds__(HD) void attn_combine_kernel(const float* __restrict__ part_o,
+                                                          const float* __restrict__ part_ml, T* __restrict__ out,
+                                                          int H, int Hkv, int S) {
+  __shared__ float w[64];
+  __shared__ float inv_den;
+  const int q = blockIdx.x, head = blockIdx.y, b = blockIdx.z, dim = threadIdx.x;
   const int G = H / Hkv, kvh = head / G, hl = head % G;
-  for (int e = threadIdx.x; e < 16 * HD; e += blockDim.x) {
-    const int q = e / HD, dim = e % HD;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s)
-      M = fmaxf(M, part_ml[((((static_cast<size_t>(b) * Hkv + kvh) * S + s) * G + hl) * 16 + q) * 2]);
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < S; ++s) {
-      const size_t pb = (((static_cast<size_t>(b) * Hkv + kvh) * S + s) * G + hl) * 16 + q;
-      const float w = exp2f(part_ml[pb * 2] - M);
-      den += w * part_ml[pb * 2 + 1];
-      num += w * part_o[pb * HD + dim];
-    }
-    out[(static_cast<size_t>(b) * 16 + q) * H * HD + head * HD + dim] = from_f<T>(num / den);
+  const size_t base = ((static_cast<size_t>(b) * Hkv + kvh) * S) * G * 16;   // split 0
+  const size_t sstride = static_cast<size_t>(G) * 16;
+  const size_t row = hl * 16 + q;
+  if (threadIdx.x < 64) {
+    // split weights: exp2(m_s - max m), computed by the first wave
+    const int s = threadIdx.x;
+    const float m = s < S ? part_ml[(base + s * sstride + row) * 2] : -INFINITY;
+    const float l = s < S ? part_ml[(base + s * sstride + row) * 2 + 1] : 0.f;
+    float M = m;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float ws = s < S ? exp2f(m - M) : 0.f;
+    w[s] = ws;
+    // fixed-order denominator: lane 0 sums the split terms in split order
+    float den = 0.f;
+    for (int t = 0; t < S; ++t) den += __shfl(ws * l, t, 64);
+    if (s == 0) inv_den = 1.f / den;
   }
+  __syncthreads();
+  float num = 0.f;
+  for (int s = 0; s < S; ++s) num += w[s] * part_o[(base + s * sstride + row) * HD + dim];
+  out[(static_cast<size_t>(b) * 16 + q) * H * HD + head * HD + dim] = from_f<T>(num * inv_den);
 }
 
 }  // namespace dflash

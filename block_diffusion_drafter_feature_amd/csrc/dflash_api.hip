@@ -10,6 +10,8 @@
 #include "gemm.h"
 #include "select.h"
 
+#include <algorithm>
+
 using namespace dflash;
 
 namespace {
@@ -92,12 +94,18 @@ template <typename T>
 struct InjectWs {
   float* hf;   // [rows][d] fused feature before its norm
   T* f;        // [rows][d] fused feature, storage type
+  float* scratch;
+  size_t scratch_bytes;
 };
 template <typename T>
 InjectWs<T> carve_inject(Carver& cv, const dflash_config* c, int rows) {
   InjectWs<T> w;
-  w.hf = cv.take<float>(static_cast<size_t>(rows) * c->d_model);
-  w.f = cv.take<T>(static_cast<size_t>(rows) * c->d_model);
+  const int d = c->d_model, dcat = c->n_feat_layers * c->d_target;
+  w.hf = cv.take<float>(static_cast<size_t>(rows) * d);
+  w.f = cv.take<T>(static_cast<size_t>(rows) * d);
+  w.scratch_bytes = std::max(splitk_scratch_bytes<T>(rows, dcat, (d + 15) / 16),
+                             splitk_scratch_bytes<T>(rows, d, c->n_layers * 2 * c->n_kv_heads * c->head_dim / 16));
+  w.scratch = cv.take<float>(w.scratch_bytes / sizeof(float) + 1);
   return w;
 }
 
@@ -124,6 +132,8 @@ struct DraftWs {
   float* logits;  // [M][V] (when the caller passes none)
   float* tk_v;    // [M][n_chunks][16]
   int32_t* tk_i;
+  float* scratch;
+  size_t scratch_bytes;
   int S;
 };
 template <typename T>
@@ -147,6 +157,17 @@ DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
   w.logits = cv.take<float>(M * c->vocab);
   w.tk_v = cv.take<float>(M * nch * 16);
   w.tk_i = cv.take<int32_t>(M * nch * 16);
+  const int Mi = static_cast<int>(M), di = c->d_model, hqi = c->n_heads * c->head_dim;
+  const int hki = c->n_kv_heads * c->head_dim, F = c->d_ffn;
+  size_t sc = 0;
+  sc = std::max(sc, splitk_scratch_bytes<T>(Mi, di, (hqi + 2 * hki) / 16));
+  sc = std::max(sc, splitk_scratch_bytes<T>(Mi, hqi, di / 16));
+  sc = std::max(sc, splitk_scratch_bytes<T>(Mi, di, 2 * (F / 16)));
+  sc = std::max(sc, splitk_scratch_bytes<T>(Mi, F, di / 16));
+  sc = std::max(sc, splitk_scratch_bytes<T>(Mi, di, c->vocab / 16));
+  if (c->use_conv) sc = std::max(sc, splitk_scratch_bytes<T>(Mi, di, (2 * (di / 16) + 15) / 16));
+  w.scratch_bytes = sc;
+  w.scratch = cv.take<float>(sc / sizeof(float) + 1);
   return w;
 }
 
@@ -156,17 +177,24 @@ struct PathWs {
   int32_t* tokens;  // [B][T]
   float* z;         // [B][T][2*PD]
   float* gamma;     // [B*16][PD]
-  float* lam;       // [B][T][r]
-  float* rho;       // [B][T][r]
+  float* S;         // [B][16][16][16] pair scores
+  float* scratch;
+  size_t scratch_bytes;
 };
+template <typename X>
 PathWs carve_path(Carver& cv, const dflash_config* c, int B) {
   PathWs w;
   const size_t T = kPathSlots;
   w.tokens = cv.take<int32_t>(B * T);
   w.z = cv.take<float>(B * T * 2 * c->ps_dim);
   w.gamma = cv.take<float>(static_cast<size_t>(B) * 16 * c->ps_dim);
-  w.lam = cv.take<float>(B * T * c->ps_rank);
-  w.rho = cv.take<float>(B * T * c->ps_rank);
+  w.S = cv.take<float>(static_cast<size_t>(B) * 16 * 256);
+  size_t sc = 0;
+  for (int nf = 0; nf < 2; ++nf)
+    sc = std::max(sc, splitk_scratch_bytes<X>(B * (16 * (16 - nf) + nf), c->d_model, 2 * c->ps_dim / 16));
+  sc = std::max(sc, splitk_scratch_bytes<X>(16 * B, c->d_model, c->ps_dim / 16));
+  w.scratch_bytes = sc;
+  w.scratch = cv.take<float>(sc / sizeof(float) + 1);
   return w;
 }
 
@@ -181,6 +209,17 @@ VerifyWs carve_verify(Carver& cv, int B, int n_draft, int V) {
   w.pi = cv.take<int32_t>(static_cast<size_t>(B) * (n_draft + 1) * nch);
   return w;
 }
+
+struct Probe {
+  const dflash_probes* p;
+  hipStream_t s;
+  void begin(int i) const {
+    if (p && p->begin[i]) (void)hipEventRecord(p->begin[i], s);
+  }
+  void end(int i) const {
+    if (p && p->end[i]) (void)hipEventRecord(p->end[i], s);
+  }
+};
 
 #define LAUNCH_CHECK()                             \
   do {                                             \
@@ -207,13 +246,16 @@ SegW<T> seg1(const void* p, int rows, int K) {
 template <typename T>
 int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv* kv, const void* hidden,
                 int rows, const int32_t* row_off, const int32_t* pos0, const int32_t* n_new, int B, void* ws,
-                hipStream_t s) {
+                const Probe& pr, hipStream_t s) {
   Carver cv(ws);
   InjectWs<T> W = carve_inject<T>(cv, c, rows);
   const int d = c->d_model, dcat = c->n_feat_layers * c->d_target;
   {
     EpiStore<T> e{seg1<T>(w->w_fc, d, dcat), W.hf, d, STORE};
-    GEMM_CHECK((run_gemm<T, T>(static_cast<const T*>(hidden), dcat, nullptr, rows, dcat, (d + 15) / 16, e, s)));
+    pr.begin(DFLASH_PROBE_INJECT_FC);
+    GEMM_CHECK((run_gemm<T, T>(static_cast<const T*>(hidden), dcat, nullptr, rows, dcat, (d + 15) / 16, e, s,
+                               W.scratch, W.scratch_bytes)));
+    pr.end(DFLASH_PROBE_INJECT_FC);
   }
   rmsnorm_kernel<T><<<rows, 256, 0, s>>>(W.hf, static_cast<const T*>(w->g_fc), d, c->rms_eps, W.f, nullptr);
   LAUNCH_CHECK();
@@ -235,7 +277,9 @@ int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv
   e.pos0 = pos0;
   e.n_new = n_new;
   const int nvt = c->n_layers * 2 * c->n_kv_heads * c->head_dim / 16;
-  GEMM_CHECK((run_gemm<T, T>(W.f, d, nullptr, rows, d, nvt, e, s)));
+  pr.begin(DFLASH_PROBE_INJECT_KV);
+  GEMM_CHECK((run_gemm<T, T>(W.f, d, nullptr, rows, d, nvt, e, s, W.scratch, W.scratch_bytes)));
+  pr.end(DFLASH_PROBE_INJECT_KV);
   return DFLASH_OK;
 }
 
@@ -259,9 +303,9 @@ hipError_t run_attention(const dflash_config* c, const AttnArgs<T>& a, int B, T*
     e = G == 1 ? launch_attn<T, 128, 1>(a, B, s) : G == 2 ? launch_attn<T, 128, 2>(a, B, s) : launch_attn<T, 128, 4>(a, B, s);
   }
   if (e != hipSuccess) return e;
-  dim3 grid(c->n_heads, B);
-  if (c->head_dim == 64) attn_combine_kernel<T, 64><<<grid, 256, 0, s>>>(a.part_o, a.part_ml, out, c->n_heads, c->n_kv_heads, a.S);
-  else attn_combine_kernel<T, 128><<<grid, 256, 0, s>>>(a.part_o, a.part_ml, out, c->n_heads, c->n_kv_heads, a.S);
+  dim3 grid(16, c->n_heads, B);
+  if (c->head_dim == 64) attn_combine_kernel<T, 64><<<grid, 64, 0, s>>>(a.part_o, a.part_ml, out, c->n_heads, c->n_kv_heads, a.S);
+  else attn_combine_kernel<T, 128><<<grid, 128, 0, s>>>(a.part_o, a.part_ml, out, c->n_heads, c->n_kv_heads, a.S);
   return hipGetLastError();
 }
 
@@ -278,7 +322,8 @@ int pre_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site
   rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, nullptr, W.uf);
   LAUNCH_CHECK();
   EpiStore<T> e{seg1<T>(L.conv_gen[site], 2 * (d / 16), d), W.delta, 2 * (d / 16), STORE};
-  GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, e, s)));
+  GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, e, s, W.scratch,
+                                   W.scratch_bytes)));
   conv_apply_kernel<T><<<M, 256, 0, s>>>(W.uf, W.delta, static_cast<const T*>(L.conv_w0[site]),
                                          static_cast<const T*>(L.conv_w1[site]), d, 0, W.ut, nullptr);
   LAUNCH_CHECK();
@@ -288,17 +333,22 @@ int pre_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site
 // post-sublayer: x += A W^T, through the conv when enabled
 template <typename T, typename AS>
 int post_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site, const void* wmat, const AS* A,
-                  int K, int M, DraftWs<T>& W, hipStream_t s) {
+                  int K, int M, DraftWs<T>& W, const Probe& pr, int probe, hipStream_t s) {
   const int d = c->d_model;
   if (!c->use_conv) {
     EpiStore<T> e{seg1<T>(wmat, d, K), W.x, d, ADD};
-    GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s)));
+    pr.begin(probe);
+    GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s, W.scratch, W.scratch_bytes)));
+    pr.end(probe);
     return DFLASH_OK;
   }
   EpiStore<T> e{seg1<T>(wmat, d, K), W.uf, d, STORE};
-  GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s)));
+  pr.begin(probe);
+  GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s, W.scratch, W.scratch_bytes)));
+  pr.end(probe);
   EpiStore<T> g{seg1<T>(L.conv_gen[site], 2 * (d / 16), d), W.delta, 2 * (d / 16), STORE};
-  GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, g, s)));
+  GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, g, s, W.scratch,
+                                   W.scratch_bytes)));
   conv_apply_kernel<T><<<M, 256, 0, s>>>(W.uf, W.delta, static_cast<const T*>(L.conv_w0[site]),
                                          static_cast<const T*>(L.conv_w1[site]), d, 1, nullptr, W.x);
   LAUNCH_CHECK();
@@ -308,7 +358,8 @@ int post_sublayer(const dflash_config* c, const dflash_layer_weights& L, int sit
 template <typename T>
 int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv* kv, const int32_t* ctx_len,
                const int32_t* block_ids, int B, int32_t* cand_ids, float* cand_logits, float* final_hidden,
-               float* logits, void* ws, hipStream_t s) {
+               float* logits, void* ws, const dflash_probes* probes, hipStream_t s) {
+  const Probe P0{probes, s}, PN{nullptr, s};
   Carver cv(ws);
   DraftWs<T> W = carve_draft<T>(cv, c, B, kv->cap);
   const int M = 16 * B, d = c->d_model, H = c->n_heads, Hkv = c->n_kv_heads, hd = c->head_dim;
@@ -318,31 +369,43 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
   LAUNCH_CHECK();
   for (int l = 0; l < c->n_layers; ++l) {
     const dflash_layer_weights& L = w->layers[l];
+    const Probe& pr = l == 0 ? P0 : PN;
     // attention sublayer
     if ((rc = pre_sublayer<T>(c, L, 0, L.g_attn, M, W, s))) return rc;
     EpiQKV<T> eq{static_cast<const T*>(L.w_q), static_cast<const T*>(L.w_k), static_cast<const T*>(L.w_v),
                  d, H, Hkv, hd, c->rope_theta, ctx_len, W.q, W.kb, W.vbt};
-    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, (hq + 2 * Hkv * hd) / 16, eq, s)));
+    pr.begin(DFLASH_PROBE_QKV);
+    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, (hq + 2 * Hkv * hd) / 16, eq, s, W.scratch,
+                               W.scratch_bytes)));
+    pr.end(DFLASH_PROBE_QKV);
     AttnArgs<T> aa{W.q, W.kb, W.vbt, static_cast<const T*>(kv->k[l]), static_cast<const T*>(kv->vt[l]), ctx_len,
                    W.part_o, W.part_ml, H, Hkv, kv->cap, W.S, 1.4426950408889634f / sqrtf(static_cast<float>(hd))};
+    pr.begin(DFLASH_PROBE_ATTN);
     GEMM_CHECK(run_attention<T>(c, aa, B, W.o, s));
-    if ((rc = post_sublayer<T, T>(c, L, 1, L.w_o, W.o, hq, M, W, s))) return rc;
+    pr.end(DFLASH_PROBE_ATTN);
+    if ((rc = post_sublayer<T, T>(c, L, 1, L.w_o, W.o, hq, M, W, pr, DFLASH_PROBE_O, s))) return rc;
     // feed-forward sublayer
     if ((rc = pre_sublayer<T>(c, L, 2, L.g_ffn, M, W, s))) return rc;
     EpiSwiGLU<T> ef{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), d, F, W.h};
-    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, 2 * (F / 16), ef, s)));
-    if ((rc = post_sublayer<T, T>(c, L, 3, L.w_down, W.h, F, M, W, s))) return rc;
+    pr.begin(DFLASH_PROBE_GATE_UP);
+    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, 2 * (F / 16), ef, s, W.scratch, W.scratch_bytes)));
+    pr.end(DFLASH_PROBE_GATE_UP);
+    if ((rc = post_sublayer<T, T>(c, L, 3, L.w_down, W.h, F, M, W, pr, DFLASH_PROBE_DOWN, s))) return rc;
   }
   rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(w->g_final), d, c->rms_eps, W.ut, final_hidden);
   LAUNCH_CHECK();
   float* lg = logits ? logits : W.logits;
-  EpiStore<T> el{seg1<T>(w->lm_head, V, d), lg, V, STORE};
-  GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, V / 16, el, s)));
+  EpiLogits<T> el{{seg1<T>(w->lm_head, V, d), lg, V, STORE}};
+  P0.begin(DFLASH_PROBE_LM_HEAD);
+  GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, V / 16, el, s, W.scratch, W.scratch_bytes)));
+  P0.end(DFLASH_PROBE_LM_HEAD);
   const int nch = (V + kTopkChunk - 1) / kTopkChunk;
+  P0.begin(DFLASH_PROBE_TOPK);
   topk_partial_kernel<<<dim3(nch, M), 256, 0, s>>>(lg, V, V, kTopkChunk, W.tk_v, W.tk_i);
   LAUNCH_CHECK();
   topk_final_kernel<<<M, 64, 0, s>>>(W.tk_v, W.tk_i, nch, cand_ids, cand_logits);
   LAUNCH_CHECK();
+  P0.end(DFLASH_PROBE_TOPK);
   return DFLASH_OK;
 }
 
@@ -353,7 +416,7 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
               const float* final_hidden, const int32_t* block_ids, int n_fixed, int mode, int B, int32_t* path_idx,
               int32_t* path_ids, float* pair_scores, void* ws, hipStream_t s) {
   Carver cv(ws);
-  PathWs W = carve_path(cv, c, B);
+  PathWs W = carve_path<T>(cv, c, B);
   const int d = c->d_model, PD = c->ps_dim, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
   path_tokens_kernel<<<B, 256, 0, s>>>(cand_ids, block_ids, n_fixed, W.tokens);
   LAUNCH_CHECK();
@@ -367,17 +430,20 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
     sw.n_seg = 2;
     sw.K = d;
     EpiStore<T> e{sw, W.z, 2 * PD, STORE};
-    GEMM_CHECK((run_gemm<T, T>(static_cast<const T*>(w->embed), d, W.tokens, B * Tn, d, 2 * PD / 16, e, s)));
+    GEMM_CHECK((run_gemm<T, T>(static_cast<const T*>(w->embed), d, W.tokens, B * Tn, d, 2 * PD / 16, e, s,
+                               W.scratch, W.scratch_bytes)));
   }
   if (c->use_gate) {
     EpiStore<T> e{seg1<T>(w->ps_gate, PD, d), W.gamma, PD, SIGMOID};
-    GEMM_CHECK((run_gemm<T, float>(final_hidden, d, nullptr, 16 * B, d, PD / 16, e, s)));
+    GEMM_CHECK((run_gemm<T, float>(final_hidden, d, nullptr, 16 * B, d, PD / 16, e, s, W.scratch,
+                                   W.scratch_bytes)));
   }
-  path_factors_kernel<T><<<B, 256, 0, s>>>(W.z, c->use_gate ? W.gamma : nullptr, static_cast<const T*>(w->ps_u),
-                                           static_cast<const T*>(w->ps_v), PD, c->ps_rank, n_fixed, W.lam, W.rho);
+  const size_t smem = 2 * 16 * (c->ps_rank + 1) * sizeof(float);
+  path_scores_kernel<T><<<dim3(P, B), 256, smem, s>>>(W.z, c->use_gate ? W.gamma : nullptr,
+                                                      static_cast<const T*>(w->ps_u), static_cast<const T*>(w->ps_v),
+                                                      PD, c->ps_rank, n_fixed, W.S, pair_scores);
   LAUNCH_CHECK();
-  path_walk_kernel<<<B, 256, 0, s>>>(W.lam, W.rho, c->ps_rank, cand_ids, cand_logits, n_fixed, mode, path_idx,
-                                     path_ids, pair_scores);
+  path_walk_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, mode, path_idx, path_ids);
   LAUNCH_CHECK();
   return DFLASH_OK;
 }
@@ -423,7 +489,8 @@ size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch, int
 size_t dflash_path_workspace_bytes(const dflash_config* cfg, int32_t batch) {
   if (check_config(cfg) != DFLASH_OK || batch <= 0) return 0;
   Carver cv(nullptr);
-  carve_path(cv, cfg, batch);
+  if (cfg->dtype == DFLASH_BF16) carve_path<bf16_t>(cv, cfg, batch);
+  else carve_path<float>(cv, cfg, batch);
   return cv.off;
 }
 
@@ -436,7 +503,8 @@ size_t dflash_verify_workspace_bytes(int32_t batch, int32_t n_draft, int32_t voc
 
 int dflash_inject_context(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, const void* hidden,
                           int32_t n_rows, const int32_t* row_off, const int32_t* pos0, const int32_t* n_new,
-                          int32_t batch, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                          int32_t batch, void* workspace, size_t workspace_bytes, const dflash_probes* probes,
+                          hipStream_t stream) {
   int rc;
   if ((rc = check_config(cfg))) return rc;
   if ((rc = check_weights(cfg, w, false, true, false))) return rc;
@@ -444,15 +512,16 @@ int dflash_inject_context(const dflash_config* cfg, const dflash_weights* w, con
   if ((rc = check_kv(cfg, kv, batch))) return rc;
   if (!hidden || !row_off || !pos0 || !n_new || !workspace) return DFLASH_E_INVAL;
   if (workspace_bytes < dflash_inject_workspace_bytes(cfg, n_rows)) return DFLASH_E_WORKSPACE;
+  const Probe pr{probes, stream};
   if (cfg->dtype == DFLASH_BF16)
-    return inject_impl<bf16_t>(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, stream);
-  return inject_impl<float>(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, stream);
+    return inject_impl<bf16_t>(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, pr, stream);
+  return inject_impl<float>(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, pr, stream);
 }
 
 int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv, const int32_t* ctx_len,
                        const int32_t* block_ids, int32_t batch, int32_t* cand_ids, float* cand_logits,
                        float* final_hidden, float* logits, void* workspace, size_t workspace_bytes,
-                       hipStream_t stream) {
+                       const dflash_probes* probes, hipStream_t stream) {
   int rc;
   if ((rc = check_config(cfg))) return rc;
   if ((rc = check_weights(cfg, w, true, false, false))) return rc;
@@ -462,9 +531,9 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const 
   if (workspace_bytes < dflash_draft_workspace_bytes(cfg, batch, kv->cap)) return DFLASH_E_WORKSPACE;
   if (cfg->dtype == DFLASH_BF16)
     return draft_impl<bf16_t>(cfg, w, kv, ctx_len, block_ids, batch, cand_ids, cand_logits, final_hidden, logits,
-                              workspace, stream);
+                              workspace, probes, stream);
   return draft_impl<float>(cfg, w, kv, ctx_len, block_ids, batch, cand_ids, cand_logits, final_hidden, logits,
-                           workspace, stream);
+                           workspace, probes, stream);
 }
 
 int dflash_select_path(const dflash_config* cfg, const dflash_weights* w, const int32_t* cand_ids,

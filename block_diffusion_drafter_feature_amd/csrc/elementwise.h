@@ -16,21 +16,47 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E, con
 }
 
 // u = x / sqrt(mean(x^2) + eps) * g.  Writes u rounded to T (out_t) and/or in fp32 (out_f).
+// One work-group per row; each thread owns 4-float groups c = tid, tid + 256, ... and issues
+// all of its row loads before reducing (d <= 256 * 4 * 16 per row in one pass of registers).
 template <typename T>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const T* __restrict__ g, int d,
                                                       float eps, T* __restrict__ out_t, float* __restrict__ out_f) {
+  constexpr int MAXV = 16;
   __shared__ float red[8];
   const int m = blockIdx.x;
-  const float* xr = x + static_cast<size_t>(m) * d;
+  const f32x4_t* xr = reinterpret_cast<const f32x4_t*>(x + static_cast<size_t>(m) * d);
+  const int nv = d >> 2;
+  f32x4_t v[MAXV];
   float ss = 0.f;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) ss += xr[k] * xr[k];
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    v[i] = c < nv ? xr[c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
+  for (int c = threadIdx.x + 256 * MAXV; c < nv; c += 256) {
+    const f32x4_t t = xr[c];
+    ss += t[0] * t[0] + t[1] * t[1] + t[2] * t[2] + t[3] * t[3];
+  }
   ss = block_sum(ss, red);
   const float inv = 1.f / sqrtf(ss / d + eps);
-  for (int k = threadIdx.x; k < d; k += blockDim.x) {
-    const float u = xr[k] * inv * to_f<T>(g[k]);
-    if (out_t) out_t[static_cast<size_t>(m) * d + k] = from_f<T>(u);
-    if (out_f) out_f[static_cast<size_t>(m) * d + k] = u;
+  auto emit = [&](int c, const f32x4_t& t) {
+    float u[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) u[e] = t[e] * inv * to_f<T>(g[4 * c + e]);
+    if (out_t) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out_t[static_cast<size_t>(m) * d + 4 * c + e] = from_f<T>(u[e]);
+    }
+    if (out_f) *reinterpret_cast<f32x4_t*>(out_f + static_cast<size_t>(m) * d + 4 * c) = f32x4_t{u[0], u[1], u[2], u[3]};
+  };
+#pragma unroll
+  for (int i = 0; i < MAXV; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    if (c < nv) emit(c, v[i]);
   }
+  for (int c = threadIdx.x + 256 * MAXV; c < nv; c += 256) emit(c, xr[c]);
 }
 
 // Dynamic short conv, apply step, for block rows m (row j = m % 16 of its block):

@@ -56,6 +56,11 @@ struct EpiStore {
   }
 };
 
+// LM-head logits: a plain fp32 store, kept as its own type so that the LM-head GEMM is a
+// kernel of its own in profiles.
+template <typename T>
+struct EpiLogits : EpiStore<T> {};
+
 // ------------------------------------------------------------------ block Q/K/V with RoPE
 
 template <typename T>

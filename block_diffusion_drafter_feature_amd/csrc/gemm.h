@@ -137,10 +137,13 @@ template <typename T> struct TiledCfg;
 template <> struct TiledCfg<bf16_t> { static constexpr int BK = 64; };
 template <> struct TiledCfg<float> { static constexpr int BK = 32; };
 
+// With partial != nullptr (split-K), work-group z covers K range [z*kslice, (z+1)*kslice)
+// and stores its raw fp32 tile to partial[z][m][ldp] instead of running the epilogue.
 template <typename T, typename AS, class Epi>
 __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ A, int lda,
                                                          const int32_t* __restrict__ arows, int M, int K,
-                                                         Epi epi) {
+                                                         Epi epi, int kslice, float* __restrict__ partial,
+                                                         int ldp) {
   typedef Frag<T> F;
   typedef typename F::type frag_t;
   constexpr int BM = 128, BN = 128, BK = TiledCfg<T>::BK;
@@ -207,12 +210,13 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ 
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  const int KT = K / BK;
-  gload(0);
+  const int kofs = blockIdx.z * kslice;
+  const int KT = (partial ? kslice : K) / BK;
+  gload(kofs);
   sstore();
   __syncthreads();
   for (int kt = 0; kt < KT; ++kt) {
-    if (kt + 1 < KT) gload((kt + 1) * BK);
+    if (kt + 1 < KT) gload(kofs + (kt + 1) * BK);
 #pragma unroll
     for (int ks = 0; ks < BK / 32; ++ks) {
       frag_t af[4], bfr[4];
@@ -232,6 +236,19 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ 
     }
   }
 
+  if (partial) {
+    float* pz = partial + static_cast<size_t>(blockIdx.z) * M * ldp;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm * 64 + i * 16 + 4 * g + e;
+          if (m < M) pz[static_cast<size_t>(m) * ldp + vt0 * 16 + wn * 64 + j * 16 + r16] = acc[i][j][e];
+        }
+    return;
+  }
   // epilogue, one 64-row half at a time through LDS
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -257,9 +274,50 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ 
   }
 }
 
+// Split-K reduction: sum the partial tiles in z order, then the epilogue.  One thread per
+// (row, virtual column).
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* __restrict__ partial, int M,
+                                                                   int ldp, int ks, int n_vtiles, Epi epi) {
+  const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (e >= static_cast<size_t>(M) * ldp) return;
+  const int m = static_cast<int>(e / ldp), col = static_cast<int>(e % ldp);
+  const int vt = col >> 4, c = col & 15;
+  if (vt >= n_vtiles) return;
+  const int pcol = ((vt ^ Epi::PX) << 4) | (c ^ Epi::PC);
+  float v = 0.f, pv = 0.f;
+  for (int z = 0; z < ks; ++z) {
+    const float* pz = partial + static_cast<size_t>(z) * M * ldp + static_cast<size_t>(m) * ldp;
+    v += pz[col];
+    pv += pz[pcol];
+  }
+  epi.apply(vt, m, c, v, pv);
+}
+
 // ---------------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------------
+
+// Split-K factor of the tiled GEMM: split K only when the output tiles alone cannot
+// fill the 256 compute units; keep >= 2 K slabs per split.
+template <typename T>
+inline int splitk_plan(int M, int K, int n_vtiles) {
+  if (M <= 64) return 1;
+  const int BK = TiledCfg<T>::BK;
+  const int tiles = ((n_vtiles + 7) / 8) * ((M + 127) / 128);
+  if (tiles >= 192) return 1;
+  int ks = (256 + tiles - 1) / tiles;
+  ks = ks > 8 ? 8 : ks;
+  const int slabs = K / BK;
+  while (ks > 1 && (slabs % ks || slabs / ks < 2)) --ks;
+  return ks;
+}
+
+template <typename T>
+inline size_t splitk_scratch_bytes(int M, int K, int n_vtiles) {
+  const int ks = splitk_plan<T>(M, K, n_vtiles);
+  return ks > 1 ? static_cast<size_t>(ks) * M * (((n_vtiles + 7) / 8) * 128) * sizeof(float) : 0;
+}
 
 template <typename T, typename AS, int MT, int NT, class Epi>
 static hipError_t launch_skinny_nw(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
@@ -275,17 +333,26 @@ static hipError_t launch_skinny_nw(const AS* A, int lda, const int32_t* arows, i
 }
 
 // n_vtiles: number of virtual 16-column tiles (multiple of 2 when Epi::PX == 1).
-// K: multiple of 64.
+// K: multiple of 64.  scratch: split-K partials (>= splitk_scratch_bytes, or nullptr: no split).
 template <typename T, typename AS, class Epi>
 static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
-                           hipStream_t s) {
+                           hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0) {
   if (M <= 0 || n_vtiles <= 0) return hipSuccess;
   constexpr int NT = Epi::PX ? 2 : 1;
   if (M <= 16) return launch_skinny_nw<T, AS, 1, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 32) return launch_skinny_nw<T, AS, 2, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 64) return launch_skinny_nw<T, AS, 4, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
-  dim3 grid((n_vtiles + 7) / 8, (M + 127) / 128);
-  gemm_tiled_kernel<T, AS, Epi><<<grid, 256, 0, s>>>(A, lda, arows, M, K, epi);
+  const int ntx = (n_vtiles + 7) / 8, ldp = ntx * 128;
+  int ks = splitk_plan<T>(M, K, n_vtiles);
+  if (!scratch || scratch_bytes < splitk_scratch_bytes<T>(M, K, n_vtiles)) ks = 1;
+  dim3 grid(ntx, (M + 127) / 128, ks);
+  gemm_tiled_kernel<T, AS, Epi><<<grid, 256, 0, s>>>(A, lda, arows, M, K, epi, K / ks, ks > 1 ? scratch : nullptr,
+                                                     ldp);
+  if (ks > 1) {
+    const size_t n = static_cast<size_t>(M) * ldp;
+    gemm_splitk_epilogue_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(scratch, M, ldp, ks,
+                                                                                          n_vtiles, epi);
+  }
   return hipGetLastError();
 }
 

@@ -5,6 +5,7 @@
 
 #include "common.h"
 #include <limits.h>
+#include <type_traits>
 
 namespace dflash {
 
@@ -230,77 +231,107 @@ __global__ void path_tokens_kernel(const int32_t* __restrict__ cand_ids, const i
   }
 }
 
-// Low-rank factors: lam[t] = U z_l(t) for left-neighbour tokens, rho[t] = V (gamma (.) z_r(t))
-// for right tokens.  grid (batch), 256 threads.  z: [B][T][2*PD] fp32 (left | right).
+// fp32 fragment of 8 consecutive values of a T row (bf16 widened exactly)
 template <typename T>
-__global__ __launch_bounds__(256) void path_factors_kernel(const float* __restrict__ z, const float* __restrict__ gamma,
-                                                           const T* __restrict__ U, const T* __restrict__ Vf, int PD,
-                                                           int r, int n_fixed, float* __restrict__ lam,
-                                                           float* __restrict__ rho) {
-  const int b = blockIdx.x, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
-  const float* zb = z + static_cast<size_t>(b) * Tn * 2 * PD;
-  for (int e = threadIdx.x; e < Tn * r; e += blockDim.x) {
-    const int t = e / r, k = e % r;
-    const int p = t < 16 * P ? t / 16 : -1;                   // drafted position of slot t (-1: anchor)
-    const bool is_left = (p >= 0 && p < P - 1) || (p < 0);
-    const bool is_right = p >= 0 && (p > 0 || n_fixed == 1);
-    const float* zl = zb + static_cast<size_t>(t) * 2 * PD;
-    const float* zr = zl + PD;
-    if (is_left) {
-      const T* u = U + static_cast<size_t>(k) * PD;
-      float s = 0.f;
-      for (int i = 0; i < PD; ++i) s += to_f<T>(u[i]) * zl[i];
-      lam[(static_cast<size_t>(b) * Tn + t) * r + k] = s;
+__device__ __forceinline__ f32x8_t load8_as_f32(const T* p) {
+  if constexpr (std::is_same<T, float>::value) {
+    return Frag<float>::load(p);
+  } else {
+    const u32x4_t u = *reinterpret_cast<const u32x4_t*>(p);
+    f32x8_t r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      r[2 * j] = __uint_as_float(u[j] << 16);
+      r[2 * j + 1] = __uint_as_float(u[j] & 0xffff0000u);
     }
-    if (is_right) {
-      const T* v = Vf + static_cast<size_t>(k) * PD;
-      const float* gm = gamma ? gamma + (static_cast<size_t>(b) * 16 + n_fixed + p) * PD : nullptr;
-      float s = 0.f;
-      if (gm) for (int i = 0; i < PD; ++i) s += to_f<T>(v[i]) * (gm[i] * zr[i]);
-      else for (int i = 0; i < PD; ++i) s += to_f<T>(v[i]) * zr[i];
-      rho[(static_cast<size_t>(b) * Tn + t) * r + k] = s;
-    }
+    return r;
   }
 }
 
-// Pair scores and the walk.  grid (batch), 256 threads.
-//   S[p][a][j] = lam(cand[p-1][a]) . rho(cand[p][j])   (p >= 1)
-//   S[0][0][j] = lam(anchor) . rho(cand[0][j])          (anchor only)
-// Greedy: c_0 = argmax_j (l_0[j] + S[0][0][j]), c_p = argmax_j (l_p[j] + S[p][c_{p-1}][j]).
-// Exact:  best_0[j] = l_0[j] + S[0][0][j]; best_p[j] = l_p[j] + max_a (best_{p-1}[a] + S[p][a][j]).
-// All sums in fp32 in exactly this order; ties to the lowest index.
-__global__ __launch_bounds__(256) void path_walk_kernel(const float* __restrict__ lam, const float* __restrict__ rho,
-                                                        int r, const int32_t* __restrict__ cand_ids,
-                                                        const float* __restrict__ cand_logits, int n_fixed, int mode,
-                                                        int32_t* __restrict__ path_idx, int32_t* __restrict__ path_ids,
-                                                        float* __restrict__ pair_scores) {
-  __shared__ float S[16][16][16];
-  __shared__ float best[16];
-  __shared__ int back[16][16];
-  const int b = blockIdx.x, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
-  const float* lb = lam + static_cast<size_t>(b) * Tn * r;
-  const float* rb = rho + static_cast<size_t>(b) * Tn * r;
-  for (int e = threadIdx.x; e < P * 256; e += blockDim.x) {
-    const int p = e / 256, a = (e / 16) % 16, j = e % 16;
-    float s = 0.f;
-    int lt = -1;
-    if (p >= 1) lt = (p - 1) * 16 + a;
-    else if (n_fixed == 1 && a == 0) lt = 16 * P;   // anchor slot
-    if (lt >= 0) {
-      const float* x = lb + static_cast<size_t>(lt) * r;
-      const float* y = rb + static_cast<size_t>(p * 16 + j) * r;
-      for (int k = 0; k < r; ++k) s += x[k] * y[k];
+// Pair scores of one drafted position p of one sequence.  grid (P, B), 256 threads.
+//   lam[a] = U z_l(left token a)                 (left tokens: candidates of p-1, or the anchor at p = 0)
+//   rho[j] = V (gamma_p (.) z_r(candidate j of p))
+//   S[p][a][j] = lam[a] . rho[j]
+// lam and rho are 16 x r products on the fp32 matrix cores (K = PD); S is a plain fp32 dot
+// product over r in order k = 0..r-1.  z: [B][Tn][2*PD] fp32 (left | right halves).
+template <typename T>
+__global__ __launch_bounds__(256) void path_scores_kernel(const float* __restrict__ z, const float* __restrict__ gamma,
+                                                          const T* __restrict__ U, const T* __restrict__ Vf, int PD,
+                                                          int r, int n_fixed, float* __restrict__ S_out,
+                                                          float* __restrict__ pair_scores) {
+  extern __shared__ float sm[];
+  float* lam = sm;                  // [16][r + 1]
+  float* rho = sm + 16 * (r + 1);   // [16][r + 1]
+  const int p = blockIdx.x, b = blockIdx.y, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
+  const bool has_left = p >= 1 || n_fixed == 1;
+  float* So = S_out + ((static_cast<size_t>(b) * P + p) * 16) * 16;
+  float* Po = pair_scores ? pair_scores + ((static_cast<size_t>(b) * P + p) * 16) * 16 : nullptr;
+  if (!has_left) {
+    for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+      So[e] = 0.f;
+      if (Po) Po[e] = 0.f;
     }
-    S[p][a][j] = s;
-    if (pair_scores) pair_scores[((static_cast<size_t>(b) * P + p) * 16 + a) * 16 + j] = s;
+    return;
+  }
+  const float* zb = z + static_cast<size_t>(b) * Tn * 2 * PD;
+  // left token slot of row a (p = 0: only row 0, the anchor), right token slot of row j
+  const int lslot = p >= 1 ? (p - 1) * 16 + r16 : 16 * P;
+  const int rslot = p * 16 + r16;
+  const float* zl = zb + static_cast<size_t>(lslot) * 2 * PD;
+  const float* zr = zb + static_cast<size_t>(rslot) * 2 * PD + PD;
+  const float* gm = gamma ? gamma + (static_cast<size_t>(b) * 16 + n_fixed + p) * PD : nullptr;
+  const int ntiles = (r + 15) / 16;
+  for (int job = wave; job < 2 * ntiles; job += 4) {
+    const bool left = job < ntiles;
+    const int nt = left ? job : job - ntiles;
+    const int n = nt * 16 + r16;                       // output column (factor index) of this lane
+    const T* wrow = (left ? U : Vf) + static_cast<size_t>(n < r ? n : 0) * PD;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int k0 = 0; k0 < PD; k0 += 32) {
+      const int k = k0 + 8 * g;
+      f32x8_t a = Frag<float>::load(left ? zl + k : zr + k);
+      if (!left && gm) {
+        const f32x8_t gg = Frag<float>::load(gm + k);
+        a *= gg;
+      }
+      f32x8_t w = n < r ? load8_as_f32<T>(wrow + k) : Frag<float>::zero();
+      acc = Frag<float>::mma(acc, a, w);
+    }
+    float* dst = left ? lam : rho;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (n < r) dst[(4 * g + i) * (r + 1) + n] = acc[i];
   }
   __syncthreads();
+  {
+    const int a = threadIdx.x >> 4, j = threadIdx.x & 15;
+    float s = 0.f;
+    if (p >= 1 || a == 0)
+      for (int k = 0; k < r; ++k) s += lam[a * (r + 1) + k] * rho[j * (r + 1) + k];
+    So[a * 16 + j] = s;
+    if (Po) Po[a * 16 + j] = s;
+  }
+}
+
+// The walk over the pair scores.  grid (B), 64 threads (lanes 0..15 hold one candidate each).
+// Greedy: c_0 = argmax_j (l_0[j] + S[0][0][j]), c_p = argmax_j (l_p[j] + S[p][c_{p-1}][j]).
+// Exact:  best_0[j] = l_0[j] + S[0][0][j]; best_p[j] = l_p[j] + max_a (best_{p-1}[a] + S[p][a][j]).
+// fp32, in exactly this order; ties to the lowest index.
+__global__ __launch_bounds__(64) void path_walk_kernel(const float* __restrict__ S_in,
+                                                       const int32_t* __restrict__ cand_ids,
+                                                       const float* __restrict__ cand_logits, int n_fixed, int mode,
+                                                       int32_t* __restrict__ path_idx, int32_t* __restrict__ path_ids) {
+  __shared__ float best[16];
+  __shared__ int back[16][16];
+  __shared__ int chosen[16];
+  const int b = blockIdx.x, P = 16 - n_fixed;
   if (threadIdx.x >= 16) return;
-  // one candidate per lane (lanes 0..15 of wave 0)
   const int j = threadIdx.x;
+  const float* S = S_in + static_cast<size_t>(b) * P * 256;
   const float* lg = cand_logits + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
   const int32_t* ci = cand_ids + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
-  auto argmax16 = [&](float v, int& bi) {   // lanes 0..15: index of the best v, lowest on ties
+  auto argmax16 = [&](float v, int& bi) {
     float bv = v;
     bi = j;
 #pragma unroll
@@ -315,23 +346,24 @@ __global__ __launch_bounds__(256) void path_walk_kernel(const float* __restrict_
     return bv;
   };
   if (mode == 0) {
-    float sc = lg[j] + (n_fixed == 1 ? S[0][0][j] : 0.f);
+    float sc = lg[j] + (n_fixed == 1 ? S[j] : 0.f);
     int c;
     argmax16(sc, c);
-    if (j == 0) path_idx[static_cast<size_t>(b) * P] = c;
+    if (j == 0) chosen[0] = c;
     for (int p = 1; p < P; ++p) {
-      sc = lg[p * 16 + j] + S[p][c][j];
+      sc = lg[p * 16 + j] + S[(p * 16 + c) * 16 + j];
       argmax16(sc, c);
-      if (j == 0) path_idx[static_cast<size_t>(b) * P + p] = c;
+      if (j == 0) chosen[p] = c;
     }
   } else {
-    float bj = lg[j] + (n_fixed == 1 ? S[0][0][j] : 0.f);
+    float bj = lg[j] + (n_fixed == 1 ? S[j] : 0.f);
     best[j] = bj;
     for (int p = 1; p < P; ++p) {
+      __builtin_amdgcn_wave_barrier();
       float bv = -INFINITY;
       int ba = 0;
       for (int a = 0; a < 16; ++a) {
-        const float v = best[a] + S[p][a][j];
+        const float v = best[a] + S[(p * 16 + a) * 16 + j];
         if (v > bv) {
           bv = v;
           ba = a;
@@ -341,23 +373,22 @@ __global__ __launch_bounds__(256) void path_walk_kernel(const float* __restrict_
       bj = lg[p * 16 + j] + bv;
       __builtin_amdgcn_wave_barrier();
       best[j] = bj;
-      __builtin_amdgcn_wave_barrier();
     }
+    __builtin_amdgcn_wave_barrier();
     int c;
     argmax16(bj, c);
     if (j == 0) {
       for (int p = P - 1; p >= 0; --p) {
-        path_idx[static_cast<size_t>(b) * P + p] = c;
+        chosen[p] = c;
         if (p > 0) c = back[p][c];
       }
     }
   }
   __builtin_amdgcn_wave_barrier();
-  if (j == 0) {
-    for (int p = 0; p < P; ++p) {
-      const int c = path_idx[static_cast<size_t>(b) * P + p];
-      path_ids[static_cast<size_t>(b) * P + p] = ci[p * 16 + c];
-    }
+  for (int p = j; p < P; p += 16) {
+    const int c = chosen[p];
+    path_idx[static_cast<size_t>(b) * P + p] = c;
+    path_ids[static_cast<size_t>(b) * P + p] = ci[p * 16 + c];
   }
 }
 

@@ -131,6 +131,25 @@ typedef struct dflash_kv {
   int32_t cap;
 } dflash_kv;
 
+/* Optional timing probes.  When a call receives a non-NULL `probes`, it records
+ * probes->begin[i] / probes->end[i] (each when non-NULL) on `stream` immediately
+ * before the first and after the last launch of stage i.  Per-layer stages are
+ * probed on layer 0.  Used to time single kernels inside a running step. */
+#define DFLASH_PROBE_LM_HEAD    0   /* draft: LM-head GEMM                          */
+#define DFLASH_PROBE_TOPK       1   /* draft: top-16 over the vocabulary            */
+#define DFLASH_PROBE_ATTN       2   /* draft: block attention (+ split combine)     */
+#define DFLASH_PROBE_QKV        3   /* draft: Q/K/V GEMM with RoPE                  */
+#define DFLASH_PROBE_O          4   /* draft: output projection (+ residual)        */
+#define DFLASH_PROBE_GATE_UP    5   /* draft: FFN gate/up GEMM with SwiGLU          */
+#define DFLASH_PROBE_DOWN       6   /* draft: FFN down projection (+ residual)      */
+#define DFLASH_PROBE_INJECT_FC  7   /* inject: context-feature projection GEMM      */
+#define DFLASH_PROBE_INJECT_KV  8   /* inject: K/V projection + RoPE + cache scatter */
+#define DFLASH_N_PROBES         9
+typedef struct dflash_probes {
+  hipEvent_t begin[DFLASH_N_PROBES];
+  hipEvent_t end[DFLASH_N_PROBES];
+} dflash_probes;
+
 /* Context-feature fusion + KV injection ("DFlash ...", section 2.2).
  *
  * For every new context row r of sequence b (rows row_off[b] .. row_off[b]+n_new[b]-1
@@ -146,12 +165,14 @@ typedef struct dflash_kv {
  *           computed but not written (lets a caller inject accept_len+1 rows of a
  *           fixed 16-row buffer without a host round trip).
  * Rows whose position would reach kv->cap are skipped (never written).
- * n_rows > 0.  Workspace: dflash_inject_workspace_bytes(cfg, n_rows).
+ * n_rows > 0.  Workspace: dflash_inject_workspace_bytes(cfg, n_rows).  probes: NULL or
+ * timing probes (see dflash_probes).
  */
 int dflash_inject_context(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv,
                           const void* hidden, int32_t n_rows, const int32_t* row_off,
                           const int32_t* pos0, const int32_t* n_new, int32_t batch,
-                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+                          void* workspace, size_t workspace_bytes, const dflash_probes* probes,
+                          hipStream_t stream);
 
 /* One parallel forward pass of the drafter over a 16-row block per sequence
  * ("DFlash ...", sections 2.2-2.3; "DFlash 2 ...", item 2 for the conv).
@@ -167,12 +188,14 @@ int dflash_inject_context(const dflash_config* cfg, const dflash_weights* w, con
  *   final_hidden float [batch, 16, d]   final RMSNorm output (input of the gate)
  *   logits       float [batch, 16, V]   optional (NULL to skip): all logits
  * Order of the top-16: larger logit first, lower id on equal logits.
- * Workspace: dflash_draft_workspace_bytes(cfg, batch, kv->cap).
+ * Workspace: dflash_draft_workspace_bytes(cfg, batch, kv->cap).  probes: NULL or timing
+ * probes (see dflash_probes).
  */
 int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const dflash_kv* kv,
                        const int32_t* ctx_len, const int32_t* block_ids, int32_t batch,
                        int32_t* cand_ids, float* cand_logits, float* final_hidden, float* logits,
-                       void* workspace, size_t workspace_bytes, hipStream_t stream);
+                       void* workspace, size_t workspace_bytes, const dflash_probes* probes,
+                       hipStream_t stream);
 
 /* Path Selector ("DFlash 2 ...", "Arquitectura del Sistema", item 1).
  *

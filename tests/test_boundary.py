@@ -95,19 +95,19 @@ def test_calls_validate_before_launch():
     ws_p = D.dflash_path_workspace_bytes(cfg, 2)
     S = 1  # any stream value: nothing is enqueued on the error paths
     # draft
-    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d - 1, S) == D.DFLASH_E_WORKSPACE
-    assert _status(D.dflash_draft_block, cfg, w, kv, None, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, S) == D.DFLASH_E_INVAL
-    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None, FAKE, ws_d * 2, S) == D.DFLASH_E_CAPACITY
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d - 1, None, S) == D.DFLASH_E_WORKSPACE
+    assert _status(D.dflash_draft_block, cfg, w, kv, None, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, None, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 3, FAKE, FAKE, FAKE, None, FAKE, ws_d * 2, None, S) == D.DFLASH_E_CAPACITY
     w.layers[1].conv_w1[3] = None
-    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, None, S) == D.DFLASH_E_INVAL
     w.layers[1].conv_w1[3] = FAKE
     kv.cap = 48
-    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, S) == D.DFLASH_E_UNSUPPORTED
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 2, FAKE, FAKE, FAKE, None, FAKE, ws_d, None, S) == D.DFLASH_E_UNSUPPORTED
     kv.cap = 64
     # inject
-    assert _status(D.dflash_inject_context, cfg, w, kv, FAKE, 8, FAKE, FAKE, FAKE, 2, FAKE, ws_i - 1, S) == D.DFLASH_E_WORKSPACE
-    assert _status(D.dflash_inject_context, cfg, w, kv, FAKE, 0, FAKE, FAKE, FAKE, 2, FAKE, ws_i, S) == D.DFLASH_E_INVAL
-    assert _status(D.dflash_inject_context, cfg, w, kv, None, 8, FAKE, FAKE, FAKE, 2, FAKE, ws_i, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_inject_context, cfg, w, kv, FAKE, 8, FAKE, FAKE, FAKE, 2, FAKE, ws_i - 1, None, S) == D.DFLASH_E_WORKSPACE
+    assert _status(D.dflash_inject_context, cfg, w, kv, FAKE, 0, FAKE, FAKE, FAKE, 2, FAKE, ws_i, None, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_inject_context, cfg, w, kv, None, 8, FAKE, FAKE, FAKE, 2, FAKE, ws_i, None, S) == D.DFLASH_E_INVAL
     # path
     assert _status(D.dflash_select_path, cfg, w, FAKE, FAKE, FAKE, FAKE, 2, 0, 2, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
     assert _status(D.dflash_select_path, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 5, 2, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
