@@ -12,7 +12,8 @@
 //  * gemm_skinny : M <= 64 (the drafted block of 1..4 sequences).  Weight
 //    streaming: each work-group owns NT virtual tiles over the whole K; its NW
 //    waves split K, stream their slice of W straight from HBM into registers
-//    (16 B per lane per fragment) and reduce through LDS in a fixed order.
+//    (16 B per lane per fragment, two register stages in flight) and reduce
+//    through LDS in a fixed order.
 //  * gemm_tiled  : M > 64.  128x128 output tile per work-group, A and W tiles
 //    staged through LDS (register prefetch of the next K slab while the matrix
 //    cores work on the current one), 2x2 waves of 64x64.
@@ -34,7 +35,10 @@ __device__ __forceinline__ typename Frag<T>::type load_a(const AS* p) {
 // skinny GEMM
 // ---------------------------------------------------------------------------------
 
-template <typename T, typename AS, int MT, int NT, int NW, class Epi>
+// NT virtual tiles per work-group (and per wave), NW waves splitting K, U k-steps per
+// register stage.  Two register stages alternate: the loads of stage i+1 are in flight
+// while the matrix cores consume stage i.
+template <typename T, typename AS, int MT, int NT, int NW, int U, class Epi>
 __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restrict__ A, int lda,
                                                               const int32_t* __restrict__ arows, int M, int K,
                                                               Epi epi) {
@@ -42,7 +46,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
   typedef typename F::type frag_t;
   constexpr int ROWS = 16 * MT;
   constexpr int TW = 16 * NT;
-  constexpr int U = (MT <= 2) ? 8 : 4;
   __shared__ float red[NW][MT * NT * 256];
   __shared__ float tile[ROWS][TW + 1];
 
@@ -51,8 +54,13 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
   const int vt0 = blockIdx.x * NT;
 
   const T* wp[NT];
+  bool wv[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) wp[nt] = epi.wrow(vt0 + nt, r16);
+  for (int nt = 0; nt < NT; ++nt) {
+    const T* p = epi.wrow(vt0 + nt, r16);
+    wv[nt] = p != nullptr;
+    wp[nt] = p ? p + g * 8 : nullptr;
+  }
   const AS* ap[MT];
   bool av[MT];
 #pragma unroll
@@ -60,7 +68,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
     const int m = mt * 16 + r16;
     av[mt] = m < M;
     const int ar = av[mt] ? (arows ? arows[m] : m) : 0;
-    ap[mt] = A + static_cast<size_t>(ar) * lda;
+    ap[mt] = A + static_cast<size_t>(ar) * lda + g * 8;
   }
 
   f32x4_t acc[MT][NT];
@@ -69,39 +77,46 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // wave-uniform K loop over this wave's slice [k0, k0 + kw); lane group g reads K offset +8g
-  const int kw = K / NW;
-  const int k0 = wave * kw, kend = k0 + kw;
-  int kb = k0;
-  for (; kb + 32 * U <= kend; kb += 32 * U) {
-    const int k = kb + g * 8;
-    frag_t w[U][NT], a[U][MT];
+  frag_t w0[U][NT], a0[U][MT], w1[U][NT], a1[U][MT];
+  auto load = [&](frag_t (&w)[U][NT], frag_t (&a)[U][MT], int kb) {
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+    for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) w[u][nt] = wp[nt] ? F::load(wp[nt] + k + 32 * u) : F::zero();
+      for (int nt = 0; nt < NT; ++nt) w[u][nt] = wv[nt] ? F::load(wp[nt] + kb + 32 * u) : F::zero();
 #pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? load_a<T, AS>(ap[mt] + k + 32 * u) : F::zero();
+      for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? load_a<T, AS>(ap[mt] + kb + 32 * u) : F::zero();
+    }
+  };
+  auto mma = [&](frag_t (&w)[U][NT], frag_t (&a)[U][MT]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = F::mma(acc[mt][nt], a[u][mt], w[u][nt]);
-  }
-  for (; kb < kend; kb += 32) {
-    const int k = kb + g * 8;
-    frag_t w[NT], a[MT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) w[nt] = wp[nt] ? F::load(wp[nt] + k) : F::zero();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) a[mt] = av[mt] ? load_a<T, AS>(ap[mt] + k) : F::zero();
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = F::mma(acc[mt][nt], a[mt], w[nt]);
+  };
+
+  // wave-uniform K loop over this wave's slice [k0, k0 + kw), kw a multiple of 32*U
+  const int kw = K / NW;
+  const int k0 = wave * kw, kend = k0 + kw;
+  int kb = k0;
+  load(w0, a0, kb);
+  kb += 32 * U;
+  while (true) {
+    if (kb >= kend) {
+      mma(w0, a0);
+      break;
+    }
+    load(w1, a1, kb);
+    kb += 32 * U;
+    mma(w0, a0);
+    if (kb >= kend) {
+      mma(w1, a1);
+      break;
+    }
+    load(w0, a0, kb);
+    kb += 32 * U;
+    mma(w1, a1);
   }
 
   // fixed-order reduction of the NW partial tiles
@@ -319,16 +334,29 @@ inline size_t splitk_scratch_bytes(int M, int K, int n_vtiles) {
   return ks > 1 ? static_cast<size_t>(ks) * M * (((n_vtiles + 7) / 8) * 128) * sizeof(float) : 0;
 }
 
-template <typename T, typename AS, int MT, int NT, class Epi>
-static hipError_t launch_skinny_nw(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
-                                   const Epi& epi, hipStream_t s) {
-  const int grid = n_vtiles / NT;
-  if (K % (8 * 32) == 0)
-    gemm_skinny_kernel<T, AS, MT, NT, 8, Epi><<<grid, 64 * 8, 0, s>>>(A, lda, arows, M, K, epi);
-  else if (K % (4 * 32) == 0)
-    gemm_skinny_kernel<T, AS, MT, NT, 4, Epi><<<grid, 64 * 4, 0, s>>>(A, lda, arows, M, K, epi);
-  else
-    gemm_skinny_kernel<T, AS, MT, NT, 2, Epi><<<grid, 64 * 2, 0, s>>>(A, lda, arows, M, K, epi);
+// Skinny launch configuration (measured on MI355X, M = 16, bf16): two tiles per wave and
+// K split over 4 waves when there are at least 192 such work-groups and K <= 8192; one
+// tile per wave (a gate/up pair for SwiGLU) and K split over 8 waves otherwise.  K must be
+// a multiple of NW * 32 * U; smaller splits are used when it is not.
+template <typename T, typename AS, int MT, int NT, int NW, int U, class Epi>
+static bool try_skinny(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
+                       hipStream_t s) {
+  if (K % (NW * 32 * U) || n_vtiles % NT) return false;
+  gemm_skinny_kernel<T, AS, MT, NT, NW, U, Epi><<<n_vtiles / NT, 64 * NW, 0, s>>>(A, lda, arows, M, K, epi);
+  return true;
+}
+
+template <typename T, typename AS, int MT, class Epi>
+static hipError_t launch_skinny(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
+                                const Epi& epi, hipStream_t s) {
+  constexpr int U = MT >= 4 ? 2 : 4;
+  const bool wide = n_vtiles / 2 >= 192 && K <= 8192;
+  bool ok = false;
+  if (wide || Epi::PX) ok = try_skinny<T, AS, MT, 2, 4, U>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok && !Epi::PX) ok = try_skinny<T, AS, MT, 1, 8, U>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok) ok = try_skinny<T, AS, MT, (Epi::PX ? 2 : 1), 4, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok) ok = try_skinny<T, AS, MT, (Epi::PX ? 2 : 1), 2, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok) return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -338,10 +366,9 @@ template <typename T, typename AS, class Epi>
 static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
                            hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0) {
   if (M <= 0 || n_vtiles <= 0) return hipSuccess;
-  constexpr int NT = Epi::PX ? 2 : 1;
-  if (M <= 16) return launch_skinny_nw<T, AS, 1, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
-  if (M <= 32) return launch_skinny_nw<T, AS, 2, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
-  if (M <= 64) return launch_skinny_nw<T, AS, 4, NT>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (M <= 16) return launch_skinny<T, AS, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (M <= 32) return launch_skinny<T, AS, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (M <= 64) return launch_skinny<T, AS, 4>(A, lda, arows, M, K, n_vtiles, epi, s);
   const int ntx = (n_vtiles + 7) / 8, ldp = ntx * 128;
   int ks = splitk_plan<T>(M, K, n_vtiles);
   if (!scratch || scratch_bytes < splitk_scratch_bytes<T>(M, K, n_vtiles)) ks = 1;
