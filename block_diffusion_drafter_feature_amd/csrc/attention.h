@@ -122,27 +122,49 @@ __global__ __launch_bounds__(64 * (G / HW)) void block_attn_kernel(AttnArgs<T> a
     }
   };
 
-  // ---- context slabs of this split
+  // ---- context slabs of this split: the next slab's K/V loads are issued before the
+  // current slab is processed (one carried register stage)
   const T* kcp = a.kc + kv_base * cap * HD;
   const T* vcp = a.vtc + kv_base * HD * cap;
-  for (int kb0 = kbeg; kb0 < kend; kb0 += 32) {
-    frag_t kf[2][KS], vf[DT];
+  auto load_slab = [&](frag_t (&kf)[2][KS], frag_t (&vf)[DT], int kb0) {
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const T* kp = kcp + static_cast<size_t>(kb0 + krow0 + 4 * t) * HD + lg * 8;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) kf[t][ks] = F::load(kp + ks * 32);
     }
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vf[dt] = F::load(vcp + static_cast<size_t>(dt * 16 + r16) * cap + kb0 + 8 * lg);
+  };
+  auto run_slab = [&](const frag_t (&kf)[2][KS], frag_t (&vf)[DT], int kb0) {
     const int nvalid = kend - kb0;                     // > 0
-    uint32_t keep = 0;
+    if (nvalid < 32) {
+      uint32_t keep = 0;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) keep |= (8 * lg + j < nvalid ? 1u : 0u) << j;
+      for (int j = 0; j < 8; ++j) keep |= (8 * lg + j < nvalid ? 1u : 0u) << j;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      const frag_t v = F::load(vcp + static_cast<size_t>(dt * 16 + r16) * cap + kb0 + 8 * lg);
-      vf[dt] = keep == 0xffu ? v : F::mask(v, keep);
+      for (int dt = 0; dt < DT; ++dt) vf[dt] = F::mask(vf[dt], keep);
     }
     slab(kf, vf, nvalid);
+  };
+  if (kbeg < kend) {
+    frag_t kc[2][KS], vc[DT];
+    load_slab(kc, vc, kbeg);
+    for (int kb0 = kbeg; kb0 < kend; kb0 += 32) {
+      if (kb0 + 32 < kend) {
+        frag_t kn[2][KS], vn[DT];
+        load_slab(kn, vn, kb0 + 32);
+        run_slab(kc, vc, kb0);
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) kc[t][ks] = kn[t][ks];
+#pragma unroll
+        for (int dt = 0; dt < DT; ++dt) vc[dt] = vn[dt];
+      } else {
+        run_slab(kc, vc, kb0);
+      }
+    }
   }
 
   // ---- the block's own 16 keys (last split only)

@@ -49,6 +49,14 @@ template <> __device__ __forceinline__ bf16_t from_f<bf16_t>(float v) { return f
 // round-trip through the storage type (identity for fp32)
 template <typename T> __device__ __forceinline__ float round_to(float v) { return to_f<T>(from_f<T>(v)); }
 
+// ------------------------------------------------------------------ buffer resources
+
+// Raw buffer descriptor over [p, p + bytes): loads at offsets >= bytes return zero.
+// Word 3 = 0x00020000 is the gfx9-family raw (untyped, unswizzled) buffer format.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+
 // ------------------------------------------------------------------ fragments
 
 template <typename T> struct Frag;
@@ -61,6 +69,10 @@ template <> struct Frag<bf16_t> {
   }
   __device__ __forceinline__ static type load(const bf16_t* p) {
     return __builtin_bit_cast(type, *reinterpret_cast<const u32x4_t*>(p));
+  }
+  // 8 elements at byte offset voff + soff of a buffer
+  __device__ __forceinline__ static type load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    return __builtin_bit_cast(type, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
   }
   // load 8 floats and round them to bf16
   __device__ __forceinline__ static type load_f32(const float* p) {
@@ -106,6 +118,12 @@ template <> struct Frag<float> {
     const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
     type r = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     return r;
+  }
+  __device__ __forceinline__ static type load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, int soff) {
+    const f32x4_t a = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    const f32x4_t b = __builtin_bit_cast(f32x4_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff + 16, soff, 0));
+    type v = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return v;
   }
   __device__ __forceinline__ static type load_f32(const float* p) { return load(p); }
   __device__ __forceinline__ static type from_floats(const float* v) {

@@ -17,7 +17,7 @@ using namespace dflash;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kTopkChunk = 4096;     // vocabulary columns per top-k work-group
+constexpr int kTopkChunk = kTopkWaveChunk;   // vocabulary columns per top-k wave
 constexpr int kArgmaxChunk = 8192;   // vocabulary columns per argmax work-group
 
 size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
@@ -57,6 +57,7 @@ int check_config(const dflash_config* c) {
   const int G = c->n_heads / c->n_kv_heads;
   if (G != 1 && G != 2 && G != 4) return DFLASH_E_UNSUPPORTED;
   if (c->vocab % 16 || c->vocab < 16) return DFLASH_E_UNSUPPORTED;
+  if (c->vocab > 256 * kTopkChunk) return DFLASH_E_UNSUPPORTED;     // top-k merges <= 256 chunk lists
   if (c->ps_dim % 64 || c->ps_rank > 256) return DFLASH_E_UNSUPPORTED;
   return DFLASH_OK;
 }
@@ -109,9 +110,11 @@ InjectWs<T> carve_inject(Carver& cv, const dflash_config* c, int rows) {
   return w;
 }
 
+// Context splits per (sequence, kv head): enough work-groups to cover the chip about 8
+// times, each split at least 64 context rows.
 int attn_splits(const dflash_config* c, int batch, int cap) {
-  const int want = (512 + batch * c->n_kv_heads - 1) / (batch * c->n_kv_heads);
-  const int maxs = (cap + 255) / 256;
+  const int want = (2048 + batch * c->n_kv_heads - 1) / (batch * c->n_kv_heads);
+  const int maxs = (cap + 63) / 64;
   int s = want < maxs ? want : maxs;
   return s < 1 ? 1 : (s > 64 ? 64 : s);
 }
@@ -401,7 +404,7 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
   P0.end(DFLASH_PROBE_LM_HEAD);
   const int nch = (V + kTopkChunk - 1) / kTopkChunk;
   P0.begin(DFLASH_PROBE_TOPK);
-  topk_partial_kernel<<<dim3(nch, M), 256, 0, s>>>(lg, V, V, kTopkChunk, W.tk_v, W.tk_i);
+  topk_partial_kernel<<<dim3(nch, M), 64, 0, s>>>(lg, V, V, W.tk_v, W.tk_i);
   LAUNCH_CHECK();
   topk_final_kernel<<<M, 64, 0, s>>>(W.tk_v, W.tk_i, nch, cand_ids, cand_logits);
   LAUNCH_CHECK();

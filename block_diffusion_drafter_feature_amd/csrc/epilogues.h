@@ -2,6 +2,8 @@
 // output element.  Interface used by gemm.h:
 //   PX, PC            partner of (virtual tile vt, column c) is (vt ^ PX, c ^ PC)
 //   wrow(vt, c)       pointer to the W row feeding column c of virtual tile vt (nullptr: zero)
+//   wseg(vt, b, n)    the weight matrix holding tile vt's rows: base b, n bytes (n = 0 when
+//                     the tile is past the end); every row of a tile lies in one matrix
 //   apply(vt, m, c, v, partner)
 #pragma once
 
@@ -46,6 +48,17 @@ struct EpiStore {
     const int s = w.find(n);
     return w.p[s] + static_cast<size_t>(n - w.off[s]) * w.K;
   }
+  __device__ __forceinline__ void wseg(int vt, const T*& b, uint32_t& n) const {
+    const int r = vt * 16;
+    if (r >= w.off[w.n_seg]) {
+      b = w.p[0];
+      n = 0;
+      return;
+    }
+    const int s = w.find(r);
+    b = w.p[s];
+    n = static_cast<uint32_t>(static_cast<size_t>(w.off[s + 1] - w.off[s]) * w.K * sizeof(T));
+  }
   __device__ __forceinline__ void apply(int vt, int m, int c, float v, float) const {
     const int n = vt * 16 + c;
     if (n >= w.off[w.n_seg]) return;
@@ -84,6 +97,14 @@ struct EpiQKV {
     vt -= tk;
     if (vt < tk) return wv + static_cast<size_t>(vt * 16 + c) * K;
     return nullptr;
+  }
+  __device__ __forceinline__ void wseg(int vt, const T*& b, uint32_t& n) const {
+    const int tq = H * hd / 16, tk = Hkv * hd / 16;
+    const size_t rb = static_cast<size_t>(K) * sizeof(T);
+    if (vt < tq) { b = wq; n = static_cast<uint32_t>(H * hd * rb); }
+    else if (vt < tq + tk) { b = wk; n = static_cast<uint32_t>(Hkv * hd * rb); }
+    else if (vt < tq + 2 * tk) { b = wv; n = static_cast<uint32_t>(Hkv * hd * rb); }
+    else { b = wq; n = 0; }
   }
   __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
     const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
@@ -129,6 +150,17 @@ struct EpiInject {
     if (t < tk) return wk[l] + static_cast<size_t>((t / tph) * hd + rope_dim(t % tph, c, hd)) * K;
     return wv[l] + static_cast<size_t>((t - tk) * 16 + c) * K;
   }
+  __device__ __forceinline__ void wseg(int vt, const T*& b, uint32_t& n) const {
+    const int tk = Hkv * hd / 16;
+    const int l = vt / (2 * tk), t = vt % (2 * tk);
+    if (l >= L) {
+      b = wk[0];
+      n = 0;
+      return;
+    }
+    b = t < tk ? wk[l] : wv[l];
+    n = static_cast<uint32_t>(static_cast<size_t>(Hkv) * hd * K * sizeof(T));
+  }
   __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
     const int tk = Hkv * hd / 16, tph = hd / 16;
     const int l = vt / (2 * tk), t = vt % (2 * tk);
@@ -170,6 +202,10 @@ struct EpiSwiGLU {
     const int n = (vt >> 1) * 16 + c;
     if (n >= Fd) return nullptr;
     return ((vt & 1) ? wu : wg) + static_cast<size_t>(n) * K;
+  }
+  __device__ __forceinline__ void wseg(int vt, const T*& b, uint32_t& n) const {
+    b = (vt & 1) ? wu : wg;
+    n = (vt >> 1) * 16 < Fd ? static_cast<uint32_t>(static_cast<size_t>(Fd) * K * sizeof(T)) : 0u;
   }
   __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
     if (vt & 1) return;

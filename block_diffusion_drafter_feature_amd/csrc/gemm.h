@@ -53,22 +53,27 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
   const int r16 = lane & 15, g = lane >> 4;
   const int vt0 = blockIdx.x * NT;
 
-  const T* wp[NT];
-  bool wv[NT];
+  // W through one buffer descriptor per tile (rows past the matrix read as zero); A rows
+  // past M are clamped to row 0 (their results are never stored).  No per-load predicates.
+  const int kw = K / NW;
+  const int k0 = wave * kw;
+  __amdgpu_buffer_rsrc_t rw[NT];
+  uint32_t vw[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
+    const T* base;
+    uint32_t bytes;
+    epi.wseg(vt0 + nt, base, bytes);
+    rw[nt] = make_rsrc(base, bytes);
     const T* p = epi.wrow(vt0 + nt, r16);
-    wv[nt] = p != nullptr;
-    wp[nt] = p ? p + g * 8 : nullptr;
+    vw[nt] = p ? static_cast<uint32_t>((p - base + g * 8 + k0) * sizeof(T)) : bytes;
   }
   const AS* ap[MT];
-  bool av[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = mt * 16 + r16;
-    av[mt] = m < M;
-    const int ar = av[mt] ? (arows ? arows[m] : m) : 0;
-    ap[mt] = A + static_cast<size_t>(ar) * lda + g * 8;
+    const int ar = m < M ? (arows ? arows[m] : m) : (arows ? arows[0] : 0);
+    ap[mt] = A + static_cast<size_t>(ar) * lda + g * 8 + k0;
   }
 
   f32x4_t acc[MT][NT];
@@ -77,14 +82,15 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  frag_t w0[U][NT], a0[U][MT], w1[U][NT], a1[U][MT];
+  constexpr int STEP = 32 * U;   // K elements per register stage
   auto load = [&](frag_t (&w)[U][NT], frag_t (&a)[U][MT], int kb) {
+    const int soff = kb * static_cast<int>(sizeof(T));
 #pragma unroll
     for (int u = 0; u < U; ++u) {
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) w[u][nt] = wv[nt] ? F::load(wp[nt] + kb + 32 * u) : F::zero();
+      for (int nt = 0; nt < NT; ++nt) w[u][nt] = F::load_buf(rw[nt], vw[nt] + 32 * u * sizeof(T), soff);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) a[u][mt] = av[mt] ? load_a<T, AS>(ap[mt] + kb + 32 * u) : F::zero();
+      for (int mt = 0; mt < MT; ++mt) a[u][mt] = load_a<T, AS>(ap[mt] + kb + 32 * u);
     }
   };
   auto mma = [&](frag_t (&w)[U][NT], frag_t (&a)[U][MT]) {
@@ -96,28 +102,25 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
         for (int nt = 0; nt < NT; ++nt) acc[mt][nt] = F::mma(acc[mt][nt], a[u][mt], w[u][nt]);
   };
 
-  // wave-uniform K loop over this wave's slice [k0, k0 + kw), kw a multiple of 32*U
-  const int kw = K / NW;
-  const int k0 = wave * kw, kend = k0 + kw;
-  int kb = k0;
-  load(w0, a0, kb);
-  kb += 32 * U;
-  while (true) {
-    if (kb >= kend) {
-      mma(w0, a0);
-      break;
+  // wave-uniform K loop over this wave's slice [k0, k0 + kw), kw a multiple of STEP.  The
+  // next stage's loads are issued before the current stage's matrix ops; the prefetched
+  // stage is then carried into the next iteration (one loop-carried stage, updated by copy).
+  const int nst = kw / STEP;
+  frag_t wc[U][NT], ac[U][MT];
+  load(wc, ac, 0);
+  for (int st = 1; st < nst; ++st) {
+    frag_t wn[U][NT], an[U][MT];
+    load(wn, an, st * STEP);
+    mma(wc, ac);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) wc[u][nt] = wn[u][nt];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) ac[u][mt] = an[u][mt];
     }
-    load(w1, a1, kb);
-    kb += 32 * U;
-    mma(w0, a0);
-    if (kb >= kend) {
-      mma(w1, a1);
-      break;
-    }
-    load(w0, a0, kb);
-    kb += 32 * U;
-    mma(w1, a1);
   }
+  mma(wc, ac);
 
   // fixed-order reduction of the NW partial tiles
 #pragma unroll
@@ -334,9 +337,10 @@ inline size_t splitk_scratch_bytes(int M, int K, int n_vtiles) {
   return ks > 1 ? static_cast<size_t>(ks) * M * (((n_vtiles + 7) / 8) * 128) * sizeof(float) : 0;
 }
 
-// Skinny launch configuration (measured on MI355X, M = 16, bf16): two tiles per wave and
-// K split over 4 waves when there are at least 192 such work-groups and K <= 8192; one
-// tile per wave (a gate/up pair for SwiGLU) and K split over 8 waves otherwise.  K must be
+// Skinny launch configuration (measured on MI355X with cold caches, M = 16, bf16): two
+// tiles per wave (a gate/up pair for SwiGLU) and K split over 4 waves when there are at
+// least 192 such work-groups and K <= 8192; one tile per wave and K split over 8 waves
+// otherwise; 8 k-steps per register stage at M = 16.  K must be
 // a multiple of NW * 32 * U; smaller splits are used when it is not.
 template <typename T, typename AS, int MT, int NT, int NW, int U, class Epi>
 static bool try_skinny(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
@@ -349,11 +353,12 @@ static bool try_skinny(const AS* A, int lda, const int32_t* arows, int M, int K,
 template <typename T, typename AS, int MT, class Epi>
 static hipError_t launch_skinny(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
                                 const Epi& epi, hipStream_t s) {
-  constexpr int U = MT >= 4 ? 2 : 4;
+  constexpr int U = MT >= 4 ? 2 : (MT == 2 ? 4 : 8);
   const bool wide = n_vtiles / 2 >= 192 && K <= 8192;
   bool ok = false;
   if (wide || Epi::PX) ok = try_skinny<T, AS, MT, 2, 4, U>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (!ok && !Epi::PX) ok = try_skinny<T, AS, MT, 1, 8, U>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok && !Epi::PX) ok = try_skinny<T, AS, MT, 1, 8, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (!ok) ok = try_skinny<T, AS, MT, (Epi::PX ? 2 : 1), 4, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (!ok) ok = try_skinny<T, AS, MT, (Epi::PX ? 2 : 1), 2, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (!ok) return hipErrorInvalidValue;

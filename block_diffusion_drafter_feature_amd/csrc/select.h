@@ -100,56 +100,146 @@ __device__ __forceinline__ void block_top16(Top16& t, float* sv, int* si) {
   }
 }
 
-// Stage 1: top-16 of each (row, column chunk).  grid (n_chunks, rows), 256 threads.
-__global__ __launch_bounds__(256) void topk_partial_kernel(const float* __restrict__ logits, int V, int ld,
-                                                           int chunk, float* __restrict__ pv,
-                                                           int32_t* __restrict__ pi) {
-  __shared__ float sv[4 * 16];
-  __shared__ int si[4 * 16];
-  const int c = blockIdx.x, m = blockIdx.y, nch = gridDim.x;
-  const int c0 = c * chunk, c1 = min(V, c0 + chunk);
-  const float* row = logits + static_cast<size_t>(m) * ld;
-  Top16 t;
-  t.init();
-  for (int j = c0 + threadIdx.x; j < c1; j += 256) t.push(row[j], j);
-  block_top16(t, sv, si);
-  if (threadIdx.x < 16) {
-    const size_t o = (static_cast<size_t>(m) * nch + c) * 16;
+// Wave-wide top 16 of the candidates the 64 lanes hold (NV per lane, value -inf = empty).
+// Exact for any input:
+//   1. tau = 16th largest of the 64 lane maxima (bitonic sort across lanes).  At least 16
+//      candidates are >= tau, so the top 16 are all >= tau.
+//   2. Lanes compact their candidates >= tau into LDS (wave prefix sum for offsets).
+//   3. Each survivor's rank under the (value desc, index asc) order is counted against all
+//      survivors; rank < 16 lands in out[rank].
+// When more than CAP candidates survive (heavy ties), the lanes fall back to exact
+// register lists merged across the wave.  Result: out_v/out_i[0..15] in LDS.
+template <int NV, int CAP>
+__device__ __forceinline__ void wave_select16(const float (&v)[NV], const int (&id)[NV], float* sv, int* si,
+                                              float* out_v, int* out_i) {
+  const int lane = threadIdx.x & 63;
+  float mx = -INFINITY;
 #pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (k == threadIdx.x) {
-        pv[o + k] = t.v[k];
-        pi[o + k] = t.i[k];
+  for (int j = 0; j < NV; ++j) mx = fmaxf(mx, v[j]);
+  // bitonic sort of the lane maxima, descending across lanes
+  float key = mx;
+#pragma unroll
+  for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const float o = __shfl_xor(key, j, 64);
+      const bool up = ((lane & k) == 0);           // this lane's block sorts descending
+      const bool lower = (lane & j) == 0;
+      const bool keep_max = (up == lower);
+      key = keep_max ? fmaxf(key, o) : fminf(key, o);
+    }
+  }
+  const float tau = __shfl(key, 15, 64);
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) cnt += (v[j] >= tau && v[j] > -INFINITY) ? 1 : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  const int total = __shfl(incl, 63, 64);
+  if (total <= CAP) {
+    int pos = incl - cnt;
+#pragma unroll
+    for (int j = 0; j < NV; ++j)
+      if (v[j] >= tau && v[j] > -INFINITY) {
+        sv[pos] = v[j];
+        si[pos] = id[j];
+        ++pos;
       }
+    if (lane < 16) {
+      out_v[lane] = -INFINITY;
+      out_i[lane] = INT_MAX;
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __builtin_amdgcn_wave_barrier();
+    for (int c = lane; c < total; c += 64) {
+      const float cv = sv[c];
+      const int ci = si[c];
+      int rank = 0;
+      for (int c2 = 0; c2 < total; ++c2) rank += better(sv[c2], si[c2], cv, ci) ? 1 : 0;
+      if (rank < 16) {
+        out_v[rank] = cv;
+        out_i[rank] = ci;
+      }
+    }
+  } else {
+    Top16 t;
+    t.init();
+#pragma unroll
+    for (int j = 0; j < NV; ++j) t.push(v[j], id[j]);
+    t.wave_merge();
+    if (lane < 16) {
+#pragma unroll
+      for (int k = 0; k < 16; ++k)
+        if (k == lane) {
+          out_v[k] = t.v[k];
+          out_i[k] = t.i[k];
+        }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+}
+
+// Stage 1: top-16 of each (row, 2048-column chunk).  grid (n_chunks, rows), one wave each.
+constexpr int kTopkWaveChunk = 2048;
+__global__ __launch_bounds__(64) void topk_partial_kernel(const float* __restrict__ logits, int V, int ld,
+                                                          float* __restrict__ pv, int32_t* __restrict__ pi) {
+  constexpr int NV = kTopkWaveChunk / 64;
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  __shared__ float ov[16];
+  __shared__ int oi[16];
+  const int c = blockIdx.x, m = blockIdx.y, nch = gridDim.x, lane = threadIdx.x;
+  const int c0 = c * kTopkWaveChunk;
+  const float* row = logits + static_cast<size_t>(m) * ld;
+  float v[NV];
+  int id[NV];
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int col = c0 + j * 64 + lane;
+    id[j] = col;
+    v[j] = col < V ? row[col] : -INFINITY;
+  }
+  wave_select16<NV, 256>(v, id, sv, si, ov, oi);
+  if (lane < 16) {
+    const size_t o = (static_cast<size_t>(m) * nch + c) * 16 + lane;
+    pv[o] = ov[lane];
+    pi[o] = oi[lane];
   }
 }
 
-// Stage 2: merge the per-chunk lists of each row.  grid (rows), 64 threads.
+// Stage 2: merge the per-chunk lists of each row.  grid (rows), one wave; lane l takes
+// lists l, l + 64, ... (at most 4 per lane).
 __global__ __launch_bounds__(64) void topk_final_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
                                                         int n_chunks, int32_t* __restrict__ out_ids,
                                                         float* __restrict__ out_vals) {
+  constexpr int LPL = 4;
+  __shared__ float sv[512];
+  __shared__ int si[512];
+  __shared__ float ov[16];
+  __shared__ int oi[16];
   const int m = blockIdx.x, lane = threadIdx.x;
-  Top16 t;
-  t.init();
-  for (int c = lane; c < n_chunks; c += 64) {
-    const size_t o = (static_cast<size_t>(m) * n_chunks + c) * 16;
-    float ov[16];
-    int oi[16];
+  float v[16 * LPL];
+  int id[16 * LPL];
+#pragma unroll
+  for (int q = 0; q < LPL; ++q) {
+    const int c = lane + 64 * q;
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
-      ov[k] = pv[o + k];
-      oi[k] = pi[o + k];
+      const bool ok = c < n_chunks;
+      const size_t o = (static_cast<size_t>(m) * n_chunks + (ok ? c : 0)) * 16 + k;
+      v[q * 16 + k] = ok ? pv[o] : -INFINITY;
+      id[q * 16 + k] = ok ? pi[o] : INT_MAX;
     }
-    t.merge(ov, oi);
   }
-  t.wave_merge();
+  wave_select16<16 * LPL, 512>(v, id, sv, si, ov, oi);
   if (lane < 16) {
-#pragma unroll
-    for (int k = 0; k < 16; ++k)
-      if (k == lane) {
-        out_ids[static_cast<size_t>(m) * 16 + k] = t.i[k];
-        out_vals[static_cast<size_t>(m) * 16 + k] = t.v[k];
-      }
+    out_ids[static_cast<size_t>(m) * 16 + lane] = oi[lane];
+    out_vals[static_cast<size_t>(m) * 16 + lane] = ov[lane];
   }
 }
 
@@ -163,9 +253,11 @@ __device__ __forceinline__ void argmax_step(float& bv, int& bi, float v, int i) 
 }
 
 // Stage 1: argmax of each (target row, column chunk).  grid (n_chunks, rows), 256 threads.
+// Rows are read in 16-byte vectors where the row start is 16-byte aligned, else per element.
 template <typename TL>
 __global__ __launch_bounds__(256) void argmax_partial_kernel(const TL* __restrict__ x, int V, int chunk,
                                                              float* __restrict__ pv, int32_t* __restrict__ pi) {
+  constexpr int EPV = 16 / sizeof(TL);
   __shared__ float sv[4];
   __shared__ int si[4];
   const int c = blockIdx.x, r = blockIdx.y, nch = gridDim.x;
@@ -173,7 +265,23 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const TL* __restric
   const TL* row = x + static_cast<size_t>(r) * V;
   float bv = -INFINITY;
   int bi = INT_MAX;
-  for (int j = c0 + threadIdx.x; j < c1; j += 256) argmax_step(bv, bi, to_f<TL>(row[j]), j);
+  const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0) && (c0 % EPV == 0);
+  if (vec) {
+    const int nvec = (c1 - c0) / EPV;
+    for (int q = threadIdx.x; q < nvec; q += 256) {
+      const u32x4_t u = *reinterpret_cast<const u32x4_t*>(row + c0 + q * EPV);
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) {
+        float f;
+        if constexpr (sizeof(TL) == 2) f = __uint_as_float((e & 1) ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
+        else f = __uint_as_float(u[e]);
+        argmax_step(bv, bi, f, c0 + q * EPV + e);
+      }
+    }
+    for (int j = c0 + nvec * EPV + threadIdx.x; j < c1; j += 256) argmax_step(bv, bi, to_f<TL>(row[j]), j);
+  } else {
+    for (int j = c0 + threadIdx.x; j < c1; j += 256) argmax_step(bv, bi, to_f<TL>(row[j]), j);
+  }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     const float ov = __shfl_xor(bv, o, 64);

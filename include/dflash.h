@@ -81,7 +81,7 @@ typedef struct dflash_config {
   int32_t n_layers;       /* 1 .. DFLASH_MAX_LAYERS                                           */
   int32_t n_feat_layers;  /* sampled target layers n_s                                        */
   int32_t d_target;       /* target width d_t; n_s * d_t multiple of 64                       */
-  int32_t vocab;          /* V; multiple of 16, >= 16                                         */
+  int32_t vocab;          /* V; multiple of 16, 16 .. 524288                                  */
   int32_t ps_dim;         /* Path Selector embedding width; 256                               */
   int32_t ps_rank;        /* rank r of the bilinear form; 1 .. 256                            */
   int32_t use_conv;       /* 0/1: dynamic short conv around every sublayer                    */

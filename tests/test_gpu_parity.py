@@ -126,6 +126,31 @@ def test_inject_parity(name):
         assert np.isnan(Vg[~np.broadcast_to(written[:, None, :], (B, dims.n_kv_heads, cap))]).all()
 
 
+@pytest.mark.parametrize("rows", [1, 16, 17, 32, 33, 48, 64, 65, 200])
+def test_inject_row_counts(rows):
+    """Every GEMM shape class: 1, 2 or 4 row tiles of the weight-streaming kernel, and the
+    LDS-tiled kernel above 64 rows (with and without split-K)."""
+    say(f"inject rows={rows}")
+    wl = synth.workload("t_small")
+    dims = wl.dims
+    W = synth.make_weights(dims, wl.seed)
+    m = oracle.Model(dims, W)
+    dr = D.Drafter(dims, W)
+    cap = ((rows + 31) // 32) * 32 + 32
+    hidden = synth.make_hidden(dims, rows, wl.seed + rows)
+    cache = D.KVCache(dims, 1, cap, fill=float("nan"))
+    nb = D.dflash_inject_workspace_bytes(dr.cfg, rows)
+    D.dflash_inject_context(dr.cfg, dr.w, cache.kv, D.to_device(hidden, dims), rows, dev_i32([0, rows]),
+                            dev_i32([5]), dev_i32([rows]), 1, ws_of(nb), nb)
+    torch.cuda.synchronize()
+    pos = 5 + np.arange(rows)
+    _, Ko, Vo = oracle.inject_rows(m, hidden, pos)
+    for l in range(dims.n_layers):
+        Kg, Vg = cache.logical(l)
+        H.assert_close_rows(f"K l{l}", Kg.float().cpu().numpy()[0][:, pos].transpose(1, 0, 2), Ko[l], H.tol(dims))
+        H.assert_close_rows(f"V l{l}", Vg.float().cpu().numpy()[0][:, pos].transpose(1, 0, 2), Vo[l], H.tol(dims))
+
+
 # ------------------------------------------------------------------ drafter forward
 
 DRAFT_CASES = ["c1", "t_small", "t_conv", "t_hd128", "t_f32", "t_batch"]
@@ -173,6 +198,26 @@ def test_draft_parity(name):
         np.testing.assert_array_equal(cl[b], np.take_along_axis(lg[b], ci[b].astype(np.int64), axis=1))
         near += H.topk_with_margin(ci[b], o["logits"], lg[b])
     say(f"  near-tie top-16 swaps: {near}")
+
+
+def test_draft_long_context():
+    """Contexts long enough for many 32-key slabs per attention split (and ragged ends)."""
+    say("draft long context t_hd128")
+    wl = synth.workload("t_hd128")
+    dims = wl.dims
+    ctx = (9000, 4097)
+    cap = ((max(ctx) + 16 + 31) // 32) * 32
+    W = synth.make_weights(dims, wl.seed)
+    K, V = synth.make_cache(dims, ctx, cap, wl.seed + 1)
+    ids = synth.make_block_ids(dims, len(ctx), wl.seed, 1)
+    dr = D.Drafter(dims, W)
+    cache = D.KVCache(dims, len(ctx), cap)
+    cache.load_logical(K, V)
+    ci, cl, fh, lg = run_draft(dims, dr, cache, ctx, ids)
+    outs = H.oracle_draft(oracle.Model(dims, W), K, V, ctx, ids)
+    for b, o in enumerate(outs):
+        H.assert_close_rows(f"logits b{b}", lg[b], o["logits"], H.tol(dims))
+        H.assert_close_rows(f"final hidden b{b}", fh[b], o["xhat"], H.tol(dims))
 
 
 def test_draft_ignores_rows_beyond_context():
