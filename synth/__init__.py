@@ -268,22 +268,27 @@ def weight_shapes(dims: Dims) -> Dict[str, tuple]:
 
 
 def make_weights(dims: Dims, seed: int, ps_scale: str = "config", conv_scale: str = "config",
-                 zero: Sequence[str] = ()) -> Dict[str, np.ndarray]:
+                 zero: Sequence[str] = (), names: Optional[Sequence[str]] = None) -> Dict[str, np.ndarray]:
     """Random-init drafter weights.
 
     Matrices and conv taps are N(0, 0.02^2); RMSNorm gains are 1.0.
     ``ps_scale="stress"`` draws the Path Selector at a scale where its pair
     scores are of the order of the logit gaps (at N(0, 0.02^2) they are ~1e-4
     and the chosen path is always the top-1 candidate, which tests nothing).
-    ``conv_scale="stress"`` likewise makes the conv taps and their content-dependent
-    corrections O(0.2) (at the config scale they are ~1e-2 and the conv is nearly the
-    identity).
-    Names listed in ``zero`` are returned as all-zero tensors.
+    ``conv_scale="stress"`` / ``"mild"`` draw the conv taps and their content-dependent
+    corrections at O(0.2) / O(0.05).  At the config scale the static taps are ~0.02 but the
+    corrections of a unit-RMS row are ~N(0, 0.02^2 d) -- O(1.3) at d = 4096 -- which makes
+    a 20-site drafter ill-conditioned (see the design notes); "mild" keeps it well
+    conditioned while still exercising every term.
+    Names listed in ``zero`` are returned as all-zero tensors.  ``names`` restricts the
+    draw to those tensors (each tensor's values do not depend on the others).
     """
     shapes = weight_shapes(dims)
     out: Dict[str, np.ndarray] = {}
     d = dims.d
     for idx, (name, shp) in enumerate(sorted(shapes.items())):
+        if names is not None and name not in names:
+            continue
         base = name.split(".")[-1]
         if name in zero:
             out[name] = const(shp, 0.0, dims.dtype)
@@ -299,10 +304,11 @@ def make_weights(dims: Dims, seed: int, ps_scale: str = "config", conv_scale: st
                 std = dims.ps_rank ** -0.25 / np.sqrt(dims.ps_dim)
             elif name == "ps_gate":
                 std = 1.0 / np.sqrt(d)
-        if conv_scale == "stress" and base == "gen":
-            std = 0.2 / np.sqrt(d)          # corrections ~N(0, 0.2^2) on unit-RMS rows
-        if conv_scale == "stress" and base in ("w0", "w1"):
-            std = 0.2
+        if conv_scale in ("stress", "mild") and base == "gen":
+            # corrections ~N(0, s^2) on unit-RMS rows: s = 0.2 (stress) or 0.05 (mild)
+            std = (0.2 if conv_scale == "stress" else 0.05) / np.sqrt(d)
+        if conv_scale in ("stress", "mild") and base in ("w0", "w1"):
+            std = 0.2 if conv_scale == "stress" else 0.05
         out[name] = normal(shp, std, seed, 100 + idx, dims.dtype)
     return out
 

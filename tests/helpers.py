@@ -12,6 +12,13 @@ def tol(dims) -> float:
     return 2e-2 if dims.dtype == "bf16" else 1e-4
 
 
+def tol_conditioned(dims, kappa: float) -> float:
+    """The stated tolerance, or three times the computation's own fp32-level spread on the
+    inputs at hand (``conditioning``) where that is larger: no fp32 implementation can be
+    held closer to an fp64 oracle than the oracle's own result moves under fp32 noise."""
+    return max(tol(dims), 3.0 * kappa)
+
+
 def rowwise_relerr(g: np.ndarray, o: np.ndarray) -> float:
     g = np.asarray(g, dtype=np.float64).reshape(-1, np.shape(g)[-1])
     o = np.asarray(o, dtype=np.float64).reshape(-1, np.shape(o)[-1])
@@ -85,6 +92,41 @@ def walk_f32(cand_logits, S, has_anchor, mode):
         j = int(back[p, j])
         idx.append(j)
     return np.asarray(idx[::-1])
+
+
+def accept_of(draft, target_logits):
+    """Accepted length and bonus token of a device draft under given target logits, by
+    direct inspection (largest logit, lowest id on ties): a validity check of device
+    outputs, independent of the oracle module."""
+    t = np.asarray(target_logits, dtype=np.float64)
+    greedy = [int(np.flatnonzero(row == row.max())[0]) for row in t]
+    a = 0
+    while a < len(draft) and int(draft[a]) == greedy[a]:
+        a += 1
+    return a, greedy[a]
+
+
+def conditioning(m, kc, vc, ctx_len, block_ids, base, seeds=(0, 1)):
+    """How far the oracle's own result moves when every value is perturbed by about one
+    fp32 ulp (relative 2^-24, random sign) just before each bf16 rounding point: the
+    spread that fp32 arithmetic alone can produce on these inputs.  Returns the row-wise
+    relative deviation (max over logits and final hidden, max over seeds)."""
+    worst = 0.0
+    for sd in seeds:
+        r = np.random.default_rng(sd)
+
+        class Perturbed(oracle.Model):
+            def rb(self, x):
+                x = np.asarray(x, dtype=np.float64)
+                if self.dims.dtype != "bf16":
+                    return x
+                return oracle.bf16_round(x * (1 + r.uniform(-2.0 ** -24, 2.0 ** -24, size=x.shape)))
+
+        mp = Perturbed(m.dims, m.stored)
+        mp._cache = m._cache
+        o = oracle.draft_block(mp, kc, vc, ctx_len, block_ids)
+        worst = max(worst, rowwise_relerr(o["logits"], base["logits"]), rowwise_relerr(o["xhat"], base["xhat"]))
+    return worst
 
 
 def oracle_draft(m, K, V, ctx_lens, block_ids):

@@ -347,8 +347,9 @@ def test_step_end_to_end(name):
         H.assert_close_rows(f"logits b{b}", lg[b], o["logits"], t)
         H.topk_with_margin(ci[b], o["logits"], lg[b])
         gp = pids.cpu().numpy()[b]
-        # verification of the device's path is exact given the same target logits
-        a, bonus = oracle.verify(gp, oracle.decode(T[b], dims.dtype))
-        assert (int(acc[b]), int(bon[b])) == (a, bonus)
+        # the device's verification of its own path is valid for the same target logits
+        Tf = oracle.decode(T[b], dims.dtype)
+        assert (int(acc[b]), int(bon[b])) == H.accept_of(gp, Tf)
+        # where both sides reach the same candidates and path, the outcomes agree
         if np.array_equal(ci[b], o["cand_ids"]) and np.array_equal(gp, o["path_ids"]):
             assert (int(acc[b]), int(bon[b])) == (o["accept_len"], o["bonus"])
