@@ -39,6 +39,9 @@ def parse():
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 to skip)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel breakdown pass")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="after the step, run a plain fp32 elementwise copy (torch.neg) of this many MiB "
+                         "three times: a kernel of known traffic that calibrates HBM byte counters")
     ap.add_argument("--prefill", choices=["inject", "synthetic"], default=None,
                     help="fill the KV cache by injecting every context row (default for c1, c2) or with "
                          "device-generated values at the scale injection produces (default for c3..c5)")
@@ -276,6 +279,16 @@ def main():
         torch.cuda.synchronize()
         for n in ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv"):
             breakdown[n] = roof(n, avg_ms(pr, n)) if n != "topk" else {"ms": round(avg_ms(pr, n), 4)}
+
+    if args.copy_mib > 0:
+        n = args.copy_mib * (1 << 20) // 4
+        src = torch.randn(n, device="cuda", dtype=torch.float32)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {n * 4} bytes read and {n * 4} bytes written per launch, 3 launches")
+        del src, dst
 
     cpu = None
     if W is not None:

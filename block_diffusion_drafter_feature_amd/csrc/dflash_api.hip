@@ -110,13 +110,15 @@ InjectWs<T> carve_inject(Carver& cv, const dflash_config* c, int rows) {
   return w;
 }
 
-// Context splits per (sequence, kv head): enough work-groups to cover the chip about 8
-// times, each split at least 64 context rows.
+// Context splits per (sequence, kv head): about two four-wave work-groups per compute
+// unit over the grid, each split at least two 64-key tiles (so the 32 KB of (O, m, l)
+// partials a split writes stay well below the K/V bytes it reads), at most 64 splits.
 int attn_splits(const dflash_config* c, int batch, int cap) {
-  const int want = (2048 + batch * c->n_kv_heads - 1) / (batch * c->n_kv_heads);
-  const int maxs = (cap + 63) / 64;
+  const int pairs = batch * c->n_kv_heads;
+  const int want = (512 + pairs - 1) / pairs;
+  const int maxs = cap / 128;
   int s = want < maxs ? want : maxs;
-  return s < 1 ? 1 : (s > 64 ? 64 : s);
+  return s < 1 ? 1 : (s > kCombineMaxSplits ? kCombineMaxSplits : s);
 }
 
 template <typename T>
@@ -290,14 +292,33 @@ int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv
 
 template <typename T, int HD, int G>
 hipError_t launch_attn(const AttnArgs<T>& a, int B, hipStream_t s) {
-  constexpr int HW = G < 2 ? G : 2;
   dim3 grid(a.S, a.Hkv, B);
-  block_attn_kernel<T, HD, G, HW><<<grid, 64 * (G / HW), 0, s>>>(a);
+  block_attn_kernel<T, HD, G><<<grid, 256, 0, s>>>(a);
   return hipGetLastError();
 }
 
+// split partials merge: 2 split groups for S <= 3, else 4; each wave loads NS splits
+template <typename T, int HD, int SG, int NS>
+hipError_t combine_grid(const AttnArgs<T>& a, int H, int Hkv, int B, hipStream_t s) {
+  constexpr int rows_per_block = (64 / (HD / 8)) * (4 / SG);
+  attn_combine_kernel<T, HD, SG, NS><<<dim3(16 / rows_per_block, H, B), 256, 0, s>>>(a.part_o, a.part_ml, a.out, H,
+                                                                                     Hkv, a.S);
+  return hipGetLastError();
+}
+template <typename T, int HD>
+hipError_t launch_combine(const AttnArgs<T>& a, int H, int Hkv, int B, hipStream_t s) {
+  const int S = a.S;
+  if (S <= 2) return combine_grid<T, HD, 2, 1>(a, H, Hkv, B, s);
+  if (S <= 3) return combine_grid<T, HD, 2, 2>(a, H, Hkv, B, s);
+  if (S <= 4) return combine_grid<T, HD, 4, 1>(a, H, Hkv, B, s);
+  if (S <= 8) return combine_grid<T, HD, 4, 2>(a, H, Hkv, B, s);
+  if (S <= 16) return combine_grid<T, HD, 4, 4>(a, H, Hkv, B, s);
+  if (S <= 32) return combine_grid<T, HD, 4, 8>(a, H, Hkv, B, s);
+  return combine_grid<T, HD, 4, 16>(a, H, Hkv, B, s);
+}
+
 template <typename T>
-hipError_t run_attention(const dflash_config* c, const AttnArgs<T>& a, int B, T* out, hipStream_t s) {
+hipError_t run_attention(const dflash_config* c, const AttnArgs<T>& a, int B, hipStream_t s) {
   const int G = c->n_heads / c->n_kv_heads;
   hipError_t e;
   if (c->head_dim == 64) {
@@ -305,11 +326,9 @@ hipError_t run_attention(const dflash_config* c, const AttnArgs<T>& a, int B, T*
   } else {
     e = G == 1 ? launch_attn<T, 128, 1>(a, B, s) : G == 2 ? launch_attn<T, 128, 2>(a, B, s) : launch_attn<T, 128, 4>(a, B, s);
   }
-  if (e != hipSuccess) return e;
-  dim3 grid(16, c->n_heads, B);
-  if (c->head_dim == 64) attn_combine_kernel<T, 64><<<grid, 64, 0, s>>>(a.part_o, a.part_ml, out, c->n_heads, c->n_kv_heads, a.S);
-  else attn_combine_kernel<T, 128><<<grid, 128, 0, s>>>(a.part_o, a.part_ml, out, c->n_heads, c->n_kv_heads, a.S);
-  return hipGetLastError();
+  if (e != hipSuccess || a.S == 1) return e;
+  return c->head_dim == 64 ? launch_combine<T, 64>(a, c->n_heads, c->n_kv_heads, B, s)
+                           : launch_combine<T, 128>(a, c->n_heads, c->n_kv_heads, B, s);
 }
 
 // pre-sublayer input: u = RMSNorm(x; g), conv'd when enabled, rounded to T into W.ut
@@ -382,9 +401,9 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
                                W.scratch_bytes)));
     pr.end(DFLASH_PROBE_QKV);
     AttnArgs<T> aa{W.q, W.kb, W.vbt, static_cast<const T*>(kv->k[l]), static_cast<const T*>(kv->vt[l]), ctx_len,
-                   W.part_o, W.part_ml, H, Hkv, kv->cap, W.S, 1.4426950408889634f / sqrtf(static_cast<float>(hd))};
+                   W.part_o, W.part_ml, W.o, H, Hkv, kv->cap, W.S, 1.4426950408889634f / sqrtf(static_cast<float>(hd))};
     pr.begin(DFLASH_PROBE_ATTN);
-    GEMM_CHECK(run_attention<T>(c, aa, B, W.o, s));
+    GEMM_CHECK(run_attention<T>(c, aa, B, s));
     pr.end(DFLASH_PROBE_ATTN);
     if ((rc = post_sublayer<T, T>(c, L, 1, L.w_o, W.o, hq, M, W, pr, DFLASH_PROBE_O, s))) return rc;
     // feed-forward sublayer
