@@ -24,6 +24,9 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
     # keep the compiler from forming packed fp32 ops (v_pk_*_f32) on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in VGPRs: keeps GEMM accumulators in place across the K loop
+    # (the AGPR form made the register allocator rotate them with copies every slab)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-Wno-unused-result",
 ]
 

@@ -14,9 +14,12 @@
 //    waves split K, stream their slice of W straight from HBM into registers
 //    (16 B per lane per fragment, two register stages in flight) and reduce
 //    through LDS in a fixed order.
-//  * gemm_tiled  : M > 64.  128x128 output tile per work-group, A and W tiles
-//    staged through LDS (register prefetch of the next K slab while the matrix
-//    cores work on the current one), 2x2 waves of 64x64.
+//  * gemm_big    : M > 64 with bf16 operands.  128 or 256 square-or-oblong output
+//    tiles per work-group of 2x2 waves, double-buffered LDS slabs, one barrier per
+//    64-wide K slab, tile shape and split-K chosen per GEMM by a cost model.
+//  * gemm_tiled  : M > 64 otherwise (fp32, or A given in fp32).  128x128 output tile
+//    per work-group, A and W tiles staged through LDS (register prefetch of the next
+//    K slab while the matrix cores work on the current one), 2x2 waves of 64x64.
 // Both are deterministic (no atomics).
 #pragma once
 
@@ -292,6 +295,160 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ 
   }
 }
 
+// ---------------------------------------------------------------------------------
+// large-tile GEMM (bf16 operands, M > 64)
+// ---------------------------------------------------------------------------------
+// BM x BN output tile per work-group of four waves (2 x 2); each wave owns a
+// (BM/2) x (BN/2) block of 16x16 matrix-core tiles, so at 256 x 256 every fragment read
+// from LDS feeds eight MFMAs and the work-group reads 128 FLOP per byte of A and W.  K
+// advances in 64-wide slabs through a double-buffered LDS tile: the next slab is fetched
+// into registers with coalesced 16-byte loads (eight lanes per 128-byte row) while the
+// matrix cores consume the current one, then written to the other buffer; one barrier per
+// slab.  blockIdx.x enumerates output tiles with the M tile fastest, so the work-groups
+// that share a W tile are dispatched together.  With partial != nullptr (split-K),
+// blockIdx.y = z covers K range [z*kslice, (z+1)*kslice) and the raw fp32 tile goes to
+// partial[z][m][ldp].
+template <typename T, int BM, int BN, class Epi>
+__global__ __launch_bounds__(256) void gemm_big_kernel(const T* __restrict__ A, int lda,
+                                                      const int32_t* __restrict__ arows, int M, int K, Epi epi,
+                                                      int tiles_m, int kslice, float* __restrict__ partial,
+                                                      int ldp) {
+  typedef Frag<T> F;
+  typedef typename F::type frag_t;
+  static_assert(sizeof(T) == 2, "bf16 operands");
+  constexpr int BK = 64, EPB = 8, CPR = BK / EPB, LD = BK + EPB;
+  constexpr int TM = BM / 32, TN = BN / 32;                 // 16x16 tiles per wave
+  constexpr int CA = BM * CPR / 256, CB = BN * CPR / 256;   // 16-byte chunks per thread per slab
+  constexpr int STAGE = (BM + BN) * LD;
+  constexpr int SMEM_AB = 2 * STAGE * static_cast<int>(sizeof(T));
+  constexpr int SMEM_EP = 64 * (BN + 1) * static_cast<int>(sizeof(float));
+  constexpr int SMEM = SMEM_AB > SMEM_EP ? SMEM_AB : SMEM_EP;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+  T* const lds = reinterpret_cast<T*>(smem);
+  float* const Ct = reinterpret_cast<float*>(smem);
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+  const int m0 = mt * BM, vt0 = nt * (BN / 16);
+
+  // Rows past M (A) or past the last weight row (W) are clamped to a valid row: their
+  // products only reach accumulators whose results are never stored, so every load is
+  // unconditional and the K loop has no branches.
+  const T* ap[CA];
+  const T* bp[CB];
+  const T* w0 = epi.wrow(vt0, 0);   // the tile's first column always exists
+#pragma unroll
+  for (int q = 0; q < CA; ++q) {
+    const int idx = q * 256 + tid, r = idx / CPR, ck = idx % CPR, m = m0 + r < M ? m0 + r : M - 1;
+    ap[q] = A + static_cast<size_t>(arows ? arows[m] : m) * lda + ck * EPB;
+  }
+#pragma unroll
+  for (int q = 0; q < CB; ++q) {
+    const int idx = q * 256 + tid, r = idx / CPR, ck = idx % CPR;
+    const T* wr = epi.wrow(vt0 + r / 16, r % 16);
+    bp[q] = (wr ? wr : w0) + ck * EPB;
+  }
+  u32x4_t ra[CA], rb[CB];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int q = 0; q < CA; ++q) ra[q] = *reinterpret_cast<const u32x4_t*>(ap[q] + k0);
+#pragma unroll
+    for (int q = 0; q < CB; ++q) rb[q] = *reinterpret_cast<const u32x4_t*>(bp[q] + k0);
+  };
+  auto sstore = [&](T* buf) {
+#pragma unroll
+    for (int q = 0; q < CA; ++q) {
+      const int idx = q * 256 + tid, r = idx / CPR, ck = idx % CPR;
+      *reinterpret_cast<u32x4_t*>(buf + r * LD + ck * EPB) = ra[q];
+    }
+#pragma unroll
+    for (int q = 0; q < CB; ++q) {
+      const int idx = q * 256 + tid, r = idx / CPR, ck = idx % CPR;
+      *reinterpret_cast<u32x4_t*>(buf + (BM + r) * LD + ck * EPB) = rb[q];
+    }
+  };
+
+  f32x4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const T* buf) {
+    const T* As = buf + (wm * (BM / 2) + r16) * LD + g * 8;
+    const T* Bs = buf + (BM + wn * (BN / 2) + r16) * LD + g * 8;
+#pragma unroll
+    for (int ks = 0; ks < BK / 32; ++ks) {
+      frag_t af[TM], bf[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) af[i] = F::load(As + i * 16 * LD + ks * 32);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bf[j] = F::load(Bs + j * 16 * LD + ks * 32);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j) acc[i][j] = F::mma(acc[i][j], af[i], bf[j]);
+    }
+  };
+
+  // K loop: slab kt computes from buffer kt & 1 while slab kt + 1 is in registers; the
+  // fetch two slabs ahead is clamped to the last slab (a harmless re-read at the end).
+  const int kofs = blockIdx.y * kslice;
+  const int KT = (partial ? kslice : K) / BK;
+  gload(kofs);
+  sstore(lds);
+  gload(kofs + (KT > 1 ? BK : 0));
+  __syncthreads();
+  for (int kt = 0; kt < KT - 1; ++kt) {
+    compute(lds + (kt & 1) * STAGE);
+    sstore(lds + ((kt + 1) & 1) * STAGE);
+    gload(kofs + (kt + 2 < KT ? kt + 2 : KT - 1) * BK);
+    __syncthreads();
+  }
+  compute(lds + ((KT - 1) & 1) * STAGE);
+  __syncthreads();
+
+  if (partial) {
+    float* pz = partial + static_cast<size_t>(blockIdx.y) * M * ldp;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = m0 + wm * (BM / 2) + i * 16 + 4 * g + e;
+          if (m < M) pz[static_cast<size_t>(m) * ldp + vt0 * 16 + wn * (BN / 2) + j * 16 + r16] = acc[i][j][e];
+        }
+    return;
+  }
+  // epilogue, 64 rows at a time through LDS
+#pragma unroll
+  for (int h = 0; h < BM / 64; ++h) {
+    // 16-row tile i of wave row wm covers tile rows wm * BM/2 + 16 i ...; those in this chunk go to Ct
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r0 = wm * (BM / 2) + i * 16 - h * 64;
+      if (r0 >= 0 && r0 < 64) {
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) Ct[(r0 + 4 * g + e) * (BN + 1) + wn * (BN / 2) + j * 16 + r16] = acc[i][j][e];
+      }
+    }
+    __syncthreads();
+    for (int e = tid; e < 64 * BN; e += 256) {
+      const int r = e / BN, c = e % BN;
+      const int m = m0 + h * 64 + r;
+      if (m < M) {
+        const int pc = (((c >> 4) ^ Epi::PX) << 4) | ((c & 15) ^ Epi::PC);
+        epi.apply(vt0 + (c >> 4), m, c & 15, Ct[r * (BN + 1) + c], Ct[r * (BN + 1) + pc]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 // Split-K reduction: sum the partial tiles in z order, then the epilogue.  One thread per
 // (row, virtual column).
 template <class Epi>
@@ -331,10 +488,59 @@ inline int splitk_plan(int M, int K, int n_vtiles) {
   return ks;
 }
 
+// Large-tile plan (bf16 operands, M > 16).  Up to 64 rows the GEMM streams the weights
+// once through 64 x 128 LDS tiles.  Above, the tile shape and split-K factor that
+// minimise a small cost model: the GEMM's work at the sustained rate measured for the
+// tile shape on MI355X (large grids, cold weights), times the padding of M and N to
+// whole tiles and the quantisation of the grid into waves of resident work-groups, plus
+// the round trip of the fp32 partials when K is split.
+struct BigPlan {
+  int bm, bn, ks;
+};
+inline BigPlan big_plan(int M, int K, int n_vtiles) {
+  if (M <= 64) {
+    // weight streaming: 64 x 128 tiles, K split until the grid covers the 256 compute units
+    const int tiles = (n_vtiles * 16 + 127) / 128;
+    int ks = 1;
+    while (ks < 8 && tiles * ks < 256 && (K / 64) % (2 * ks) == 0 && K / 64 / (2 * ks) >= 2) ks *= 2;
+    return {64, 128, ks};
+  }
+  struct Shape {
+    int bm, bn, per_cu;
+    double tflops;
+  };
+  static const Shape shapes[] = {{256, 256, 1, 840.0}, {128, 256, 1, 755.0}, {256, 128, 1, 720.0}, {128, 128, 2, 750.0}};
+  const int N = n_vtiles * 16;
+  BigPlan best{128, 128, 1};
+  double best_t = 1e30;
+  for (const Shape& c : shapes) {
+    const long tm = (M + c.bm - 1) / c.bm, tn = (N + c.bn - 1) / c.bn;
+    const double work = 2.0 * static_cast<double>(tm * c.bm) * static_cast<double>(tn * c.bn) * K;
+    for (int ks = 1; ks <= 8; ks *= 2) {
+      if ((K / 64) % ks || K / 64 / ks < 2) break;
+      const long wgs = tm * tn * ks, slots = 256L * c.per_cu;
+      const double quant = static_cast<double>((wgs + slots - 1) / slots) * slots / wgs;
+      double t = work / (c.tflops * 1e12) * quant;
+      if (ks > 1) t += 2.0 * ks * M * static_cast<double>(tn * c.bn) * 4.0 / 4e12 + 3e-6;
+      if (t < best_t) {
+        best_t = t;
+        best = {c.bm, c.bn, ks};
+      }
+    }
+  }
+  return best;
+}
+
 template <typename T>
 inline size_t splitk_scratch_bytes(int M, int K, int n_vtiles) {
   const int ks = splitk_plan<T>(M, K, n_vtiles);
-  return ks > 1 ? static_cast<size_t>(ks) * M * (((n_vtiles + 7) / 8) * 128) * sizeof(float) : 0;
+  size_t b = ks > 1 ? static_cast<size_t>(ks) * M * (((n_vtiles + 7) / 8) * 128) * sizeof(float) : 0;
+  if (std::is_same<T, bf16_t>::value && M > 16 && K % 64 == 0) {
+    const BigPlan p = big_plan(M, K, n_vtiles);
+    const size_t ldp = static_cast<size_t>((n_vtiles * 16 + p.bn - 1) / p.bn) * p.bn;
+    if (p.ks > 1) b = std::max(b, static_cast<size_t>(p.ks) * M * ldp * sizeof(float));
+  }
+  return b;
 }
 
 // Skinny launch configuration (measured on MI355X with cold caches, M = 16, bf16): two
@@ -365,6 +571,33 @@ static hipError_t launch_skinny(const AS* A, int lda, const int32_t* arows, int 
   return hipGetLastError();
 }
 
+template <typename T, int BM, int BN, class Epi>
+static hipError_t launch_big_shape(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
+                                   const Epi& epi, int ks, float* scratch, hipStream_t s) {
+  const int tm = (M + BM - 1) / BM, tn = (n_vtiles * 16 + BN - 1) / BN, ldp = tn * BN;
+  gemm_big_kernel<T, BM, BN, Epi><<<dim3(tm * tn, ks), 256, 0, s>>>(A, lda, arows, M, K, epi, tm, K / ks,
+                                                                    ks > 1 ? scratch : nullptr, ldp);
+  if (ks > 1) {
+    const size_t n = static_cast<size_t>(M) * ldp;
+    gemm_splitk_epilogue_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(scratch, M, ldp, ks,
+                                                                                          n_vtiles, epi);
+  }
+  return hipGetLastError();
+}
+
+template <typename T, class Epi>
+static hipError_t launch_big(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
+                             hipStream_t s, float* scratch, size_t scratch_bytes) {
+  BigPlan p = big_plan(M, K, n_vtiles);
+  const size_t ldp = static_cast<size_t>((n_vtiles * 16 + p.bn - 1) / p.bn) * p.bn;
+  if (p.ks > 1 && (!scratch || scratch_bytes < static_cast<size_t>(p.ks) * M * ldp * sizeof(float))) p.ks = 1;
+  if (p.bm == 64) return launch_big_shape<T, 64, 128>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 256 && p.bn == 256) return launch_big_shape<T, 256, 256>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 128 && p.bn == 256) return launch_big_shape<T, 128, 256>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 256 && p.bn == 128) return launch_big_shape<T, 256, 128>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  return launch_big_shape<T, 128, 128>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+}
+
 // n_vtiles: number of virtual 16-column tiles (multiple of 2 when Epi::PX == 1).
 // K: multiple of 64.  scratch: split-K partials (>= splitk_scratch_bytes, or nullptr: no split).
 template <typename T, typename AS, class Epi>
@@ -372,8 +605,14 @@ static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, in
                            hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0) {
   if (M <= 0 || n_vtiles <= 0) return hipSuccess;
   if (M <= 16) return launch_skinny<T, AS, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value) {
+    if (K % 64 == 0) return launch_big<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
+  }
   if (M <= 32) return launch_skinny<T, AS, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 64) return launch_skinny<T, AS, 4>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value) {
+    if (K % 64 == 0) return launch_big<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
+  }
   const int ntx = (n_vtiles + 7) / 8, ldp = ntx * 128;
   int ks = splitk_plan<T>(M, K, n_vtiles);
   if (!scratch || scratch_bytes < splitk_scratch_bytes<T>(M, K, n_vtiles)) ks = 1;
