@@ -144,11 +144,11 @@ template <> struct Frag<float> {
 
 // ------------------------------------------------------------------ rotary encoding
 
-// cos/sin of the rotary angle pos * theta^(-2i/hd).  The angle is formed and
+// cos/sin of the rotary angle pos * theta^(-2i/hd) (log_theta = ln theta).  The angle is formed and
 // reduced to [-pi, pi] in double precision (context positions reach 10^5 and a
 // float angle would be off by ~1e-2 rad there), then evaluated in float.
-__device__ __forceinline__ void rope_cs(int pos, int i, int hd, float theta, float* c, float* s) {
-  const double inv = exp(-(2.0 * i / hd) * log(static_cast<double>(theta)));
+__device__ __forceinline__ void rope_cs(int pos, int i, int hd, double log_theta, float* c, float* s) {
+  const double inv = exp(-(2.0 * i / hd) * log_theta);
   double a = static_cast<double>(pos) * inv;
   const double two_pi = 6.283185307179586476925286766559;
   a -= two_pi * rint(a / two_pi);

@@ -4,6 +4,7 @@
 #include "dflash.h"
 
 #include "attention.h"
+#include <cmath>
 #include "common.h"
 #include "elementwise.h"
 #include "epilogues.h"
@@ -277,7 +278,7 @@ int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv
   e.hd = c->head_dim;
   e.B = B;
   e.cap = kv->cap;
-  e.theta = c->rope_theta;
+  e.log_theta = std::log(static_cast<double>(c->rope_theta));
   e.row_off = row_off;
   e.pos0 = pos0;
   e.n_new = n_new;
@@ -395,7 +396,7 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
     // attention sublayer
     if ((rc = pre_sublayer<T>(c, L, 0, L.g_attn, M, W, s))) return rc;
     EpiQKV<T> eq{static_cast<const T*>(L.w_q), static_cast<const T*>(L.w_k), static_cast<const T*>(L.w_v),
-                 d, H, Hkv, hd, c->rope_theta, ctx_len, W.q, W.kb, W.vbt};
+                 d, H, Hkv, hd, std::log(static_cast<double>(c->rope_theta)), ctx_len, W.q, W.kb, W.vbt};
     pr.begin(DFLASH_PROBE_QKV);
     GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, (hq + 2 * Hkv * hd) / 16, eq, s, W.scratch,
                                W.scratch_bytes)));

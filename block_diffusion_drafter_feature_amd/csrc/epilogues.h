@@ -4,7 +4,13 @@
 //   wrow(vt, c)       pointer to the W row feeding column c of virtual tile vt (nullptr: zero)
 //   wseg(vt, b, n)    the weight matrix holding tile vt's rows: base b, n bytes (n = 0 when
 //                     the tile is past the end); every row of a tile lies in one matrix
-//   apply(vt, m, c, v, partner)
+//   Row, row(m)       per-row facts the epilogue needs (owning sequence, position), worked
+//                     out once per output row and shared by all its columns
+//   colmajor(vt)      true when tile vt's outputs are contiguous along m (transposed
+//                     stores): the kernels then hand consecutive rows to consecutive threads
+//   kDirect           true when Row is empty and no tile is colmajor (plain per-element
+//                     epilogues need no staging tile)
+//   apply(vt, m, row, c, v, partner)
 #pragma once
 
 #include "common.h"
@@ -42,6 +48,7 @@ struct EpiStore {
   int ldo;
   int mode;
   static constexpr int PX = 0, PC = 0;
+  static constexpr bool kDirect = true;
   __device__ __forceinline__ const T* wrow(int vt, int c) const {
     const int n = vt * 16 + c;
     if (n >= w.off[w.n_seg]) return nullptr;
@@ -59,7 +66,10 @@ struct EpiStore {
     b = w.p[s];
     n = static_cast<uint32_t>(static_cast<size_t>(w.off[s + 1] - w.off[s]) * w.K * sizeof(T));
   }
-  __device__ __forceinline__ void apply(int vt, int m, int c, float v, float) const {
+  struct Row {};
+  __device__ __forceinline__ Row row(int) const { return Row{}; }
+  __device__ __forceinline__ bool colmajor(int) const { return false; }
+  __device__ __forceinline__ void apply(int vt, int m, const Row&, int c, float v, float) const {
     const int n = vt * 16 + c;
     if (n >= w.off[w.n_seg]) return;
     float* o = out + static_cast<size_t>(m) * ldo + n;
@@ -82,12 +92,13 @@ struct EpiQKV {
   const T* wk;
   const T* wv;
   int K, H, Hkv, hd;
-  float theta;
+  double log_theta;        // ln(rope theta)
   const int32_t* ctx_len;  // [B]
   T* q;                    // [M][H][hd]
   T* kb;                   // [B][Hkv][16][hd]
   T* vbt;                  // [B][Hkv][hd][16]
   static constexpr int PX = 0, PC = 8;
+  static constexpr bool kDirect = false;
   // virtual tiles: H*hd/16 query tiles, Hkv*hd/16 key tiles (both RoPE-paired), Hkv*hd/16 value tiles
   __device__ __forceinline__ const T* wrow(int vt, int c) const {
     const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
@@ -106,7 +117,12 @@ struct EpiQKV {
     else if (vt < tq + 2 * tk) { b = wv; n = static_cast<uint32_t>(Hkv * hd * rb); }
     else { b = wq; n = 0; }
   }
-  __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
+  struct Row {
+    int pos;   // position of block row m: its sequence's context length + m % 16
+  };
+  __device__ __forceinline__ Row row(int m) const { return Row{ctx_len[m >> 4] + (m & 15)}; }
+  __device__ __forceinline__ bool colmajor(int vt) const { return vt >= (H + Hkv) * hd / 16; }
+  __device__ __forceinline__ void apply(int vt, int m, const Row& rw, int c, float v, float pv) const {
     const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
     const int b = m >> 4, j = m & 15;
     if (vt < tq + tk) {
@@ -115,7 +131,7 @@ struct EpiQKV {
       const int head = t / tph, tt = t % tph;
       const int dim = rope_dim(tt, c, hd);
       float cs, sn;
-      rope_cs(ctx_len[b] + j, 8 * tt + (c & 7), hd, theta, &cs, &sn);
+      rope_cs(rw.pos, 8 * tt + (c & 7), hd, log_theta, &cs, &sn);
       const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
       if (isq) q[(static_cast<size_t>(m) * H + head) * hd + dim] = from_f<T>(r);
       else kb[((static_cast<size_t>(b) * Hkv + head) * 16 + j) * hd + dim] = from_f<T>(r);
@@ -137,11 +153,12 @@ struct EpiInject {
   T* kc[16];
   T* vtc[16];
   int K, L, Hkv, hd, B, cap;
-  float theta;
+  double log_theta;        // ln(rope theta)
   const int32_t* row_off;  // [B+1]
   const int32_t* pos0;     // [B]
   const int32_t* n_new;    // [B]
   static constexpr int PX = 0, PC = 8;
+  static constexpr bool kDirect = false;
   // virtual tiles per layer: Hkv*hd/16 key tiles (RoPE-paired) then Hkv*hd/16 value tiles
   __device__ __forceinline__ const T* wrow(int vt, int c) const {
     const int tk = Hkv * hd / 16, tph = hd / 16;
@@ -161,25 +178,33 @@ struct EpiInject {
     b = t < tk ? wk[l] : wv[l];
     n = static_cast<uint32_t>(static_cast<size_t>(Hkv) * hd * K * sizeof(T));
   }
-  __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
-    const int tk = Hkv * hd / 16, tph = hd / 16;
-    const int l = vt / (2 * tk), t = vt % (2 * tk);
-    if (l >= L) return;
-    // sequence owning row m: row_off[b] <= m < row_off[b+1]
+  struct Row {
+    int b, pos;   // owning sequence and cache position of row m; b < 0: row not stored
+  };
+  // sequence owning row m: row_off[b] <= m < row_off[b+1]; rows past n_new[b] or outside
+  // the cache are dropped
+  __device__ __forceinline__ Row row(int m) const {
+    if (m < row_off[0] || m >= row_off[B]) return Row{-1, 0};
     int lo = 0, hi = B;
-    if (m < row_off[0] || m >= row_off[B]) return;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
       if (row_off[mid] <= m) lo = mid; else hi = mid;
     }
-    const int b = lo, i = m - row_off[b];
-    if (i >= n_new[b]) return;
-    const int pos = pos0[b] + i;
-    if (pos < 0 || pos >= cap) return;
+    const int i = m - row_off[lo];
+    const int pos = pos0[lo] + i;
+    if (i >= n_new[lo] || pos < 0 || pos >= cap) return Row{-1, 0};
+    return Row{lo, pos};
+  }
+  __device__ __forceinline__ bool colmajor(int vt) const { return vt % (2 * (Hkv * hd / 16)) >= Hkv * hd / 16; }
+  __device__ __forceinline__ void apply(int vt, int m, const Row& rw, int c, float v, float pv) const {
+    const int tk = Hkv * hd / 16, tph = hd / 16;
+    const int l = vt / (2 * tk), t = vt % (2 * tk);
+    if (l >= L || rw.b < 0) return;
+    const int b = rw.b, pos = rw.pos;
     if (t < tk) {
       const int head = t / tph, tt = t % tph, dim = rope_dim(tt, c, hd);
       float cs, sn;
-      rope_cs(pos, 8 * tt + (c & 7), hd, theta, &cs, &sn);
+      rope_cs(pos, 8 * tt + (c & 7), hd, log_theta, &cs, &sn);
       const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
       kc[l][((static_cast<size_t>(b) * Hkv + head) * cap + pos) * hd + dim] = from_f<T>(r);
     } else {
@@ -198,6 +223,7 @@ struct EpiSwiGLU {
   int K, Fd;
   T* h;  // [M][Fd]
   static constexpr int PX = 1, PC = 0;
+  static constexpr bool kDirect = true;
   __device__ __forceinline__ const T* wrow(int vt, int c) const {
     const int n = (vt >> 1) * 16 + c;
     if (n >= Fd) return nullptr;
@@ -207,7 +233,10 @@ struct EpiSwiGLU {
     b = (vt & 1) ? wu : wg;
     n = (vt >> 1) * 16 < Fd ? static_cast<uint32_t>(static_cast<size_t>(Fd) * K * sizeof(T)) : 0u;
   }
-  __device__ __forceinline__ void apply(int vt, int m, int c, float v, float pv) const {
+  struct Row {};
+  __device__ __forceinline__ Row row(int) const { return Row{}; }
+  __device__ __forceinline__ bool colmajor(int) const { return false; }
+  __device__ __forceinline__ void apply(int vt, int m, const Row&, int c, float v, float pv) const {
     if (vt & 1) return;
     const int n = (vt >> 1) * 16 + c;
     if (n >= Fd) return;

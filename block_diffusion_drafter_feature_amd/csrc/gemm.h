@@ -34,6 +34,31 @@ __device__ __forceinline__ typename Frag<T>::type load_a(const AS* p) {
   else return Frag<T>::load_f32(p);
 }
 
+// Epilogue of an output tile held in LDS: Ct[r][.] (row stride ldc) holds rows m_base + r
+// (r < rows) and the 16 columns of virtual tiles vt0 .. vt0 + nvt - 1.  The per-row facts
+// are worked out once per row; a tile whose stores run along m (Epi::colmajor) gives
+// consecutive rows to consecutive threads.  Called by every thread of the work-group;
+// rinfo holds >= rows entries.  Ends without a barrier (the caller syncs before reusing Ct).
+template <class Epi>
+__device__ __forceinline__ void epilogue_tile(const Epi& epi, const float* Ct, int ldc, int m_base, int rows,
+                                              int vt0, int nvt, int M, typename Epi::Row* rinfo) {
+  const int nth = blockDim.x, tid = threadIdx.x;
+  for (int r = tid; r < rows; r += nth) rinfo[r] = epi.row(m_base + r < M ? m_base + r : M - 1);
+  __syncthreads();
+  const int per = rows * 16;
+  for (int v = 0; v < nvt; ++v) {
+    const int vt = vt0 + v;
+    const bool cm = epi.colmajor(vt);
+    for (int e = tid; e < per; e += nth) {
+      const int r = cm ? e % rows : e >> 4, c = cm ? e / rows : e & 15;
+      const int m = m_base + r;
+      if (m >= M) continue;
+      const float* row = Ct + r * ldc;
+      epi.apply(vt, m, rinfo[r], c, row[v * 16 + c], row[((v ^ Epi::PX) << 4) | (c ^ Epi::PC)]);
+    }
+  }
+}
+
 // ---------------------------------------------------------------------------------
 // skinny GEMM
 // ---------------------------------------------------------------------------------
@@ -141,13 +166,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
     const int mt = t / NT, nt = t % NT;
     tile[mt * 16 + 4 * (l >> 4) + i][nt * 16 + (l & 15)] = s;
   }
-  __syncthreads();
-  for (int e = threadIdx.x; e < ROWS * TW; e += 64 * NW) {
-    const int m = e / TW, c = e % TW;
-    if (m >= M) continue;
-    const int pc = (((c >> 4) ^ Epi::PX) << 4) | ((c & 15) ^ Epi::PC);
-    epi.apply(vt0 + (c >> 4), m, c & 15, tile[m][c], tile[m][pc]);
-  }
+  __shared__ typename Epi::Row rinfo[ROWS];
+  epilogue_tile(epi, &tile[0][0], TW + 1, 0, ROWS, vt0, NT, M, rinfo);
 }
 
 // ---------------------------------------------------------------------------------
@@ -283,14 +303,8 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ 
             Ct[(i * 16 + 4 * g + e) * (BN + 1) + wn * 64 + j * 16 + r16] = acc[i][j][e];
     }
     __syncthreads();
-    for (int e = tid; e < 64 * BN; e += 256) {
-      const int r = e / BN, c = e % BN;
-      const int m = m0 + half * 64 + r;
-      if (m < M) {
-        const int pc = (((c >> 4) ^ Epi::PX) << 4) | ((c & 15) ^ Epi::PC);
-        epi.apply(vt0 + (c >> 4), m, c & 15, Ct[r * (BN + 1) + c], Ct[r * (BN + 1) + pc]);
-      }
-    }
+    __shared__ typename Epi::Row rinfo[64];
+    epilogue_tile(epi, Ct, BN + 1, m0 + half * 64, 64, vt0, BN / 16, M, rinfo);
     __syncthreads();
   }
 }
@@ -437,36 +451,66 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const T* __restrict__ A, 
       }
     }
     __syncthreads();
-    for (int e = tid; e < 64 * BN; e += 256) {
-      const int r = e / BN, c = e % BN;
-      const int m = m0 + h * 64 + r;
-      if (m < M) {
-        const int pc = (((c >> 4) ^ Epi::PX) << 4) | ((c & 15) ^ Epi::PC);
-        epi.apply(vt0 + (c >> 4), m, c & 15, Ct[r * (BN + 1) + c], Ct[r * (BN + 1) + pc]);
-      }
-    }
+    __shared__ typename Epi::Row rinfo[64];
+    epilogue_tile(epi, Ct, BN + 1, m0 + h * 64, 64, vt0, BN / 16, M, rinfo);
     __syncthreads();
   }
 }
 
-// Split-K reduction: sum the partial tiles in z order, then the epilogue.  One thread per
-// (row, virtual column).
+// Split-K reduction for epilogues that need no per-row facts and store along n
+// (Epi::kDirect): one thread per (row, column), partials summed in z order.
 template <class Epi>
-__global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* __restrict__ partial, int M,
-                                                                   int ldp, int ks, int n_vtiles, Epi epi) {
+__global__ __launch_bounds__(256) void gemm_splitk_direct_kernel(const float* __restrict__ partial, int M, int ldp,
+                                                                 int ks, int n_vtiles, Epi epi) {
   const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
   if (e >= static_cast<size_t>(M) * ldp) return;
   const int m = static_cast<int>(e / ldp), col = static_cast<int>(e % ldp);
   const int vt = col >> 4, c = col & 15;
   if (vt >= n_vtiles) return;
   const int pcol = ((vt ^ Epi::PX) << 4) | (c ^ Epi::PC);
+  const size_t zs = static_cast<size_t>(M) * ldp;
+  const float* p = partial + static_cast<size_t>(m) * ldp;
   float v = 0.f, pv = 0.f;
   for (int z = 0; z < ks; ++z) {
-    const float* pz = partial + static_cast<size_t>(z) * M * ldp + static_cast<size_t>(m) * ldp;
-    v += pz[col];
-    pv += pz[pcol];
+    v += p[z * zs + col];
+    if (Epi::PX || Epi::PC) pv += p[z * zs + pcol];
   }
-  epi.apply(vt, m, c, v, pv);
+  epi.apply(vt, m, epi.row(m), c, v, pv);
+}
+
+template <class Epi>
+static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks, int n_vtiles, const Epi& epi,
+                                   hipStream_t s);
+
+// Split-K reduction: sum the partial tiles in z order into an LDS block of 16 rows x 64
+// columns (each wave reads one 256-byte row segment of every partial), then the epilogue.
+// grid (ldp / 64, ceil(M / 16)), 256 threads.
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* __restrict__ partial, int M,
+                                                                   int ldp, int ks, int n_vtiles, Epi epi) {
+  __shared__ float Ct[16 * 65];
+  __shared__ typename Epi::Row rinfo[16];
+  const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 16;
+  const int r = threadIdx.x >> 6, cc = threadIdx.x & 63;
+  const size_t zs = static_cast<size_t>(M) * ldp;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const int m = m0 + 4 * k + r;
+    float v = 0.f;
+    if (m < M) {
+      const float* p = partial + static_cast<size_t>(m) * ldp + c0 + cc;
+      float part[8];
+#pragma unroll
+      for (int z = 0; z < 8; ++z) part[z] = z < ks ? p[z * zs] : 0.f;
+#pragma unroll
+      for (int z = 0; z < 8; ++z) v += part[z];
+      for (int z = 8; z < ks; ++z) v += p[z * zs];
+    }
+    Ct[(4 * k + r) * 65 + cc] = v;
+  }
+  __syncthreads();
+  const int vt0 = c0 / 16, nvt = min(4, n_vtiles - vt0);
+  epilogue_tile(epi, Ct, 65, m0, 16, vt0, nvt, M, rinfo);
 }
 
 // ---------------------------------------------------------------------------------
@@ -571,6 +615,18 @@ static hipError_t launch_skinny(const AS* A, int lda, const int32_t* arows, int 
   return hipGetLastError();
 }
 
+template <class Epi>
+static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks, int n_vtiles, const Epi& epi,
+                                   hipStream_t s) {
+  if (Epi::kDirect) {
+    const size_t n = static_cast<size_t>(M) * ldp;
+    gemm_splitk_direct_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(partial, M, ldp, ks,
+                                                                                        n_vtiles, epi);
+  } else {
+    gemm_splitk_epilogue_kernel<Epi><<<dim3(ldp / 64, (M + 15) / 16), 256, 0, s>>>(partial, M, ldp, ks, n_vtiles, epi);
+  }
+}
+
 template <typename T, int BM, int BN, class Epi>
 static hipError_t launch_big_shape(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
                                    const Epi& epi, int ks, float* scratch, hipStream_t s) {
@@ -578,9 +634,7 @@ static hipError_t launch_big_shape(const T* A, int lda, const int32_t* arows, in
   gemm_big_kernel<T, BM, BN, Epi><<<dim3(tm * tn, ks), 256, 0, s>>>(A, lda, arows, M, K, epi, tm, K / ks,
                                                                     ks > 1 ? scratch : nullptr, ldp);
   if (ks > 1) {
-    const size_t n = static_cast<size_t>(M) * ldp;
-    gemm_splitk_epilogue_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(scratch, M, ldp, ks,
-                                                                                          n_vtiles, epi);
+    launch_splitk_epilogue(scratch, M, ldp, ks, n_vtiles, epi, s);
   }
   return hipGetLastError();
 }
@@ -620,9 +674,7 @@ static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, in
   gemm_tiled_kernel<T, AS, Epi><<<grid, 256, 0, s>>>(A, lda, arows, M, K, epi, K / ks, ks > 1 ? scratch : nullptr,
                                                      ldp);
   if (ks > 1) {
-    const size_t n = static_cast<size_t>(M) * ldp;
-    gemm_splitk_epilogue_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(scratch, M, ldp, ks,
-                                                                                          n_vtiles, epi);
+    launch_splitk_epilogue(scratch, M, ldp, ks, n_vtiles, epi, s);
   }
   return hipGetLastError();
 }
