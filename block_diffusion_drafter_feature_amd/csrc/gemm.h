@@ -8,19 +8,21 @@
 // tile hold columns that belong together (a RoPE pair d, d+hd/2; a gate/up pair)
 // so the epilogue can combine them without another pass.
 //
-// Two kernels:
-//  * gemm_skinny : M <= 64 (the drafted block of 1..4 sequences).  Weight
+// Three kernels:
+//  * gemm_skinny : M <= 16 (one drafted block), and M <= 64 when gemm_pipe does not
+//    apply (fp32).  Weight
 //    streaming: each work-group owns NT virtual tiles over the whole K; its NW
 //    waves split K, stream their slice of W straight from HBM into registers
 //    (16 B per lane per fragment, two register stages in flight) and reduce
 //    through LDS in a fixed order.
-//  * gemm_big    : M > 64 with bf16 operands.  128 or 256 square-or-oblong output
-//    tiles per work-group of 2x2 waves, double-buffered LDS slabs, one barrier per
-//    64-wide K slab, tile shape and split-K chosen per GEMM by a cost model.
-//  * gemm_tiled  : M > 64 otherwise (fp32, or A given in fp32).  128x128 output tile
-//    per work-group, A and W tiles staged through LDS (register prefetch of the next
-//    K slab while the matrix cores work on the current one), 2x2 waves of 64x64.
-// Both are deterministic (no atomics).
+//  * gemm_pipe   : bf16 operands (A in bf16), M > 16.  64/128/256 x 128 output tiles per
+//    work-group of 2x2 waves; 64-wide K slabs stream from memory straight into a ring
+//    of LDS slots with several slabs in flight; tile shape and split-K per GEMM shape.
+//  * gemm_tiled  : M > 64 when gemm_pipe does not apply (fp32, or A given in fp32).
+//    128x128 output tile per work-group, A and W tiles staged through LDS (register
+//    prefetch of the next K slab while the matrix cores work on the current one), 2x2
+//    waves of 64x64.
+// All are deterministic (no atomics).
 #pragma once
 
 #include "common.h"
@@ -310,78 +312,95 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------------
-// large-tile GEMM (bf16 operands, M > 64)
+// pipelined large-tile GEMM (bf16 operands): direct global -> LDS loads
 // ---------------------------------------------------------------------------------
-// BM x BN output tile per work-group of four waves (2 x 2); each wave owns a
-// (BM/2) x (BN/2) block of 16x16 matrix-core tiles, so at 256 x 256 every fragment read
-// from LDS feeds eight MFMAs and the work-group reads 128 FLOP per byte of A and W.  K
-// advances in 64-wide slabs through a double-buffered LDS tile: the next slab is fetched
-// into registers with coalesced 16-byte loads (eight lanes per 128-byte row) while the
-// matrix cores consume the current one, then written to the other buffer; one barrier per
-// slab.  blockIdx.x enumerates output tiles with the M tile fastest, so the work-groups
-// that share a W tile are dispatched together.  With partial != nullptr (split-K),
-// blockIdx.y = z covers K range [z*kslice, (z+1)*kslice) and the raw fp32 tile goes to
-// partial[z][m][ldp].
-template <typename T, int BM, int BN, class Epi>
-__global__ __launch_bounds__(256) void gemm_big_kernel(const T* __restrict__ A, int lda,
-                                                      const int32_t* __restrict__ arows, int M, int K, Epi epi,
-                                                      int tiles_m, int kslice, float* __restrict__ partial,
-                                                      int ldp) {
+// BM x BN output tile per work-group of four waves (2 x 2), each wave a (BM/2) x (BN/2)
+// block of 16x16 matrix-core tiles.  The 64-wide K slabs go straight from memory into a
+// ring of NS LDS slots (16-byte direct loads, no staging registers), so
+// NS - 1 slabs are in flight while the matrix cores consume one.  The direct loads are
+// issued as instructions the compiler does not track, so it adds no waits of its own for
+// them: each step waits (vmcnt) for this wave's loads of the slab about to be read, then
+// meets the other waves at a barrier without a memory fence, which leaves the loads of
+// later slabs in flight.  The loop ends by draining every load.
+// Slot layout: row r of a tile holds its 8 16-byte chunks (64 K values) with chunk c at
+// position c ^ ((r >> 1) & 7), so the 16 rows of a fragment read hit 16 distinct bank
+// groups.  A wave's direct load writes 1 KB = 8 rows; lane l fetches the chunk that
+// belongs at position l & 7 of row l >> 3.
+template <typename T, int STAGE, int I>
+__device__ __forceinline__ T* pipe_slot() {
+  __shared__ __attribute__((aligned(16))) T s[STAGE];
+  return s;
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// 16 bytes per lane from global address g into LDS at (wave-uniform) byte address lds + 16 * lane
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
+
+// wait until at most N of this wave's memory loads are outstanding and its LDS accesses
+// are done, then a work-group barrier that carries no memory fence
+template <int N>
+__device__ __forceinline__ void pipe_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
+
+template <typename T, int BM, int BN, int NS, class Epi>
+__global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A, int lda,
+                                                       const int32_t* __restrict__ arows, int M, int K, Epi epi,
+                                                       int tiles_m, int kslice, float* __restrict__ partial,
+                                                       int ldp) {
   typedef Frag<T> F;
   typedef typename F::type frag_t;
   static_assert(sizeof(T) == 2, "bf16 operands");
-  constexpr int BK = 64, EPB = 8, CPR = BK / EPB, LD = BK + EPB;
-  constexpr int TM = BM / 32, TN = BN / 32;                 // 16x16 tiles per wave
-  constexpr int CA = BM * CPR / 256, CB = BN * CPR / 256;   // 16-byte chunks per thread per slab
-  constexpr int STAGE = (BM + BN) * LD;
-  constexpr int SMEM_AB = 2 * STAGE * static_cast<int>(sizeof(T));
-  constexpr int SMEM_EP = 64 * (BN + 1) * static_cast<int>(sizeof(float));
-  constexpr int SMEM = SMEM_AB > SMEM_EP ? SMEM_AB : SMEM_EP;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  T* const lds = reinterpret_cast<T*>(smem);
-  float* const Ct = reinterpret_cast<float*>(smem);
+  static_assert(NS >= 2 && NS <= 4, "ring of 2..4 slots");
+  constexpr int TM = BM / 32, TN = BN / 32;        // 16x16 tiles per wave
+  constexpr int LA = BM / 32, LB = BN / 32;        // direct loads per thread per slab
+  constexpr int LPS = LA + LB;
+  constexpr int STAGE = (BM + BN) * 64;            // elements per slot
+  constexpr int EPR = 32;                          // epilogue rows per LDS pass
+  static_assert(EPR * (BN + 1) * 4 <= STAGE * 2, "epilogue pass must fit in one slot");
+  static_assert((NS - 2) * LPS < 64, "vmcnt range");
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
   const int m0 = mt * BM, vt0 = nt * (BN / 16);
 
-  // Rows past M (A) or past the last weight row (W) are clamped to a valid row: their
-  // products only reach accumulators whose results are never stored, so every load is
-  // unconditional and the K loop has no branches.
-  const T* ap[CA];
-  const T* bp[CB];
-  const T* w0 = epi.wrow(vt0, 0);   // the tile's first column always exists
+  // this lane's source chunk for each of its direct loads: LDS block (8 rows) j*4 + wave,
+  // row block*8 + lane/8, position lane%8 <- chunk (lane%8) ^ ((row >> 1) & 7).
+  // A: byte offsets from A (rows past M clamped); W: row pointers (past the end: row 0).
+  uint32_t aoff[LA];
+  const T* wsrc[LB];
+  const T* w0 = epi.wrow(vt0, 0);
 #pragma unroll
-  for (int q = 0; q < CA; ++q) {
-    const int idx = q * 256 + tid, r = idx / CPR, ck = idx % CPR, m = m0 + r < M ? m0 + r : M - 1;
-    ap[q] = A + static_cast<size_t>(arows ? arows[m] : m) * lda + ck * EPB;
+  for (int j = 0; j < LA; ++j) {
+    const int row = (j * 4 + wave) * 8 + (lane >> 3);
+    const int ck = (lane & 7) ^ ((row >> 1) & 7);
+    const int m = m0 + row < M ? m0 + row : M - 1;
+    aoff[j] = static_cast<uint32_t>((static_cast<size_t>(arows ? arows[m] : m) * lda + ck * 8) * sizeof(T));
   }
 #pragma unroll
-  for (int q = 0; q < CB; ++q) {
-    const int idx = q * 256 + tid, r = idx / CPR, ck = idx % CPR;
-    const T* wr = epi.wrow(vt0 + r / 16, r % 16);
-    bp[q] = (wr ? wr : w0) + ck * EPB;
+  for (int j = 0; j < LB; ++j) {
+    const int row = (j * 4 + wave) * 8 + (lane >> 3);
+    const int ck = (lane & 7) ^ ((row >> 1) & 7);
+    const T* wr = epi.wrow(vt0 + row / 16, row % 16);
+    wsrc[j] = (wr ? wr : w0) + ck * 8;
   }
-  u32x4_t ra[CA], rb[CB];
-  auto gload = [&](int k0) {
+  auto issue = [&](const T* slot, int k0) {
+    const uint32_t base = lds_addr(slot);
+    const char* ak = reinterpret_cast<const char*>(A + k0);
 #pragma unroll
-    for (int q = 0; q < CA; ++q) ra[q] = *reinterpret_cast<const u32x4_t*>(ap[q] + k0);
+    for (int j = 0; j < LA; ++j) dma16(ak + aoff[j], base + (j * 4 + wave) * 1024);
 #pragma unroll
-    for (int q = 0; q < CB; ++q) rb[q] = *reinterpret_cast<const u32x4_t*>(bp[q] + k0);
-  };
-  auto sstore = [&](T* buf) {
-#pragma unroll
-    for (int q = 0; q < CA; ++q) {
-      const int idx = q * 256 + tid, r = idx / CPR, ck = idx % CPR;
-      *reinterpret_cast<u32x4_t*>(buf + r * LD + ck * EPB) = ra[q];
-    }
-#pragma unroll
-    for (int q = 0; q < CB; ++q) {
-      const int idx = q * 256 + tid, r = idx / CPR, ck = idx % CPR;
-      *reinterpret_cast<u32x4_t*>(buf + (BM + r) * LD + ck * EPB) = rb[q];
-    }
+    for (int j = 0; j < LB; ++j) dma16(wsrc[j] + k0, base + (BM / 8 + j * 4 + wave) * 1024);
   };
 
   f32x4_t acc[TM][TN];
@@ -389,39 +408,48 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const T* __restrict__ A, 
   for (int i = 0; i < TM; ++i)
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  auto compute = [&](const T* buf) {
-    const T* As = buf + (wm * (BM / 2) + r16) * LD + g * 8;
-    const T* Bs = buf + (BM + wn * (BN / 2) + r16) * LD + g * 8;
+  const int sw = (r16 >> 1) & 7;
+  auto compute = [&](const T* slot) {
+    const T* As = slot + (wm * (BM / 2) + r16) * 64;
+    const T* Bs = slot + (BM + wn * (BN / 2) + r16) * 64;
+    frag_t af[2][TM], bf[2][TN];
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      frag_t af[TM], bf[TN];
+    for (int ks = 0; ks < 2; ++ks) {
+      const int pos = ((4 * ks + g) ^ sw) * 8;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[i] = F::load(As + i * 16 * LD + ks * 32);
+      for (int i = 0; i < TM; ++i) af[ks][i] = F::load(As + i * 16 * 64 + pos);
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bf[j] = F::load(Bs + j * 16 * LD + ks * 32);
+      for (int j = 0; j < TN; ++j) bf[ks][j] = F::load(Bs + j * 16 * 64 + pos);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = F::mma(acc[i][j], af[i], bf[j]);
-    }
+        for (int j = 0; j < TN; ++j) acc[i][j] = F::mma(acc[i][j], af[ks][i], bf[ks][j]);
   };
 
-  // K loop: slab kt computes from buffer kt & 1 while slab kt + 1 is in registers; the
-  // fetch two slabs ahead is clamped to the last slab (a harmless re-read at the end).
   const int kofs = blockIdx.y * kslice;
-  const int KT = (partial ? kslice : K) / BK;
-  gload(kofs);
-  sstore(lds);
-  gload(kofs + (KT > 1 ? BK : 0));
-  __syncthreads();
-  for (int kt = 0; kt < KT - 1; ++kt) {
-    compute(lds + (kt & 1) * STAGE);
-    sstore(lds + ((kt + 1) & 1) * STAGE);
-    gload(kofs + (kt + 2 < KT ? kt + 2 : KT - 1) * BK);
-    __syncthreads();
+  const int KT = (partial ? kslice : K) / 64;
+  auto kslab = [&](int t) { return kofs + (t < KT ? t : KT - 1) * 64; };   // past the end: re-read the last
+  T* const s0 = pipe_slot<T, STAGE, 0>();
+  T* const s1 = pipe_slot<T, STAGE, 1>();
+  T* const s2 = pipe_slot<T, (NS > 2 ? STAGE : 8), 2>();
+  T* const s3 = pipe_slot<T, (NS > 3 ? STAGE : 8), 3>();
+  auto slot = [&](int i) { return i == 0 ? s0 : i == 1 ? s1 : i == 2 ? s2 : s3; };
+#pragma unroll
+  for (int i = 0; i < NS - 1; ++i) issue(slot(i), kslab(i));
+  for (int kt = 0; kt < KT; kt += NS) {
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      if (kt + u < KT) {
+        pipe_barrier<(NS - 2) * LPS>();                  // slab kt+u landed; slot (u-1) free
+        issue(slot((u + NS - 1) % NS), kslab(kt + u + NS - 1));
+        compute(slot(u));
+      }
+    }
   }
-  compute(lds + ((KT - 1) & 1) * STAGE);
-  __syncthreads();
+  pipe_barrier<0>();   // drain the tail re-reads before the slots are reused
 
   if (partial) {
     float* pz = partial + static_cast<size_t>(blockIdx.y) * M * ldp;
@@ -436,14 +464,14 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const T* __restrict__ A, 
         }
     return;
   }
-  // epilogue, 64 rows at a time through LDS
+  // epilogue, EPR rows at a time through slot 0
+  float* const Ct = reinterpret_cast<float*>(s0);
 #pragma unroll
-  for (int h = 0; h < BM / 64; ++h) {
-    // 16-row tile i of wave row wm covers tile rows wm * BM/2 + 16 i ...; those in this chunk go to Ct
+  for (int h = 0; h < BM / EPR; ++h) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int r0 = wm * (BM / 2) + i * 16 - h * 64;
-      if (r0 >= 0 && r0 < 64) {
+      const int r0 = wm * (BM / 2) + i * 16 - h * EPR;
+      if (r0 >= 0 && r0 < EPR) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
 #pragma unroll
@@ -451,8 +479,8 @@ __global__ __launch_bounds__(256) void gemm_big_kernel(const T* __restrict__ A, 
       }
     }
     __syncthreads();
-    __shared__ typename Epi::Row rinfo[64];
-    epilogue_tile(epi, Ct, BN + 1, m0 + h * 64, 64, vt0, BN / 16, M, rinfo);
+    __shared__ typename Epi::Row rinfo[EPR];
+    epilogue_tile(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rinfo);
     __syncthreads();
   }
 }
@@ -532,54 +560,41 @@ inline int splitk_plan(int M, int K, int n_vtiles) {
   return ks;
 }
 
-// Large-tile plan (bf16 operands, M > 16).  Up to 64 rows the GEMM streams the weights
-// once through 64 x 128 LDS tiles.  Above, the tile shape and split-K factor that
-// minimise a small cost model: the GEMM's work at the sustained rate measured for the
-// tile shape on MI355X (large grids, cold weights), times the padding of M and N to
-// whole tiles and the quantisation of the grid into waves of resident work-groups, plus
-// the round trip of the fp32 partials when K is split.
+// Pipelined-GEMM plan (bf16 operands, A in bf16, M > 16): tile shape, LDS ring depth and split-K
+// factor, from measurements on MI355X.
+//  * M <= 64 (weight streaming): 64 x 128 tiles, 3 slots; K split until the grid has
+//    >= 128 work-groups.
+//  * M >= 384 with >= 256 tiles of 256 x 128: those tiles, 3 slots (each weight tile is
+//    read by fewer work-groups).
+//  * otherwise 128 x 128 tiles, 2 slots (two work-groups per compute unit); when there are
+//    fewer than 256 tiles, K split until the grid has >= 512 work-groups with >= 16 slabs
+//    (1024 K values) per split.
+// Splits keep K / 64 divisible (the fp32 partials are read back while still in cache).
 struct BigPlan {
-  int bm, bn, ks;
+  int bm, bn, ns, ks;
 };
 inline BigPlan big_plan(int M, int K, int n_vtiles) {
-  if (M <= 64) {
-    // weight streaming: 64 x 128 tiles, K split until the grid covers the 256 compute units
-    const int tiles = (n_vtiles * 16 + 127) / 128;
-    int ks = 1;
-    while (ks < 8 && tiles * ks < 256 && (K / 64) % (2 * ks) == 0 && K / 64 / (2 * ks) >= 2) ks *= 2;
-    return {64, 128, ks};
-  }
-  struct Shape {
-    int bm, bn, per_cu;
-    double tflops;
-  };
-  static const Shape shapes[] = {{256, 256, 1, 840.0}, {128, 256, 1, 755.0}, {256, 128, 1, 720.0}, {128, 128, 2, 750.0}};
   const int N = n_vtiles * 16;
-  BigPlan best{128, 128, 1};
-  double best_t = 1e30;
-  for (const Shape& c : shapes) {
-    const long tm = (M + c.bm - 1) / c.bm, tn = (N + c.bn - 1) / c.bn;
-    const double work = 2.0 * static_cast<double>(tm * c.bm) * static_cast<double>(tn * c.bn) * K;
-    for (int ks = 1; ks <= 8; ks *= 2) {
-      if ((K / 64) % ks || K / 64 / ks < 2) break;
-      const long wgs = tm * tn * ks, slots = 256L * c.per_cu;
-      const double quant = static_cast<double>((wgs + slots - 1) / slots) * slots / wgs;
-      double t = work / (c.tflops * 1e12) * quant;
-      if (ks > 1) t += 2.0 * ks * M * static_cast<double>(tn * c.bn) * 4.0 / 4e12 + 3e-6;
-      if (t < best_t) {
-        best_t = t;
-        best = {c.bm, c.bn, ks};
-      }
-    }
+  auto split = [&](long tiles, long want, int min_slabs) {
+    int ks = 1;
+    while (ks < 8 && tiles * ks < want && (K / 64) % (2 * ks) == 0 && K / 64 / (2 * ks) >= min_slabs) ks *= 2;
+    return ks;
+  };
+  if (M <= 64) {
+    const long tiles = (N + 127) / 128;
+    return {64, 128, 3, split(tiles, 128, 4)};
   }
-  return best;
+  const long t256 = static_cast<long>((M + 255) / 256) * ((N + 127) / 128);
+  if (M >= 384 && t256 >= 256) return {256, 128, 3, 1};
+  const long t128 = static_cast<long>((M + 127) / 128) * ((N + 127) / 128);
+  return {128, 128, 2, t128 >= 256 ? 1 : split(t128, 512, 16)};
 }
 
 template <typename T>
 inline size_t splitk_scratch_bytes(int M, int K, int n_vtiles) {
   const int ks = splitk_plan<T>(M, K, n_vtiles);
   size_t b = ks > 1 ? static_cast<size_t>(ks) * M * (((n_vtiles + 7) / 8) * 128) * sizeof(float) : 0;
-  if (std::is_same<T, bf16_t>::value && M > 16 && K % 64 == 0) {
+  if (std::is_same<T, bf16_t>::value && K % 64 == 0) {   // (an upper bound: also for GEMMs that take another path)
     const BigPlan p = big_plan(M, K, n_vtiles);
     const size_t ldp = static_cast<size_t>((n_vtiles * 16 + p.bn - 1) / p.bn) * p.bn;
     if (p.ks > 1) b = std::max(b, static_cast<size_t>(p.ks) * M * ldp * sizeof(float));
@@ -627,15 +642,13 @@ static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks,
   }
 }
 
-template <typename T, int BM, int BN, class Epi>
-static hipError_t launch_big_shape(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
-                                   const Epi& epi, int ks, float* scratch, hipStream_t s) {
+template <typename T, int BM, int BN, int NS, class Epi>
+static hipError_t launch_pipe_shape(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
+                                    const Epi& epi, int ks, float* scratch, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (n_vtiles * 16 + BN - 1) / BN, ldp = tn * BN;
-  gemm_big_kernel<T, BM, BN, Epi><<<dim3(tm * tn, ks), 256, 0, s>>>(A, lda, arows, M, K, epi, tm, K / ks,
-                                                                    ks > 1 ? scratch : nullptr, ldp);
-  if (ks > 1) {
-    launch_splitk_epilogue(scratch, M, ldp, ks, n_vtiles, epi, s);
-  }
+  gemm_pipe_kernel<T, BM, BN, NS, Epi><<<dim3(tm * tn, ks), 256, 0, s>>>(A, lda, arows, M, K, epi, tm, K / ks,
+                                                                        ks > 1 ? scratch : nullptr, ldp);
+  if (ks > 1) launch_splitk_epilogue(scratch, M, ldp, ks, n_vtiles, epi, s);
   return hipGetLastError();
 }
 
@@ -645,11 +658,9 @@ static hipError_t launch_big(const T* A, int lda, const int32_t* arows, int M, i
   BigPlan p = big_plan(M, K, n_vtiles);
   const size_t ldp = static_cast<size_t>((n_vtiles * 16 + p.bn - 1) / p.bn) * p.bn;
   if (p.ks > 1 && (!scratch || scratch_bytes < static_cast<size_t>(p.ks) * M * ldp * sizeof(float))) p.ks = 1;
-  if (p.bm == 64) return launch_big_shape<T, 64, 128>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
-  if (p.bm == 256 && p.bn == 256) return launch_big_shape<T, 256, 256>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
-  if (p.bm == 128 && p.bn == 256) return launch_big_shape<T, 128, 256>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
-  if (p.bm == 256 && p.bn == 128) return launch_big_shape<T, 256, 128>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
-  return launch_big_shape<T, 128, 128>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 64) return launch_pipe_shape<T, 64, 128, 3>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 256) return launch_pipe_shape<T, 256, 128, 3>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  return launch_pipe_shape<T, 128, 128, 2>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
 }
 
 // n_vtiles: number of virtual 16-column tiles (multiple of 2 when Epi::PX == 1).
@@ -658,15 +669,14 @@ template <typename T, typename AS, class Epi>
 static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
                            hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0) {
   if (M <= 0 || n_vtiles <= 0) return hipSuccess;
-  if (M <= 16) return launch_skinny<T, AS, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
   if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value) {
-    if (K % 64 == 0) return launch_big<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
+    // gemm_pipe addresses A with 32-bit byte offsets: contiguous rows only, < 2 GiB
+    if (M > 16 && K % 64 == 0 && !arows && static_cast<size_t>(M) * lda * sizeof(T) < (size_t{1} << 31))
+      return launch_big<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
   }
+  if (M <= 16) return launch_skinny<T, AS, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 32) return launch_skinny<T, AS, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 64) return launch_skinny<T, AS, 4>(A, lda, arows, M, K, n_vtiles, epi, s);
-  if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value) {
-    if (K % 64 == 0) return launch_big<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
-  }
   const int ntx = (n_vtiles + 7) / 8, ldp = ntx * 128;
   int ks = splitk_plan<T>(M, K, n_vtiles);
   if (!scratch || scratch_bytes < splitk_scratch_bytes<T>(M, K, n_vtiles)) ks = 1;
