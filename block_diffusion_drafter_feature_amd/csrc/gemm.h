@@ -602,11 +602,12 @@ inline size_t splitk_scratch_bytes(int M, int K, int n_vtiles) {
   return b;
 }
 
-// Skinny launch configuration (measured on MI355X with cold caches, M = 16, bf16): two
-// tiles per wave (a gate/up pair for SwiGLU) and K split over 4 waves when there are at
-// least 192 such work-groups and K <= 8192; one tile per wave and K split over 8 waves
-// otherwise; 8 k-steps per register stage at M = 16.  K must be
-// a multiple of NW * 32 * U; smaller splits are used when it is not.
+// Skinny launch configuration (measured on MI355X with cold weights, M = 16, bf16): K
+// split over 4 waves with 16 k-steps per register stage; two tiles per wave (a gate/up
+// pair for SwiGLU) when there are at least 192 such work-groups and K <= 8192, else one.
+// LM head 269 -> 246 us, gate/up 48 -> 44 us, down 30.5 -> 29.3 us against 8 k-steps.
+// At M = 32, 64 (fp32 only) shorter stages.  K must be a multiple of NW * 32 * U;
+// smaller stages and splits are used when it is not.
 template <typename T, typename AS, int MT, int NT, int NW, int U, class Epi>
 static bool try_skinny(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
                        hipStream_t s) {
@@ -618,11 +619,13 @@ static bool try_skinny(const AS* A, int lda, const int32_t* arows, int M, int K,
 template <typename T, typename AS, int MT, class Epi>
 static hipError_t launch_skinny(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
                                 const Epi& epi, hipStream_t s) {
-  constexpr int U = MT >= 4 ? 2 : (MT == 2 ? 4 : 8);
+  constexpr int U = MT >= 4 ? 2 : (MT == 2 ? 4 : 16);
   const bool wide = n_vtiles / 2 >= 192 && K <= 8192;
   bool ok = false;
   if (wide || Epi::PX) ok = try_skinny<T, AS, MT, 2, 4, U>(A, lda, arows, M, K, n_vtiles, epi, s);
-  if (!ok && !Epi::PX) ok = try_skinny<T, AS, MT, 1, 8, U>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok && !Epi::PX && MT == 1) ok = try_skinny<T, AS, MT, 1, 4, U>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok && (wide || Epi::PX)) ok = try_skinny<T, AS, MT, 2, 4, (U > 8 ? 8 : U)>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok && !Epi::PX) ok = try_skinny<T, AS, MT, 1, 8, (U > 8 ? 8 : U)>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (!ok && !Epi::PX) ok = try_skinny<T, AS, MT, 1, 8, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (!ok) ok = try_skinny<T, AS, MT, (Epi::PX ? 2 : 1), 4, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (!ok) ok = try_skinny<T, AS, MT, (Epi::PX ? 2 : 1), 2, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
