@@ -335,14 +335,14 @@ hipError_t run_attention(const dflash_config* c, const AttnArgs<T>& a, int B, hi
 // pre-sublayer input: u = RMSNorm(x; g), conv'd when enabled, rounded to T into W.ut
 template <typename T>
 int pre_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site, const void* gain, int M,
-                 DraftWs<T>& W, hipStream_t s) {
+                 DraftWs<T>& W, hipStream_t s, const T* emb = nullptr, const int32_t* ids = nullptr) {
   const int d = c->d_model;
   if (!c->use_conv) {
-    rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, W.ut, nullptr);
+    rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, W.ut, nullptr, emb, ids);
     LAUNCH_CHECK();
     return DFLASH_OK;
   }
-  rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, nullptr, W.uf);
+  rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, nullptr, W.uf, emb, ids);
   LAUNCH_CHECK();
   EpiStore<T> e{seg1<T>(L.conv_gen[site], 2 * (d / 16), d), W.delta, 2 * (d / 16), STORE};
   GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, e, s, W.scratch,
@@ -388,13 +388,13 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
   const int M = 16 * B, d = c->d_model, H = c->n_heads, Hkv = c->n_kv_heads, hd = c->head_dim;
   const int hq = H * hd, F = c->d_ffn, V = c->vocab;
   int rc;
-  embed_kernel<T><<<M, 256, 0, s>>>(static_cast<const T*>(w->embed), block_ids, d, W.x);
-  LAUNCH_CHECK();
   for (int l = 0; l < c->n_layers; ++l) {
     const dflash_layer_weights& L = w->layers[l];
     const Probe& pr = l == 0 ? P0 : PN;
-    // attention sublayer
-    if ((rc = pre_sublayer<T>(c, L, 0, L.g_attn, M, W, s))) return rc;
+    // attention sublayer (layer 0: the block's embedding rows are gathered by the same pass)
+    if ((rc = pre_sublayer<T>(c, L, 0, L.g_attn, M, W, s, l == 0 ? static_cast<const T*>(w->embed) : nullptr,
+                              l == 0 ? block_ids : nullptr)))
+      return rc;
     EpiQKV<T> eq{static_cast<const T*>(L.w_q), static_cast<const T*>(L.w_k), static_cast<const T*>(L.w_v),
                  d, H, Hkv, hd, std::log(static_cast<double>(c->rope_theta)), ctx_len, W.q, W.kb, W.vbt};
     pr.begin(DFLASH_PROBE_QKV);
@@ -454,7 +454,7 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
     sw.K = d;
     EpiStore<T> e{sw, W.z, 2 * PD, STORE};
     GEMM_CHECK((run_gemm<T, T>(static_cast<const T*>(w->embed), d, W.tokens, B * Tn, d, 2 * PD / 16, e, s,
-                               W.scratch, W.scratch_bytes)));
+                               W.scratch, W.scratch_bytes, c->vocab)));
   }
   if (c->use_gate) {
     EpiStore<T> e{seg1<T>(w->ps_gate, PD, d), W.gamma, PD, SIGMOID};

@@ -1,42 +1,45 @@
-// Row-wise kernels of the drafter: embedding gather, RMSNorm, the dynamic short
-// conv's apply step.  One work-group per row; fixed-order reductions.
+// Row-wise kernels of the drafter: RMSNorm (optionally gathering the embedding rows
+// first), the dynamic short conv's apply step.  One work-group per row; fixed-order reductions.
 #pragma once
 
 #include "common.h"
 
 namespace dflash {
 
-// x[m] = E[ids[m]] widened to fp32.
-template <typename T>
-__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E, const int32_t* __restrict__ ids, int d,
-                                                    float* __restrict__ x) {
-  const int m = blockIdx.x;
-  const T* e = E + static_cast<size_t>(ids[m]) * d;
-  for (int k = threadIdx.x; k < d; k += blockDim.x) x[static_cast<size_t>(m) * d + k] = to_f<T>(e[k]);
-}
-
 // u = x / sqrt(mean(x^2) + eps) * g.  Writes u rounded to T (out_t) and/or in fp32 (out_f).
 // One work-group per row; each thread owns 4-float groups c = tid, tid + 256, ... and issues
 // all of its row loads before reducing (d <= 256 * 4 * 16 per row in one pass of registers).
+// With emb != nullptr the row is first gathered: x[m] = E[ids[m]] widened to fp32 (and
+// stored to x), then normalised -- the embedding step and the first norm in one pass.
 template <typename T>
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ x, const T* __restrict__ g, int d,
-                                                      float eps, T* __restrict__ out_t, float* __restrict__ out_f) {
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, const T* __restrict__ g, int d,
+                                                      float eps, T* __restrict__ out_t, float* __restrict__ out_f,
+                                                      const T* __restrict__ emb = nullptr,
+                                                      const int32_t* __restrict__ ids = nullptr) {
   constexpr int MAXV = 16;
   __shared__ float red[8];
   const int m = blockIdx.x;
-  const f32x4_t* xr = reinterpret_cast<const f32x4_t*>(x + static_cast<size_t>(m) * d);
+  f32x4_t* const xw = reinterpret_cast<f32x4_t*>(x + static_cast<size_t>(m) * d);
+  const f32x4_t* xr = xw;
+  const T* er = emb ? emb + static_cast<size_t>(ids[m]) * d : nullptr;
+  auto src = [&](int c) {
+    if (!er) return xr[c];
+    const f32x4_t t{to_f<T>(er[4 * c]), to_f<T>(er[4 * c + 1]), to_f<T>(er[4 * c + 2]), to_f<T>(er[4 * c + 3])};
+    xw[c] = t;
+    return t;
+  };
   const int nv = d >> 2;
   f32x4_t v[MAXV];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int c = threadIdx.x + 256 * i;
-    v[i] = c < nv ? xr[c] : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    v[i] = c < nv ? src(c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
   for (int c = threadIdx.x + 256 * MAXV; c < nv; c += 256) {
-    const f32x4_t t = xr[c];
+    const f32x4_t t = src(c);
     ss += t[0] * t[0] + t[1] * t[1] + t[2] * t[2] + t[3] * t[3];
   }
   ss = block_sum(ss, red);

@@ -562,8 +562,8 @@ inline int splitk_plan(int M, int K, int n_vtiles) {
 
 // Pipelined-GEMM plan (bf16 operands, A in bf16, M > 16): tile shape, LDS ring depth and split-K
 // factor, from measurements on MI355X.
-//  * M <= 64 (weight streaming): 64 x 128 tiles, 3 slots; K split until the grid has
-//    >= 128 work-groups.
+//  * M <= 64 (weight streaming), or grids of fewer than 32 tiles of 128 x 128: 64 x 128
+//    tiles, 3 slots; K split until the grid has >= 128 work-groups.
 //  * M >= 384 with >= 256 tiles of 256 x 128: those tiles, 3 slots (each weight tile is
 //    read by fewer work-groups).
 //  * otherwise 128 x 128 tiles, 2 slots (two work-groups per compute unit); when there are
@@ -580,13 +580,13 @@ inline BigPlan big_plan(int M, int K, int n_vtiles) {
     while (ks < 8 && tiles * ks < want && (K / 64) % (2 * ks) == 0 && K / 64 / (2 * ks) >= min_slabs) ks *= 2;
     return ks;
   };
-  if (M <= 64) {
-    const long tiles = (N + 127) / 128;
+  const long t128 = static_cast<long>((M + 127) / 128) * ((N + 127) / 128);
+  if (M <= 64 || t128 < 32) {
+    const long tiles = static_cast<long>((M + 63) / 64) * ((N + 127) / 128);
     return {64, 128, 3, split(tiles, 128, 4)};
   }
   const long t256 = static_cast<long>((M + 255) / 256) * ((N + 127) / 128);
   if (M >= 384 && t256 >= 256) return {256, 128, 3, 1};
-  const long t128 = static_cast<long>((M + 127) / 128) * ((N + 127) / 128);
   return {128, 128, 2, t128 >= 256 ? 1 : split(t128, 512, 16)};
 }
 
@@ -670,11 +670,13 @@ static hipError_t launch_big(const T* A, int lda, const int32_t* arows, int M, i
 // K: multiple of 64.  scratch: split-K partials (>= splitk_scratch_bytes, or nullptr: no split).
 template <typename T, typename AS, class Epi>
 static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
-                           hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0) {
+                           hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0, size_t a_rows = 0) {
   if (M <= 0 || n_vtiles <= 0) return hipSuccess;
   if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value) {
-    // gemm_pipe addresses A with 32-bit byte offsets: contiguous rows only, < 2 GiB
-    if (M > 16 && K % 64 == 0 && !arows && static_cast<size_t>(M) * lda * sizeof(T) < (size_t{1} << 31))
+    // gemm_pipe addresses A with 32-bit byte offsets: the rows A spans (M, or the a_rows of
+    // the table that arows gathers from) must fit in 2 GiB
+    const size_t span = arows ? a_rows : static_cast<size_t>(M);
+    if (M > 16 && K % 64 == 0 && span > 0 && span * lda * sizeof(T) < (size_t{1} << 31))
       return launch_big<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
   }
   if (M <= 16) return launch_skinny<T, AS, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
