@@ -9,13 +9,13 @@
 // so the epilogue can combine them without another pass.
 //
 // Three kernels:
-//  * gemm_skinny : M <= 16 (one drafted block), and M <= 64 when gemm_pipe does not
-//    apply (fp32).  Weight
+//  * gemm_skinny : M <= 16 (one drafted block) up to K < 16384, and M <= 64 when
+//    gemm_pipe does not apply (fp32).  Weight
 //    streaming: each work-group owns NT virtual tiles over the whole K; its NW
 //    waves split K, stream their slice of W straight from HBM into registers
 //    (16 B per lane per fragment, two register stages in flight) and reduce
 //    through LDS in a fixed order.
-//  * gemm_pipe   : bf16 operands (A in bf16), M > 16.  64/128/256 x 128 output tiles per
+//  * gemm_pipe   : bf16 operands (A in bf16), M > 16 (and M <= 16 with K >= 16384).  64/128/256 x 128 output tiles per
 //    work-group of 2x2 waves; 64-wide K slabs stream from memory straight into a ring
 //    of LDS slots with several slabs in flight; tile shape and split-K per GEMM shape.
 //  * gemm_tiled  : M > 64 when gemm_pipe does not apply (fp32, or A given in fp32).
@@ -563,7 +563,7 @@ inline int splitk_plan(int M, int K, int n_vtiles) {
 // Pipelined-GEMM plan (bf16 operands, A in bf16, M > 16): tile shape, LDS ring depth and split-K
 // factor, from measurements on MI355X.
 //  * M <= 64 (weight streaming), or grids of fewer than 32 tiles of 128 x 128: 64 x 128
-//    tiles, 3 slots; K split until the grid has >= 128 work-groups.
+//    tiles, 3 slots; K split until the grid has >= 128 work-groups (>= 256 at M <= 16).
 //  * M >= 384 with >= 256 tiles of 256 x 128: those tiles, 3 slots (each weight tile is
 //    read by fewer work-groups).
 //  * otherwise 128 x 128 tiles, 2 slots (two work-groups per compute unit); when there are
@@ -583,7 +583,7 @@ inline BigPlan big_plan(int M, int K, int n_vtiles) {
   const long t128 = static_cast<long>((M + 127) / 128) * ((N + 127) / 128);
   if (M <= 64 || t128 < 32) {
     const long tiles = static_cast<long>((M + 63) / 64) * ((N + 127) / 128);
-    return {64, 128, 3, split(tiles, 128, 4)};
+    return {64, 128, 3, split(tiles, M <= 16 ? 256 : 128, 4)};
   }
   const long t256 = static_cast<long>((M + 255) / 256) * ((N + 127) / 128);
   if (M >= 384 && t256 >= 256) return {256, 128, 3, 1};
@@ -676,7 +676,9 @@ static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, in
     // gemm_pipe addresses A with 32-bit byte offsets: the rows A spans (M, or the a_rows of
     // the table that arows gathers from) must fit in 2 GiB
     const size_t span = arows ? a_rows : static_cast<size_t>(M);
-    if (M > 16 && K % 64 == 0 && span > 0 && span * lda * sizeof(T) < (size_t{1} << 31))
+    // (at M <= 16 only for long K, where its split-K streams the weights faster than
+    // gemm_skinny: 16 x 4096 x 20480 cold, 44 -> 39 us)
+    if ((M > 16 || K >= 16384) && K % 64 == 0 && span > 0 && span * lda * sizeof(T) < (size_t{1} << 31))
       return launch_big<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
   }
   if (M <= 16) return launch_skinny<T, AS, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
