@@ -37,7 +37,7 @@ PROBES = ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc",
 N_PROBES = len(PROBES)
 
 EXPORTED = (
-    "dflash_inject_context", "dflash_draft_block", "dflash_select_path", "dflash_verify",
+    "dflash_inject_context", "dflash_draft_block", "dflash_select_path", "dflash_verify", "dflash_advance",
     "dflash_inject_workspace_bytes", "dflash_draft_workspace_bytes", "dflash_path_workspace_bytes",
     "dflash_verify_workspace_bytes", "dflash_check_config", "dflash_status_string",
 )
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
             "dflash_select_path": ([cfgp, wp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, PC, _vp],
                                    ctypes.c_int),
             "dflash_verify": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
+            "dflash_advance": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
             "dflash_inject_workspace_bytes": ([cfgp, _i32], PC),
             "dflash_draft_workspace_bytes": ([cfgp, _i32, _i32], PC),
             "dflash_path_workspace_bytes": ([cfgp, _i32], PC),
@@ -167,6 +168,12 @@ def dflash_path_workspace_bytes(cfg: dflash_config, batch: int) -> int:
 
 def dflash_verify_workspace_bytes(batch: int, n_draft: int, vocab: int) -> int:
     return lib().dflash_verify_workspace_bytes(batch, n_draft, vocab)
+
+
+def dflash_advance(accept_len, bonus, batch, mask_id, cap, ctx_len, pos0, n_new, block_ids, stream=None) -> None:
+    _check("dflash_advance", lib().dflash_advance(
+        _ptr(accept_len), _ptr(bonus), batch, mask_id, cap, _ptr(ctx_len), _ptr(pos0), _ptr(n_new), _ptr(block_ids),
+        _stream(stream)))
 
 
 def _probes(p):

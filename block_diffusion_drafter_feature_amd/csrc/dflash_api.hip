@@ -602,4 +602,14 @@ int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtyp
   return DFLASH_OK;
 }
 
+int dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batch, int32_t mask_id, int32_t cap,
+                   int32_t* ctx_len, int32_t* pos0, int32_t* n_new, int32_t* block_ids, hipStream_t stream) {
+  if (batch <= 0 || cap <= 0 || !accept_len || !bonus || !ctx_len || !pos0 || !n_new || !block_ids)
+    return DFLASH_E_INVAL;
+  advance_kernel<<<(batch + 63) / 64, 64, 0, stream>>>(accept_len, bonus, batch, mask_id, cap, ctx_len, pos0, n_new,
+                                                       block_ids);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
 }  // extern "C"

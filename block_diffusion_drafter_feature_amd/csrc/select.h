@@ -325,6 +325,27 @@ __global__ __launch_bounds__(64) void accept_kernel(const float* __restrict__ pv
   }
 }
 
+// Next cycle's state from a verified block (one thread per sequence): the anchor and the
+// a accepted drafts become the next a + 1 context rows, the bonus token the next anchor.
+__global__ __launch_bounds__(64) void advance_kernel(const int32_t* __restrict__ accept_len,
+                                                     const int32_t* __restrict__ bonus, int B, int mask_id, int cap,
+                                                     int32_t* __restrict__ ctx_len, int32_t* __restrict__ pos0,
+                                                     int32_t* __restrict__ n_new, int32_t* __restrict__ block_ids) {
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= B) return;
+  int a = accept_len[b];
+  a = a < 0 ? 0 : (a > 15 ? 15 : a);
+  int L = ctx_len[b];
+  L = L < 0 ? 0 : (L > cap ? cap : L);
+  pos0[b] = L;
+  n_new[b] = a + 1;
+  ctx_len[b] = L + a + 1 > cap ? cap : L + a + 1;
+  int32_t* ids = block_ids + static_cast<size_t>(b) * 16;
+  ids[0] = bonus[b];
+#pragma unroll
+  for (int j = 1; j < 16; ++j) ids[j] = mask_id;
+}
+
 // ------------------------------------------------------------------ Path Selector
 
 // Tokens whose 256-d embeddings are needed, per sequence: the 16 candidates of each

@@ -239,6 +239,31 @@ int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtyp
                   int32_t n_draft, int32_t vocab, int32_t* accept_len, int32_t* bonus,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Advance the drafting cycle on the device ("DFlash 2 ...", "Flujo de Inferencia con
+ * DFlash 2": the verified prefix plus the bonus token are emitted and drafting resumes
+ * from them; "DFlash ...", section 2.2: the target's hidden states of the tokens it has
+ * processed become new context rows).
+ *
+ * For a block drafted with an anchor (n_fixed = 1) at position ctx_len[b] and verified
+ * with accept_len[b] = a, the target has processed the anchor and the a accepted drafts
+ * (positions ctx_len[b] .. ctx_len[b] + a); their hidden states are the next rows to
+ * inject, and the bonus token anchors the next block.  Per sequence b:
+ *   pos0[b]      = ctx_len[b]
+ *   n_new[b]     = a + 1
+ *   ctx_len[b]  += a + 1                          (saturating at cap)
+ *   block_ids[b] = [bonus[b], mask_id x 15]
+ * so the next dflash_inject_context (pos0, n_new) and dflash_draft_block (ctx_len,
+ * block_ids) read everything from device memory, with no host synchronisation.
+ *
+ * accept_len, bonus : device int32 [batch] (dflash_verify's outputs); a is clamped to 0..15.
+ * ctx_len           : device int32 [batch], updated in place (clamped to 0..cap first).
+ * pos0, n_new       : device int32 [batch], written.
+ * block_ids         : device int32 [batch, 16], written.
+ * Returns DFLASH_E_INVAL for NULL pointers, batch <= 0 or cap <= 0.  No workspace.
+ */
+int dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batch, int32_t mask_id, int32_t cap,
+                   int32_t* ctx_len, int32_t* pos0, int32_t* n_new, int32_t* block_ids, hipStream_t stream);
+
 /* Workspace sizes in bytes (0 when the arguments are invalid). */
 size_t dflash_inject_workspace_bytes(const dflash_config* cfg, int32_t n_rows);
 size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t cap);

@@ -47,7 +47,7 @@ __all__ = [
     "bf16_round", "decode", "Model", "rmsnorm", "rope", "silu", "sigmoid",
     "inject_rows", "short_conv", "block_attention", "draft_block", "topk",
     "path_pair_scores", "select_path", "verify", "conv_param_count",
-    "path_selector_param_count", "drafting_step",
+    "path_selector_param_count", "drafting_step", "advance", "drafting_cycles",
 ]
 
 
@@ -486,3 +486,57 @@ def drafting_step(m: Model, k_cache: List[np.ndarray], v_cache: List[np.ndarray]
     a, bonus = verify(path_ids, target_logits)
     return {"cand_ids": ids, "cand_logits": vals, "xhat": out["xhat"], "logits": out["logits"],
             "pair_scores": S, "path_idx": idx, "path_ids": path_ids, "accept_len": a, "bonus": bonus}
+
+
+# --------------------------------------------------------------------------------------
+# the drafting cycle (draft -> verify -> inject)
+# --------------------------------------------------------------------------------------
+
+def advance(accept_len: int, bonus: int, ctx_len: int, mask_id: int, cap: int, block: int = 16):
+    """State of the next cycle after a block drafted with an anchor at position ctx_len was
+    verified ("DFlash 2 ...", inference flow: the accepted prefix and the bonus token are
+    emitted and drafting resumes from them; "DFlash ...", section 2.2: the target's hidden
+    states of the tokens it processed become new context rows).  The target processed the
+    anchor and the a accepted drafts, positions ctx_len .. ctx_len + a: those a + 1 rows are
+    injected next, and the bonus token anchors the next block.  a is clamped to
+    0 .. block - 1 and ctx_len to 0 .. cap; the new ctx_len saturates at cap."""
+    a = min(max(int(accept_len), 0), block - 1)
+    L = min(max(int(ctx_len), 0), cap)
+    ids = np.full(block, mask_id, dtype=np.int32)
+    ids[0] = bonus
+    return {"pos0": L, "n_new": a + 1, "ctx_len": min(L + a + 1, cap), "block_ids": ids}
+
+
+def drafting_cycles(m: Model, k_cache: List[np.ndarray], v_cache: List[np.ndarray], ctx_len: int, cap: int,
+                    pos0: int, n_new: int, block_ids: np.ndarray, hidden_fn, logits_fn, cycles: int,
+                    mode: str = "greedy"):
+    """``cycles`` drafting cycles of one sequence.  Each cycle injects n_new rows at pos0
+    (``hidden_fn(c, n)`` gives the target's hidden states of those rows, stored values as
+    for ``inject_rows``; rows at positions >= cap are dropped), drafts the block anchored by block_ids[0], chooses the path,
+    verifies it against ``logits_fn(c, path_ids)`` (the target's logits for the block),
+    emits the accepted drafts and the bonus token, and advances.  k_cache/v_cache are
+    updated in place.  Returns one dict per cycle."""
+    D = m.dims
+    out = []
+    for c in range(cycles):
+        pos = pos0 + np.arange(n_new)
+        keep = pos < cap
+        if keep.any():
+            rows = np.asarray(hidden_fn(c, n_new))[keep]
+            _, K, V = inject_rows(m, rows, pos[keep])
+            for l in range(D.n_layers):
+                k_cache[l][:, pos[keep]] = np.transpose(K[l], (1, 0, 2))
+                v_cache[l][:, pos[keep]] = np.transpose(V[l], (1, 0, 2))
+        d = draft_block(m, k_cache, v_cache, min(ctx_len, cap), block_ids)
+        ids, vals = topk(d["logits"], D.topk)
+        S = path_pair_scores(m, ids, d["xhat"], block_ids, 1)
+        idx, _ = select_path(vals[1:], S, True, mode)
+        path_ids = ids[np.arange(1, D.block), idx]
+        T = logits_fn(c, path_ids)
+        a, bonus = verify(path_ids, T)
+        nxt = advance(a, bonus, ctx_len, D.mask_id, cap, D.block)
+        out.append({"cand_ids": ids, "logits": d["logits"], "path_ids": path_ids, "target_logits": T,
+                    "accept_len": a, "bonus": bonus, "emitted": list(path_ids[:a]) + [bonus],
+                    "ctx_len": ctx_len, "pos0": pos0, "n_new": n_new, "next": nxt})
+        ctx_len, pos0, n_new, block_ids = nxt["ctx_len"], nxt["pos0"], nxt["n_new"], nxt["block_ids"]
+    return out

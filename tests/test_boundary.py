@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 10
+    assert len(names) == 11
     lib = ctypes.CDLL(D.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -119,3 +119,12 @@ def test_calls_validate_before_launch():
     assert _status(D.dflash_verify, FAKE, FAKE, 9, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_INVAL
     assert _status(D.dflash_verify, FAKE, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v - 1, S) == D.DFLASH_E_WORKSPACE
     assert _status(D.dflash_verify, None, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_INVAL
+
+
+def test_advance_rejects_bad_arguments():
+    lib = D.lib()
+    f = FAKE
+    assert lib.dflash_advance(None, f, 1, 0, 64, f, f, f, f, None) == D.DFLASH_E_INVAL
+    assert lib.dflash_advance(f, f, 0, 0, 64, f, f, f, f, None) == D.DFLASH_E_INVAL
+    assert lib.dflash_advance(f, f, 1, 0, 0, f, f, f, f, None) == D.DFLASH_E_INVAL
+    assert lib.dflash_advance(f, f, 1, 0, 64, f, f, None, f, None) == D.DFLASH_E_INVAL
