@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 to skip)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel breakdown pass")
+    ap.add_argument("--cycles", type=int, default=32,
+                    help="also time this many full drafting cycles (inject the accepted rows with counts read "
+                         "on the device, draft, path, verify, advance) and report tau and tokens/s")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the step, run a plain fp32 elementwise copy (torch.neg) of this many MiB "
                          "three times: a kernel of known traffic that calibrates HBM byte counters")
@@ -131,6 +134,93 @@ def cpu_baseline(wl, W, seconds):
 
 
 # ------------------------------------------------------------------ main
+
+def run_cycles(n, D, torch, np, synth, wl, dr, new_hid, row_off, tdt, log):
+    """Full drafting cycles with the state on the device: inject n_new rows (the anchor and
+    the accepted drafts of the previous cycle) at pos0, draft, choose the path, verify,
+    advance, for every sequence of the workload, starting from its context lengths.  The
+    cache is a second one with room for the growth (seeded noise of the injected rows'
+    scale), so the timed step above keeps its own layout.  The target side is synthetic:
+    its hidden rows are a fixed seeded buffer and its logits N(0,1) with +8 planted on the
+    first A drafts and on another token at row A, A uniform in 0..15 per sequence and cycle
+    (tau = 1 + E[A] = 8.5 by construction), planted by device tensor ops inside the timed
+    loop.  Returns tau (mean emitted tokens per cycle) and tokens/s."""
+    dims = wl.dims
+    B, V = wl.batch, dims.vocab
+    ctx = np.asarray(wl.ctx_lens, dtype=np.int32)
+    warm = 3
+    cap = ((int(ctx.max()) + 16 * (n + warm + 1) + 31) // 32) * 32
+    dt_t = D.torch_dtype(dims)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wl.seed + 4242)
+    cache = D.KVCache(dims, B, cap, fill=None)
+    scale = 0.02 * dims.d ** 0.5
+    for l in range(dims.n_layers):
+        for t in (cache.k[l], cache.vt[l]):
+            t.copy_((torch.randn(t.shape, generator=g, device="cuda", dtype=torch.float32) * scale).to(dt_t))
+    T0 = torch.randn((B, 16, V), generator=g, device="cuda", dtype=torch.float32).to(dt_t)
+    T = torch.empty_like(T0)
+    i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()  # noqa: E731
+    ctx_t = i32(ctx)
+    pos0_t = i32(np.maximum(ctx - 16, 0))
+    nnew_t = i32(np.minimum(ctx, 16))
+    ids_t = i32(synth.make_block_ids(dims, B, wl.seed + 99, 1))
+    ci = torch.zeros((B, 16, 16), dtype=torch.int32, device="cuda")
+    cl = torch.zeros((B, 16, 16), dtype=torch.float32, device="cuda")
+    fh = torch.zeros((B, 16, dims.d), dtype=torch.float32, device="cuda")
+    pidx = torch.zeros((B, 15), dtype=torch.int32, device="cuda")
+    pids = torch.zeros((B, 15), dtype=torch.int32, device="cuda")
+    acc = torch.zeros(B, dtype=torch.int32, device="cuda")
+    bon = torch.zeros(B, dtype=torch.int32, device="cuda")
+    emitted = torch.zeros(B, dtype=torch.int64, device="cuda")
+    rows = torch.arange(16, device="cuda")
+    pad = torch.zeros((B, 1), dtype=torch.long, device="cuda")
+    nb = {k: f for k, f in (("i", D.dflash_inject_workspace_bytes(dr.cfg, 16 * B)),
+                            ("d", D.dflash_draft_workspace_bytes(dr.cfg, B, cap)),
+                            ("p", D.dflash_path_workspace_bytes(dr.cfg, B)),
+                            ("v", D.dflash_verify_workspace_bytes(B, 15, V)))}
+    ws = {k: torch.empty(max(v, 256), dtype=torch.uint8, device="cuda") for k, v in nb.items()}
+
+    def cycle():
+        D.dflash_inject_context(dr.cfg, dr.w, cache.kv, new_hid, 16 * B, row_off, pos0_t, nnew_t, B,
+                                ws["i"], nb["i"])
+        D.dflash_draft_block(dr.cfg, dr.w, cache.kv, ctx_t, ids_t, B, ci, cl, fh, None, ws["d"], nb["d"])
+        D.dflash_select_path(dr.cfg, dr.w, ci, cl, fh, ids_t, 1, D.DFLASH_PATH_GREEDY, B, pidx, pids, None,
+                             ws["p"], nb["p"])
+        # synthetic target: the first A drafts are its greedy tokens, row A holds another
+        A = torch.randint(0, 16, (B, 1), generator=g, device="cuda")
+        tok = torch.cat([pids.long(), pad], 1)
+        other = (tok + 1 + torch.randint(0, V - 2, (B, 16), generator=g, device="cuda")) % (V - 1)
+        T.copy_(T0)
+        T.scatter_(2, torch.where(rows[None, :] < A, tok, other)[:, :, None], 8.0)
+        D.dflash_verify(pids, T, tdt, B, 15, V, acc, bon, ws["v"], nb["v"])
+        D.dflash_advance(acc, bon, B, dims.mask_id, cap, ctx_t, pos0_t, nnew_t, ids_t)
+        emitted.add_(acc.long() + 1)
+
+    for _ in range(warm):
+        cycle()
+    torch.cuda.synchronize()
+    emitted.zero_()
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(n):
+        cycle()
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / n
+    tot = int(emitted.sum())
+    tau = tot / (n * B)
+    ctx_end = ctx_t.cpu().numpy()
+    assert (ctx_end <= cap - 16).all(), "cycle cache overflow"
+    tps = tot / (ms * n) * 1e3
+    log(f"[bench] {n} cycles: {ms:.3f} ms/cycle, tau {tau:.2f}, {tps:.0f} tokens/s, "
+        f"contexts now {ctx_end.min()}..{ctx_end.max()}")
+    del cache
+    return {"cycles": n, "ms_per_cycle": round(ms, 4), "tau": round(tau, 3), "tokens_per_s": round(tps, 1),
+            "target": "synthetic: fixed seeded target hidden rows; target logits N(0,1) with +8 on the first A "
+                      "drafts and on another token at row A, A ~ U{0..15} per sequence and cycle (tau = 8.5 "
+                      "expected); planting by device tensor ops inside the timed loop"}
+
 
 def main():
     args = parse()
@@ -286,6 +376,10 @@ def main():
         for n in ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv"):
             breakdown[n] = roof(n, avg_ms(pr, n)) if n != "topk" else {"ms": round(avg_ms(pr, n), 4)}
 
+    cycle = None
+    if args.cycles > 0:
+        cycle = run_cycles(args.cycles, D, torch, np, synth, wl, dr, new_hid, row_off, tdt, log)
+
     if args.copy_mib > 0:
         n = args.copy_mib * (1 << 20) // 4
         src = torch.randn(n, device="cuda", dtype=torch.float32)
@@ -321,6 +415,8 @@ def main():
         "breakdown": breakdown,
         "cpu_baseline": cpu,
     }
+    if cycle is not None:
+        out["cycle"] = cycle
     print(json.dumps(out), flush=True)
 
 
