@@ -48,6 +48,7 @@ __all__ = [
     "inject_rows", "short_conv", "block_attention", "draft_block", "topk",
     "path_pair_scores", "select_path", "verify", "conv_param_count",
     "path_selector_param_count", "drafting_step", "advance", "drafting_cycles",
+    "sample_path", "verify_sampled",
 ]
 
 
@@ -424,6 +425,56 @@ def select_path(cand_logits: np.ndarray, S: np.ndarray, has_anchor: bool, mode: 
     raise ValueError(mode)
 
 
+def sample_path(cand_logits: np.ndarray, S: np.ndarray, has_anchor: bool, temperature: float,
+                uniforms: np.ndarray):
+    """Draw one candidate per drafted position from the precomputed scores.
+
+    [DFlash2] item 1 names sampling over the precomputed scores as the alternative to the
+    greedy walk.  Reading: left to right, the candidate at position p is drawn from the
+    softmax, at the given temperature, of the very scores the greedy walk maximises
+    (drafter logit plus compatibility with the candidate drawn at p - 1; the anchor, or
+    nothing, at p = 0).  Each draw inverts the cumulative distribution in candidate-index
+    order with the uniform ``uniforms[p]`` in [0, 1): the first j whose cumulative
+    probability exceeds u (the last candidate of non-zero probability if rounding leaves
+    u above the total).
+
+    cand_logits: [P, K]; S: [P, K, K] as from ``path_pair_scores``; temperature > 0.
+    Returns (indices [P] int32, q [P, K]) where q[p] is the distribution position p was
+    drawn from: the proposal distribution that rejection sampling divides by.
+    """
+    lg = np.asarray(cand_logits, dtype=np.float64)
+    P, K = lg.shape
+    t = float(temperature)
+    if not t > 0:
+        raise ValueError("temperature must be positive")
+    idx = np.zeros(P, dtype=np.int32)
+    q = np.zeros((P, K))
+    prev = None
+    for p in range(P):
+        if p == 0:
+            sc = lg[0] + (S[0, 0] if has_anchor else 0.0)
+        else:
+            sc = lg[p] + S[p, prev]
+        w = np.exp((sc - sc.max()) / t)
+        q[p] = w / w.sum()
+        idx[p] = _inverse_cdf(q[p], float(uniforms[p]))
+        prev = idx[p]
+    return idx, q
+
+
+def _inverse_cdf(w: np.ndarray, u: float) -> int:
+    """First index whose running sum of the non-negative weights ``w`` exceeds u * sum(w);
+    the last index of positive weight if none does (rounding at the top end)."""
+    w = np.asarray(w, dtype=np.float64)
+    target = u * w.sum()
+    run = 0.0
+    for i, wi in enumerate(w):
+        run += wi
+        if target < run:
+            return i
+    return int(np.flatnonzero(w > 0)[-1])
+
+
 # ----------------------------------------------------------------------------------
 # (a11) greedy verification
 # ----------------------------------------------------------------------------------
@@ -450,6 +501,55 @@ def verify(draft: np.ndarray, target_logits: np.ndarray):
             break
         a += 1
     return a, _argmax_lowest(target_logits[a])
+
+
+def verify_sampled(draft: np.ndarray, q_ids: np.ndarray, q_probs: np.ndarray, target_logits: np.ndarray,
+                   temperature: float, u_accept: np.ndarray, u_bonus: float):
+    """Verification by rejection sampling, which keeps the target's distribution exactly.
+
+    [DFlash2] item 1: besides the greedy walk, the block can be chosen so that rejection
+    sampling restores the target model's exact distribution; [FlexDraft] problem
+    statement: the bonus token is drawn at the first rejection.  Reading (speculative
+    sampling in its standard form): the target's distribution at row i is
+    p_i = softmax(target_logits[i] / temperature); draft token x_i was drawn from the
+    proposal q_i, given sparsely by (q_ids[i], q_probs[i]) (q_i(x) = 0 for ids not listed).
+    Draft i is accepted with probability min(1, p_i(x_i) / q_i(x_i)), decided as
+    u_accept[i] * q_i(x_i) < p_i(x_i) (a draft with q_i(x_i) = 0 is rejected).  At the first
+    rejection a the bonus token is drawn from the residual max(0, p_a - q_a), normalised;
+    if every draft is accepted (a = P) it is drawn from p_P.  The draw inverts the
+    cumulative distribution in ascending token id with u_bonus.  If the residual has no
+    positive mass (possible only through rounding) the bonus is drawn from p_a.
+
+    draft: [P]; q_ids, q_probs: [P, K]; target_logits: [P+1, V]; u_accept: [P]; u_bonus
+    scalar, uniforms in [0, 1).  Returns (accepted length a, bonus token).
+    """
+    t = float(temperature)
+    if not t > 0:
+        raise ValueError("temperature must be positive")
+    T = np.asarray(target_logits, dtype=np.float64)
+    P = len(draft)
+
+    def probs(row):
+        z = (T[row] - T[row].max()) / t
+        w = np.exp(z)
+        return w / w.sum()
+
+    a = 0
+    while a < P:
+        x = int(draft[a])
+        hit = np.flatnonzero(np.asarray(q_ids[a]) == x)
+        q = float(q_probs[a][hit[0]]) if len(hit) else 0.0
+        if not (q > 0.0 and float(u_accept[a]) * q < probs(a)[x]):
+            break
+        a += 1
+    p = probs(a)
+    r = p.copy()
+    if a < P:
+        ids = np.asarray(q_ids[a])
+        r[ids] = np.maximum(0.0, p[ids] - np.asarray(q_probs[a], dtype=np.float64))
+    if not r.sum() > 0.0:
+        r = p
+    return a, _inverse_cdf(r, float(u_bonus))
 
 
 def _argmax_lowest(row: np.ndarray, exclude: Optional[np.ndarray] = None) -> int:
