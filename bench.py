@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--cycles", type=int, default=32,
                     help="also time this many full drafting cycles (inject the accepted rows with counts read "
                          "on the device, draft, path, verify, advance) and report tau and tokens/s")
+    ap.add_argument("--sampled-steps", type=int, default=20,
+                    help="also time this many steps of the sampling variant (sampled path choice and "
+                         "verification by rejection sampling, temperature 0.8) and report them apart")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the step, run a plain fp32 elementwise copy (torch.neg) of this many MiB "
                          "three times: a kernel of known traffic that calibrates HBM byte counters")
@@ -376,6 +379,41 @@ def main():
         for n in ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv"):
             breakdown[n] = roof(n, avg_ms(pr, n)) if n != "topk" else {"ms": round(avg_ms(pr, n), 4)}
 
+    sampled = None
+    if args.sampled_steps > 0:
+        temp = 0.8
+        rng = torch.Generator(device="cuda")
+        rng.manual_seed(wl.seed + 77)
+        u_path = torch.rand((B, 15), generator=rng, device="cuda")
+        u_acc = torch.rand((B, 15), generator=rng, device="cuda")
+        u_bon = torch.rand((B,), generator=rng, device="cuda")
+        pq = torch.zeros((B, 15, 16), dtype=torch.float32, device="cuda")
+        nb_s = D.dflash_verify_sampled_workspace_bytes(B, 15, dims.vocab)
+        ws_s = torch.empty(nb_s, dtype=torch.uint8, device="cuda")
+        cand_rows = ci[:, 1:].data_ptr()          # rows 1..15 of the draft call's candidates
+
+        def sampled_step():
+            D.dflash_inject_context(dr.cfg, dr.w, cache.kv, new_hid, 16 * B, row_off, pos0, n_new, B, ws_i, nb_i)
+            D.dflash_draft_block(dr.cfg, dr.w, cache.kv, ctx_t, ids_t, B, ci, cl, fh, None, ws_d, nb_d)
+            D.dflash_sample_path(dr.cfg, dr.w, ci, cl, fh, ids_t, 1, B, temp, u_path, pidx, pids, pq, None,
+                                 ws_p, nb_p)
+            D.dflash_verify_sampled(pids, cand_rows, 256, pq, T, tdt, B, 15, dims.vocab, temp, u_acc, u_bon, acc,
+                                    bon, ws_s, nb_s)
+
+        for _ in range(3):
+            sampled_step()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.sampled_steps):
+            sampled_step()
+        stop.record()
+        torch.cuda.synchronize()
+        ms_s = start.elapsed_time(stop) / args.sampled_steps
+        log(f"[bench] sampling variant: {ms_s:.3f} ms/step, {B * 1000.0 / ms_s:.1f} blocks/s")
+        sampled = {"steps": args.sampled_steps, "ms_per_step": round(ms_s, 4),
+                   "blocks_per_s": round(B * 1000.0 / ms_s, 2), "temperature": temp,
+                   "path": "sampled over the pair scores", "verify": "rejection sampling"}
+
     cycle = None
     if args.cycles > 0:
         cycle = run_cycles(args.cycles, D, torch, np, synth, wl, dr, new_hid, row_off, tdt, log)
@@ -415,6 +453,8 @@ def main():
         "breakdown": breakdown,
         "cpu_baseline": cpu,
     }
+    if sampled is not None:
+        out["sampled"] = sampled
     if cycle is not None:
         out["cycle"] = cycle
     print(json.dumps(out), flush=True)

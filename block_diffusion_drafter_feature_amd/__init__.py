@@ -38,8 +38,10 @@ N_PROBES = len(PROBES)
 
 EXPORTED = (
     "dflash_inject_context", "dflash_draft_block", "dflash_select_path", "dflash_verify", "dflash_advance",
+    "dflash_sample_path", "dflash_verify_sampled",
     "dflash_inject_workspace_bytes", "dflash_draft_workspace_bytes", "dflash_path_workspace_bytes",
-    "dflash_verify_workspace_bytes", "dflash_check_config", "dflash_status_string",
+    "dflash_verify_workspace_bytes", "dflash_verify_sampled_workspace_bytes", "dflash_check_config",
+    "dflash_status_string",
 )
 
 
@@ -106,6 +108,11 @@ def lib() -> ctypes.CDLL:
                                    ctypes.c_int),
             "dflash_verify": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
             "dflash_advance": ([_vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp], ctypes.c_int),
+            "dflash_sample_path": ([cfgp, wp, _vp, _vp, _vp, _vp, _i32, _i32, ctypes.c_float, _vp, _vp, _vp, _vp,
+                                    _vp, _vp, PC, _vp], ctypes.c_int),
+            "dflash_verify_sampled": ([_vp, _vp, ctypes.c_int64, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                       _vp, _vp, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
+            "dflash_verify_sampled_workspace_bytes": ([_i32, _i32, _i32], PC),
             "dflash_inject_workspace_bytes": ([cfgp, _i32], PC),
             "dflash_draft_workspace_bytes": ([cfgp, _i32, _i32], PC),
             "dflash_path_workspace_bytes": ([cfgp, _i32], PC),
@@ -201,6 +208,28 @@ def dflash_select_path(cfg, w, cand_ids, cand_logits, final_hidden, block_ids, n
         ctypes.byref(cfg), ctypes.byref(w), _ptr(cand_ids), _ptr(cand_logits), _ptr(final_hidden), _ptr(block_ids),
         n_fixed, mode, batch, _ptr(path_idx), _ptr(path_ids), _ptr(pair_scores), _ptr(workspace), workspace_bytes,
         _stream(stream)))
+
+
+def dflash_sample_path(cfg, w, cand_ids, cand_logits, final_hidden, block_ids, n_fixed, batch, temperature,
+                       uniforms, path_idx, path_ids, path_q, pair_scores, workspace, workspace_bytes,
+                       stream=None) -> None:
+    _check("dflash_sample_path", lib().dflash_sample_path(
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(cand_ids), _ptr(cand_logits), _ptr(final_hidden), _ptr(block_ids),
+        n_fixed, batch, temperature, _ptr(uniforms), _ptr(path_idx), _ptr(path_ids), _ptr(path_q),
+        _ptr(pair_scores), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+def dflash_verify_sampled_workspace_bytes(batch: int, n_draft: int, vocab: int) -> int:
+    return lib().dflash_verify_sampled_workspace_bytes(batch, n_draft, vocab)
+
+
+def dflash_verify_sampled(draft, q_ids, q_ids_stride, q_probs, tgt_logits, tgt_dtype, batch, n_draft, vocab,
+                          temperature, u_accept, u_bonus, accept_len, bonus, workspace, workspace_bytes,
+                          stream=None) -> None:
+    _check("dflash_verify_sampled", lib().dflash_verify_sampled(
+        _ptr(draft), _ptr(q_ids), q_ids_stride, _ptr(q_probs), _ptr(tgt_logits), tgt_dtype, batch, n_draft, vocab,
+        temperature, _ptr(u_accept), _ptr(u_bonus), _ptr(accept_len), _ptr(bonus), _ptr(workspace),
+        workspace_bytes, _stream(stream)))
 
 
 def dflash_verify(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_len, bonus, workspace,

@@ -216,6 +216,27 @@ VerifyWs carve_verify(Carver& cv, int B, int n_draft, int V) {
   return w;
 }
 
+struct VerifySampledWs {
+  float* pm;
+  float* ps;
+  BonusSel* sel;
+};
+VerifySampledWs carve_verify_sampled(Carver& cv, int B, int n_draft, int V) {
+  VerifySampledWs w;
+  const size_t nch = (V + kSoftmaxChunk - 1) / kSoftmaxChunk;
+  w.pm = cv.take<float>(static_cast<size_t>(B) * (n_draft + 1) * nch);
+  w.ps = cv.take<float>(static_cast<size_t>(B) * (n_draft + 1) * nch);
+  w.sel = cv.take<BonusSel>(static_cast<size_t>(B));
+  return w;
+}
+
+// log2(e) / t, the exponent scale of a softmax at temperature t; 0 for an invalid t
+float temp_scale(float t) {
+  if (!(t > 0.f) || !std::isfinite(t)) return 0.f;
+  const double k = 1.4426950408889634 / static_cast<double>(t);
+  return std::isfinite(static_cast<float>(k)) ? static_cast<float>(k) : 0.f;
+}
+
 struct Probe {
   const dflash_probes* p;
   hipStream_t s;
@@ -437,7 +458,8 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
 template <typename T>
 int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* cand_ids, const float* cand_logits,
               const float* final_hidden, const int32_t* block_ids, int n_fixed, int mode, int B, int32_t* path_idx,
-              int32_t* path_ids, float* pair_scores, void* ws, hipStream_t s) {
+              int32_t* path_ids, float* pair_scores, void* ws, hipStream_t s, float k2 = 0.f,
+              const float* uniforms = nullptr, float* path_q = nullptr) {
   Carver cv(ws);
   PathWs W = carve_path<T>(cv, c, B);
   const int d = c->d_model, PD = c->ps_dim, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
@@ -466,7 +488,11 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
                                                       static_cast<const T*>(w->ps_u), static_cast<const T*>(w->ps_v),
                                                       PD, c->ps_rank, n_fixed, W.S, pair_scores);
   LAUNCH_CHECK();
-  path_walk_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, mode, path_idx, path_ids);
+  if (uniforms)
+    path_sample_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, k2, uniforms, path_idx, path_ids,
+                                        path_q);
+  else
+    path_walk_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, mode, path_idx, path_ids);
   LAUNCH_CHECK();
   return DFLASH_OK;
 }
@@ -598,6 +624,74 @@ int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtyp
                                                            kArgmaxChunk, W.pv, W.pi);
   LAUNCH_CHECK();
   accept_kernel<<<batch, 64, 0, stream>>>(W.pv, W.pi, nch, draft, n_draft, accept_len, bonus);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+int dflash_sample_path(const dflash_config* cfg, const dflash_weights* w, const int32_t* cand_ids,
+                       const float* cand_logits, const float* final_hidden, const int32_t* block_ids, int32_t n_fixed,
+                       int32_t batch, float temperature, const float* uniforms, int32_t* path_idx, int32_t* path_ids,
+                       float* path_q, float* pair_scores, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if ((rc = check_weights(cfg, w, false, false, true))) return rc;
+  if (batch <= 0 || (n_fixed != 0 && n_fixed != 1)) return DFLASH_E_INVAL;
+  const float k2 = temp_scale(temperature);
+  if (k2 == 0.f) return DFLASH_E_INVAL;
+  if (!cand_ids || !cand_logits || !block_ids || !uniforms || !path_idx || !path_ids || !path_q || !workspace)
+    return DFLASH_E_INVAL;
+  if (cfg->use_gate && !final_hidden) return DFLASH_E_INVAL;
+  if (workspace_bytes < dflash_path_workspace_bytes(cfg, batch)) return DFLASH_E_WORKSPACE;
+  if (cfg->dtype == DFLASH_BF16)
+    return path_impl<bf16_t>(cfg, w, cand_ids, cand_logits, final_hidden, block_ids, n_fixed, DFLASH_PATH_GREEDY,
+                             batch, path_idx, path_ids, pair_scores, workspace, stream, k2, uniforms, path_q);
+  return path_impl<float>(cfg, w, cand_ids, cand_logits, final_hidden, block_ids, n_fixed, DFLASH_PATH_GREEDY, batch,
+                          path_idx, path_ids, pair_scores, workspace, stream, k2, uniforms, path_q);
+}
+
+size_t dflash_verify_sampled_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab) {
+  if (batch <= 0 || n_draft < 0 || n_draft > 64 || vocab <= 0 || vocab > kSoftmaxChunk * 1024) return 0;
+  Carver cv(nullptr);
+  carve_verify_sampled(cv, batch, n_draft, vocab);
+  return cv.off;
+}
+
+int dflash_verify_sampled(const int32_t* draft, const int32_t* q_ids, int64_t q_ids_stride, const float* q_probs,
+                          const void* tgt_logits, int32_t tgt_dtype, int32_t batch, int32_t n_draft, int32_t vocab,
+                          float temperature, const float* u_accept, const float* u_bonus, int32_t* accept_len,
+                          int32_t* bonus, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (batch <= 0 || n_draft < 0 || vocab <= 0) return DFLASH_E_INVAL;
+  if (n_draft > 64 || vocab > kSoftmaxChunk * 1024) return DFLASH_E_UNSUPPORTED;
+  if (tgt_dtype != DFLASH_BF16 && tgt_dtype != DFLASH_F32) return DFLASH_E_INVAL;
+  const float k2 = temp_scale(temperature);
+  if (k2 == 0.f) return DFLASH_E_INVAL;
+  if (n_draft > 0 && (!draft || !q_ids || !q_probs || !u_accept || q_ids_stride < 16LL * n_draft))
+    return DFLASH_E_INVAL;
+  if (!tgt_logits || !u_bonus || !accept_len || !bonus || !workspace) return DFLASH_E_INVAL;
+  if (workspace_bytes < dflash_verify_sampled_workspace_bytes(batch, n_draft, vocab)) return DFLASH_E_WORKSPACE;
+  Carver cv(workspace);
+  VerifySampledWs W = carve_verify_sampled(cv, batch, n_draft, vocab);
+  const int nch = (vocab + kSoftmaxChunk - 1) / kSoftmaxChunk;
+  const dim3 grid(nch, batch * (n_draft + 1));
+  const long long qs = static_cast<long long>(q_ids_stride);
+  if (tgt_dtype == DFLASH_BF16) {
+    const bf16_t* T = static_cast<const bf16_t*>(tgt_logits);
+    softmax_partial_kernel<bf16_t><<<grid, 256, 0, stream>>>(T, vocab, k2, W.pm, W.ps);
+    LAUNCH_CHECK();
+    reject_kernel<bf16_t><<<batch, 64, 0, stream>>>(W.pm, W.ps, nch, T, vocab, k2, draft, n_draft, q_ids, qs, q_probs,
+                                                     u_accept, u_bonus, accept_len, W.sel);
+    LAUNCH_CHECK();
+    bonus_kernel<bf16_t><<<batch, 256, 0, stream>>>(T, vocab, k2, n_draft, q_ids, qs, q_probs, W.sel, bonus);
+  } else {
+    const float* T = static_cast<const float*>(tgt_logits);
+    softmax_partial_kernel<float><<<grid, 256, 0, stream>>>(T, vocab, k2, W.pm, W.ps);
+    LAUNCH_CHECK();
+    reject_kernel<float><<<batch, 64, 0, stream>>>(W.pm, W.ps, nch, T, vocab, k2, draft, n_draft, q_ids, qs, q_probs,
+                                                    u_accept, u_bonus, accept_len, W.sel);
+    LAUNCH_CHECK();
+    bonus_kernel<float><<<batch, 256, 0, stream>>>(T, vocab, k2, n_draft, q_ids, qs, q_probs, W.sel, bonus);
+  }
   LAUNCH_CHECK();
   return DFLASH_OK;
 }

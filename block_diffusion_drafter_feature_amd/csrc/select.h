@@ -325,6 +325,226 @@ __global__ __launch_bounds__(64) void accept_kernel(const float* __restrict__ pv
   }
 }
 
+// ------------------------------------------------------------------ verification by rejection sampling
+//
+// p_r = softmax(target row r / t) over the vocabulary; draft i (drawn from a proposal q_i
+// given sparsely by 16 ids and probabilities) is accepted when u_accept[i] * q_i(x_i) <
+// p_i(x_i); at the first rejection a the bonus is drawn from max(0, p_a - q_a) (from p_a
+// when every draft is accepted, or when rounding leaves that residual no mass), by
+// inverting its running sum in ascending token id with u_bonus.  Exponentials are
+// exp2((x - max) * k2), k2 = log2(e) / t, in fp32.
+
+constexpr int kSoftmaxChunk = 4096;   // vocabulary columns per work-group of the stages below
+
+// Stage 1: per (target row, column chunk) the chunk's largest logit m and
+// sum exp2((x - m) * k2).  grid (n_chunks, rows), 256 threads.
+template <typename TL>
+__global__ __launch_bounds__(256) void softmax_partial_kernel(const TL* __restrict__ x, int V, float k2,
+                                                              float* __restrict__ pm, float* __restrict__ ps) {
+  __shared__ float red[4];
+  const int c = blockIdx.x, r = blockIdx.y, nch = gridDim.x;
+  const int c0 = c * kSoftmaxChunk, c1 = min(V, c0 + kSoftmaxChunk);
+  const TL* row = x + static_cast<size_t>(r) * V;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  float m = -INFINITY;
+  for (int j = c0 + threadIdx.x; j < c1; j += 256) m = fmaxf(m, to_f<TL>(row[j]));
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+  if (lane == 0) red[w] = m;
+  __syncthreads();
+  m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = c0 + threadIdx.x; j < c1; j += 256) sum += exp2f((to_f<TL>(row[j]) - m) * k2);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, 64);
+  if (lane == 0) red[w] = sum;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    pm[static_cast<size_t>(r) * nch + c] = m;
+    ps[static_cast<size_t>(r) * nch + c] = ((red[0] + red[1]) + red[2]) + red[3];
+  }
+}
+
+// What stage 2 hands to stage 3, per sequence.
+struct BonusSel {
+  int row;        // a: the row the bonus is drawn from
+  int chunk;      // the chunk holding the draw
+  int corr;       // 1: subtract the proposal of row a (a residual draw)
+  float target;   // remaining mass to walk inside the chunk
+  float m, inv_z; // row a's max and 1 / normaliser
+};
+
+// Stage 2: per sequence (64 threads, n_draft <= 64): row maxima and normalisers from the
+// partials (chunks in ascending order), the acceptance of every draft, a, and the chunk
+// of the bonus draw (residual mass per chunk; the proposal's 16 ids subtracted in order).
+template <typename TL>
+__global__ __launch_bounds__(64) void reject_kernel(const float* __restrict__ pm, const float* __restrict__ ps,
+                                                    int nch, const TL* __restrict__ tgt, int V, float k2,
+                                                    const int32_t* __restrict__ draft, int n_draft,
+                                                    const int32_t* __restrict__ q_ids, long long q_stride,
+                                                    const float* __restrict__ q_probs,
+                                                    const float* __restrict__ u_accept,
+                                                    const float* __restrict__ u_bonus,
+                                                    int32_t* __restrict__ accept_len, BonusSel* __restrict__ sel) {
+  __shared__ float M[65], IZ[65];
+  __shared__ float R[1024];
+  __shared__ int a_s;
+  const int b = blockIdx.x, lane = threadIdx.x, R_rows = n_draft + 1;
+  const TL* T = tgt + static_cast<size_t>(b) * R_rows * V;
+  for (int r = lane; r < R_rows; r += 64) {
+    const size_t o = (static_cast<size_t>(b) * R_rows + r) * nch;
+    float m = -INFINITY;
+    for (int c = 0; c < nch; ++c) m = fmaxf(m, pm[o + c]);
+    float z = 0.f;
+    for (int c = 0; c < nch; ++c) z += ps[o + c] * exp2f((pm[o + c] - m) * k2);
+    M[r] = m;
+    IZ[r] = 1.f / z;
+  }
+  __syncthreads();
+  bool reject = false;
+  if (lane < n_draft) {
+    const int x = draft[static_cast<size_t>(b) * n_draft + lane];
+    const int32_t* ids = q_ids + b * q_stride + lane * 16;
+    const float* qp = q_probs + (static_cast<size_t>(b) * n_draft + lane) * 16;
+    float q = 0.f;
+    for (int j = 15; j >= 0; --j)
+      if (ids[j] == x) q = qp[j];
+    const float px = (x >= 0 && x < V) ? exp2f((to_f<TL>(T[static_cast<size_t>(lane) * V + x]) - M[lane]) * k2) * IZ[lane]
+                                       : 0.f;
+    reject = !(q > 0.f && u_accept[static_cast<size_t>(b) * n_draft + lane] * q < px);
+  }
+  const unsigned long long bal = __ballot(reject);
+  const int a = bal ? __ffsll(static_cast<long long>(bal)) - 1 : n_draft;
+  const float m = M[a], iz = IZ[a];
+  const size_t o = (static_cast<size_t>(b) * R_rows + a) * nch;
+  for (int c = lane; c < nch; c += 64) R[c] = ps[o + c] * exp2f((pm[o + c] - m) * k2) * iz;
+  __syncthreads();
+  if (lane == 0) {
+    const int32_t* ids = q_ids + b * q_stride + a * 16;
+    const float* qp = q_probs + (static_cast<size_t>(b) * n_draft + a) * 16;
+    const TL* Ta = T + static_cast<size_t>(a) * V;
+    float tot = 0.f;
+    int corr = 0;
+    if (a < n_draft) {
+      for (int j = 0; j < 16; ++j) {
+        const int y = ids[j];
+        if (y < 0 || y >= V) continue;
+        const float py = exp2f((to_f<TL>(Ta[y]) - m) * k2) * iz;
+        R[y / kSoftmaxChunk] -= fminf(py, fmaxf(qp[j], 0.f));
+      }
+      for (int c = 0; c < nch; ++c) tot += fmaxf(R[c], 0.f);
+      corr = tot > 0.f;
+      if (!corr) {   // no residual mass: draw from p_a
+        tot = 0.f;
+        for (int c = 0; c < nch; ++c) tot += (R[c] = ps[o + c] * exp2f((pm[o + c] - m) * k2) * iz);
+      }
+    } else {
+      for (int c = 0; c < nch; ++c) tot += R[c];
+    }
+    const float target = u_bonus[b] * tot;
+    float run = 0.f;
+    int ch = -1, last = 0;
+    float rem = 0.f;
+    for (int c = 0; c < nch; ++c) {
+      const float rc = fmaxf(R[c], 0.f);
+      if (rc > 0.f) last = c;
+      if (ch < 0 && target < run + rc) {
+        ch = c;
+        rem = target - run;
+      }
+      run += rc;
+    }
+    if (ch < 0) {
+      ch = last;
+      rem = INFINITY;   // past the end through rounding: the chunk's last token of positive mass
+    }
+    accept_len[b] = a;
+    BonusSel s;
+    s.row = a;
+    s.chunk = ch;
+    s.corr = corr;
+    s.target = rem;
+    s.m = m;
+    s.inv_z = iz;
+    sel[b] = s;
+  }
+}
+
+// Stage 3: per sequence (256 threads), the draw inside the chosen chunk: each thread walks
+// 16 consecutive tokens; thread offsets by an exclusive scan in thread order.
+template <typename TL>
+__global__ __launch_bounds__(256) void bonus_kernel(const TL* __restrict__ tgt, int V, float k2, int n_draft,
+                                                    const int32_t* __restrict__ q_ids, long long q_stride,
+                                                    const float* __restrict__ q_probs,
+                                                    const BonusSel* __restrict__ sel, int32_t* __restrict__ bonus) {
+  constexpr int E = kSoftmaxChunk / 256;
+  __shared__ int cid[16];
+  __shared__ float cq[16];
+  __shared__ float wsum[4];
+  __shared__ int pick_s, last_s;
+  const int b = blockIdx.x, t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const BonusSel s = sel[b];
+  if (t < 16) {
+    cid[t] = s.corr ? q_ids[b * q_stride + s.row * 16 + t] : -1;
+    cq[t] = s.corr ? fmaxf(q_probs[(static_cast<size_t>(b) * n_draft + s.row) * 16 + t], 0.f) : 0.f;
+  }
+  if (t == 0) {
+    pick_s = INT_MAX;
+    last_s = -1;
+  }
+  __syncthreads();
+  const TL* row = tgt + (static_cast<size_t>(b) * (n_draft + 1) + s.row) * V;
+  const int y0 = s.chunk * kSoftmaxChunk + t * E;
+  float r[E];
+  float sum = 0.f;
+  int lastpos = -1;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int y = y0 + e;
+    float v = 0.f;
+    if (y < V) {
+      v = exp2f((to_f<TL>(row[y]) - s.m) * k2) * s.inv_z;
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (cid[j] == y) v = fmaxf(v - cq[j], 0.f);
+    }
+    r[e] = v;
+    sum += v;
+    if (v > 0.f) lastpos = y;
+  }
+  // inclusive scan of the thread sums in thread order; thread t owns [incl_{t-1}, incl_t),
+  // both ends computed by the same operations in the two threads that share them
+  float inc = sum;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float up = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += up;
+  }
+  const float prev = __shfl_up(inc, 1, 64);
+  if (lane == 63) wsum[w] = inc;
+  __syncthreads();
+  float base = 0.f;
+  for (int k = 0; k < w; ++k) base += wsum[k];
+  const float lo = lane == 0 ? base : base + prev, hi = base + inc;
+  if (s.target >= lo && s.target < hi) {
+    float run = lo;
+    int pick = lastpos;                 // the walk can fall short of hi through rounding
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      run += r[e];
+      if (s.target < run) {
+        pick = y0 + e;
+        break;
+      }
+    }
+    atomicMin(&pick_s, pick);
+  }
+  if (lastpos >= 0) atomicMax(&last_s, lastpos);
+  __syncthreads();
+  if (t == 0) bonus[b] = pick_s != INT_MAX ? pick_s : (last_s >= 0 ? last_s : s.chunk * kSoftmaxChunk);
+}
+
 // Next cycle's state from a verified block (one thread per sequence): the anchor and the
 // a accepted drafts become the next a + 1 context rows, the bonus token the next anchor.
 __global__ __launch_bounds__(64) void advance_kernel(const int32_t* __restrict__ accept_len,
@@ -518,6 +738,55 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const float* __restrict__
     const int c = chosen[p];
     path_idx[static_cast<size_t>(b) * P + p] = c;
     path_ids[static_cast<size_t>(b) * P + p] = ci[p * 16 + c];
+  }
+}
+
+// The sampled walk: q_p[j] = softmax_j of the greedy walk's score of candidate j at
+// temperature t (scores scaled by k2 = log2(e)/t; max and sum by a 16-lane butterfly),
+// and c_p = the first j whose running sum of q_p (candidate order) exceeds
+// uniforms[b][p] times the total (the last j with q_p > 0 if none does).  grid (B), 64
+// threads (lanes 0..15 hold one candidate each).
+__global__ __launch_bounds__(64) void path_sample_kernel(const float* __restrict__ S_in,
+                                                         const int32_t* __restrict__ cand_ids,
+                                                         const float* __restrict__ cand_logits, int n_fixed, float k2,
+                                                         const float* __restrict__ uniforms,
+                                                         int32_t* __restrict__ path_idx,
+                                                         int32_t* __restrict__ path_ids,
+                                                         float* __restrict__ path_q) {
+  const int b = blockIdx.x, P = 16 - n_fixed;
+  if (threadIdx.x >= 16) return;
+  const int j = threadIdx.x;
+  const float* S = S_in + static_cast<size_t>(b) * P * 256;
+  const float* lg = cand_logits + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
+  const int32_t* ci = cand_ids + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
+  int c = 0;
+  for (int p = 0; p < P; ++p) {
+    const float sc = p == 0 ? lg[j] + (n_fixed == 1 ? S[j] : 0.f) : lg[p * 16 + j] + S[(p * 16 + c) * 16 + j];
+    float mx = sc;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 16));
+    const float e = exp2f((sc - mx) * k2);
+    float z = e;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) z += __shfl_xor(z, o, 16);
+    const float q = e / z;
+    path_q[(static_cast<size_t>(b) * P + p) * 16 + j] = q;
+    float tot = 0.f;
+    for (int i = 0; i < 16; ++i) tot += __shfl(q, i, 16);
+    const float target = uniforms[static_cast<size_t>(b) * P + p] * tot;
+    float run = 0.f;
+    int pick = -1, last = 0;
+    for (int i = 0; i < 16; ++i) {
+      const float qi = __shfl(q, i, 16);
+      run += qi;
+      if (pick < 0 && target < run) pick = i;
+      if (qi > 0.f) last = i;
+    }
+    c = pick >= 0 ? pick : last;
+    if (j == 0) {
+      path_idx[static_cast<size_t>(b) * P + p] = c;
+      path_ids[static_cast<size_t>(b) * P + p] = ci[p * 16 + c];
+    }
   }
 }
 

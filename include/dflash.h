@@ -239,6 +239,57 @@ int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtyp
                   int32_t n_draft, int32_t vocab, int32_t* accept_len, int32_t* bonus,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Sampled path choice ("DFlash 2 ...", "Arquitectura del Sistema", item 1: the block can
+ * be chosen by sampling over the precomputed scores instead of the greedy walk).
+ *
+ * Same scores as dflash_select_path.  Left to right, position p's candidate is drawn from
+ *   q_p[j] = softmax_j( (cand_logits[p][j] + phi_{row p}(c_{p-1}, cand_ids[p][j])) / temperature )
+ * (no pair term at p = 0 without an anchor): c_p is the first j whose running sum of
+ * q_p in candidate order exceeds uniforms[b][p] times the sum of q_p (the last j with
+ * q_p[j] > 0 if rounding leaves none).  fp32 throughout.
+ *
+ * temperature : > 0 and finite (else DFLASH_E_INVAL).
+ * uniforms    : device float [batch, P], the caller's uniform draws in [0, 1).
+ * path_q      : device float [batch, P, 16], written: q_p, the distribution each position
+ *               was drawn from (the proposal that dflash_verify_sampled divides by).
+ * Other arguments, outputs and workspace as for dflash_select_path.
+ */
+int dflash_sample_path(const dflash_config* cfg, const dflash_weights* w,
+                       const int32_t* cand_ids, const float* cand_logits, const float* final_hidden,
+                       const int32_t* block_ids, int32_t n_fixed, int32_t batch, float temperature,
+                       const float* uniforms, int32_t* path_idx, int32_t* path_ids, float* path_q,
+                       float* pair_scores, void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Verification by rejection sampling, which keeps the target's distribution exactly
+ * ("DFlash 2 ...", "Arquitectura del Sistema", item 1; "FlexDraft", problem statement: the
+ * bonus token is drawn at the first rejection).
+ *
+ * p_i = softmax(tgt_logits[b][i] / temperature) over the vocabulary.  Draft token x_i was
+ * drawn from the proposal q_i, given sparsely by 16 ids and probabilities (q_i(x) = 0 for
+ * ids not listed; ids within a row must be distinct).  Draft i is accepted when
+ * u_accept[b][i] * q_i(x_i) < p_i(x_i), i.e. with probability min(1, p_i(x_i) / q_i(x_i));
+ * a draft with q_i(x_i) = 0 is rejected.  accept_len[b] = a, the number of leading
+ * accepted drafts.  The bonus token is drawn from max(0, p_a - q_a) normalised (from p_a
+ * when a = n_draft, or when rounding leaves that residual no mass), inverting its running
+ * sum in ascending token id with u_bonus[b].  fp32 exponentials and sums.
+ *
+ * draft        : device int32 [batch, n_draft]
+ * q_ids        : device int32; row i of sequence b at q_ids[b * q_ids_stride + 16 * i + j],
+ *                j = 0..15 (q_ids_stride >= 16 * n_draft; the draft call's candidate array
+ *                offset by 16 * n_fixed with stride 256 serves directly).
+ * q_probs      : device float [batch, n_draft, 16] (dflash_sample_path's path_q).
+ * tgt_logits   : device [batch, n_draft+1, vocab], DFLASH_BF16 or DFLASH_F32 (tgt_dtype).
+ * u_accept     : device float [batch, n_draft]; u_bonus: device float [batch]; uniforms in [0, 1).
+ * accept_len, bonus : device int32 [batch], written.
+ * n_draft in 0..64 and vocab <= 4194304 (else DFLASH_E_UNSUPPORTED); temperature > 0 and
+ * finite.  Workspace: dflash_verify_sampled_workspace_bytes(batch, n_draft, vocab).
+ */
+int dflash_verify_sampled(const int32_t* draft, const int32_t* q_ids, int64_t q_ids_stride,
+                          const float* q_probs, const void* tgt_logits, int32_t tgt_dtype, int32_t batch,
+                          int32_t n_draft, int32_t vocab, float temperature, const float* u_accept,
+                          const float* u_bonus, int32_t* accept_len, int32_t* bonus,
+                          void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Advance the drafting cycle on the device ("DFlash 2 ...", "Flujo de Inferencia con
  * DFlash 2": the verified prefix plus the bonus token are emitted and drafting resumes
  * from them; "DFlash ...", section 2.2: the target's hidden states of the tokens it has
@@ -269,6 +320,7 @@ size_t dflash_inject_workspace_bytes(const dflash_config* cfg, int32_t n_rows);
 size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t cap);
 size_t dflash_path_workspace_bytes(const dflash_config* cfg, int32_t batch);
 size_t dflash_verify_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab);
+size_t dflash_verify_sampled_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab);
 
 /* Check a configuration against what the kernels support: DFLASH_OK, DFLASH_E_INVAL
  * or DFLASH_E_UNSUPPORTED. */

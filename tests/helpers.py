@@ -138,3 +138,20 @@ def oracle_draft(m, K, V, ctx_lens, block_ids):
         vc = [oracle.decode(V[l, b], D.dtype) for l in range(D.n_layers)]
         outs.append(oracle.draft_block(m, kc, vc, int(L), block_ids[b]))
     return outs
+
+
+def draw_f32(q, u):
+    """The device's inverse-CDF draw over given fp32 probabilities, in its documented
+    order: total and running sum sequential in fp32, target = u * total; the first index
+    whose running sum exceeds the target, else the last index of positive probability."""
+    q = np.asarray(q, dtype=np.float32)
+    tot = np.float32(0)
+    for v in q:
+        tot = np.float32(tot + v)
+    target = np.float32(np.float32(u) * tot)
+    run = np.float32(0)
+    for i, v in enumerate(q):
+        run = np.float32(run + v)
+        if target < run:
+            return i
+    return int(np.flatnonzero(q > 0)[-1])

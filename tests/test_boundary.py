@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 14
     lib = ctypes.CDLL(D.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -128,3 +128,44 @@ def test_advance_rejects_bad_arguments():
     assert lib.dflash_advance(f, f, 0, 0, 64, f, f, f, f, None) == D.DFLASH_E_INVAL
     assert lib.dflash_advance(f, f, 1, 0, 0, f, f, f, f, None) == D.DFLASH_E_INVAL
     assert lib.dflash_advance(f, f, 1, 0, 64, f, f, None, f, None) == D.DFLASH_E_INVAL
+
+
+def test_sampling_calls_reject_bad_arguments():
+    dims = synth.workload("t_conv").dims
+    cfg, w, kv = _fake_structs(dims)
+    ws_p = D.dflash_path_workspace_bytes(cfg, 2)
+    S = 1
+    sp = D.dflash_sample_path
+    # (cfg, w, cand_ids, cand_logits, xhat, block_ids, n_fixed, batch, t, uniforms, idx, ids, q, ps, ws, nb)
+    assert _status(sp, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 2, 0.0, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(sp, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 2, -1.0, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(sp, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 2, float("nan"), FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(sp, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 2, 1.0, None, FAKE, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(sp, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 2, 1.0, FAKE, FAKE, FAKE, None, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(sp, cfg, w, FAKE, FAKE, FAKE, FAKE, 2, 2, 1.0, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_p, S) == D.DFLASH_E_INVAL
+    assert _status(sp, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 2, 1.0, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws_p - 1, S) == D.DFLASH_E_WORKSPACE
+    vs = D.dflash_verify_sampled
+    ws_v = D.dflash_verify_sampled_workspace_bytes(2, 15, 1024)
+    assert ws_v > 0 and D.dflash_verify_sampled_workspace_bytes(2, 65, 1024) == 0
+    assert D.dflash_verify_sampled_workspace_bytes(2, 15, 4096 * 1024 + 1) == 0
+    # (draft, q_ids, stride, q_probs, T, dtype, batch, n_draft, vocab, t, u_acc, u_bonus, acc, bonus, ws, nb)
+    ok = (FAKE, FAKE, 256, FAKE, FAKE, D.DFLASH_BF16, 2, 15, 1024, 1.0, FAKE, FAKE, FAKE, FAKE, FAKE, ws_v, S)
+
+    def bad(**kw):
+        names = ("draft", "q_ids", "stride", "q_probs", "T", "dtype", "batch", "n_draft", "vocab", "t", "u_acc",
+                 "u_bonus", "acc", "bonus", "ws", "nb", "s")
+        a = dict(zip(names, ok))
+        a.update(kw)
+        return _status(vs, *[a[n] for n in names])
+    assert bad(t=0.0) == D.DFLASH_E_INVAL
+    assert bad(t=float("inf")) == D.DFLASH_E_INVAL
+    assert bad(n_draft=65) == D.DFLASH_E_UNSUPPORTED
+    assert bad(vocab=4096 * 1024 + 1) == D.DFLASH_E_UNSUPPORTED
+    assert bad(dtype=7) == D.DFLASH_E_INVAL
+    assert bad(stride=16 * 15 - 1) == D.DFLASH_E_INVAL
+    assert bad(q_ids=None) == D.DFLASH_E_INVAL
+    assert bad(q_probs=None) == D.DFLASH_E_INVAL
+    assert bad(u_acc=None) == D.DFLASH_E_INVAL
+    assert bad(u_bonus=None) == D.DFLASH_E_INVAL
+    assert bad(nb=ws_v - 1) == D.DFLASH_E_WORKSPACE
+    assert bad(batch=0) == D.DFLASH_E_INVAL
