@@ -48,7 +48,8 @@ __all__ = [
     "inject_rows", "short_conv", "block_attention", "draft_block", "topk",
     "path_pair_scores", "select_path", "verify", "conv_param_count",
     "path_selector_param_count", "drafting_step", "advance", "drafting_cycles",
-    "sample_path", "verify_sampled",
+    "sample_path", "verify_sampled", "e4m3_values", "e4m3_encode", "e4m3_decode", "quantize_fp8_rows",
+    "dequantize_fp8_rows", "FP8_MATRICES", "is_fp8_matrix",
 ]
 
 
@@ -85,6 +86,88 @@ def bf16_round(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def e4m3_values() -> np.ndarray:
+    """Value of each of the 256 codes of the OCP 8-bit floating-point format E4M3 (the
+    "fn" variant: no infinities), float64: bit 7 sign, bits 6..3 exponent with bias 7,
+    bits 2..0 mantissa; exponent 0 encodes subnormals m * 2^-9; exponent 15 with
+    mantissa 7 is NaN, so the largest finite magnitude is 1.75 * 2^8 = 448."""
+    v = np.empty(256)
+    for c in range(256):
+        sign = -1.0 if c & 0x80 else 1.0
+        e, m = (c >> 3) & 15, c & 7
+        if e == 15 and m == 7:
+            v[c] = np.nan
+        elif e == 0:
+            v[c] = sign * m * 2.0 ** -9
+        else:
+            v[c] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return v
+
+
+_E4M3 = e4m3_values()
+_E4M3_POS = _E4M3[:127]                    # codes 0..126: the finite non-negative values, increasing
+
+
+def e4m3_encode(x: np.ndarray) -> np.ndarray:
+    """Codes of the E4M3 values nearest to x, ties to the even code (even mantissa),
+    magnitudes above 448 saturating to +-448; zero (of either sign) encodes as 0."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first grid value >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
+    code = np.where(dhi < dlo, hi, lo)
+    tie = (dhi == dlo) & (hi != lo)
+    code = np.where(tie, np.where(hi % 2 == 0, hi, lo), code)
+    code = np.where(_E4M3_POS[hi] == a, hi, code)
+    code = code.astype(np.uint8)
+    neg = (x < 0) & (code != 0)
+    return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
+
+
+def e4m3_decode(codes: np.ndarray) -> np.ndarray:
+    return _E4M3[np.asarray(codes, dtype=np.uint8)]
+
+
+def quantize_fp8_rows(w: np.ndarray):
+    """Weight quantization to E4M3 with one scale per output row (row of W).
+
+    "DFlash 2 ..." table: the drafter is served with draft quantization enabled.  Reading:
+    8-bit E4M3 weights with a float32 scale per output row, the scale being the row's
+    largest magnitude over 448 (the format's largest finite value) and each code the E4M3
+    value nearest to w / scale; both divisions in float32 (the values the codes are taken
+    from are thereby fixed exactly).  A row of zeros gets scale 0 and codes 0.
+
+    w: [rows, cols] float32 (the stored bf16 weights, decoded).  Returns (codes uint8
+    [rows, cols], scales float32 [rows]).
+    """
+    w = np.asarray(w, dtype=np.float32)
+    amax = np.abs(w).max(axis=1).astype(np.float32)
+    scale = (amax / np.float32(448.0)).astype(np.float32)
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    x = (w / safe[:, None]).astype(np.float32)
+    codes = e4m3_encode(x)
+    codes[scale == 0] = 0
+    return codes, scale
+
+
+def dequantize_fp8_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """The weights an E4M3 matrix stands for: code value times its row's scale (float64)."""
+    return e4m3_decode(codes) * np.asarray(scales, dtype=np.float64)[:, None]
+
+
+# Weights held in E4M3 under fp8 weight storage: every streamed projection of the drafter
+# (fusion, Q/K/V, O, gate/up, down, LM head).  The token embedding (gathered by rows), the
+# dynamic-conv generators and taps, the Path Selector's factors and the norm gains stay in
+# the storage type.
+FP8_MATRICES = ("w_fc", "lm_head", "w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")
+
+
+def is_fp8_matrix(name: str) -> bool:
+    return name.split(".")[-1] in FP8_MATRICES
+
+
 # ----------------------------------------------------------------------------------
 # model container
 # ----------------------------------------------------------------------------------
@@ -96,14 +179,22 @@ class Model:
     ``weights`` maps names to stored tensors (bf16 bit patterns or float32).
     """
 
-    def __init__(self, dims, weights: Dict[str, np.ndarray]):
+    def __init__(self, dims, weights: Dict[str, np.ndarray], fp8: bool = False):
+        if fp8 and dims.dtype != "bf16":
+            raise ValueError("fp8 weight storage applies to bf16 drafters")
         self.dims = dims
         self.stored = weights
+        self.fp8 = fp8
         self._cache: Dict[str, np.ndarray] = {}
 
     def w(self, name: str) -> np.ndarray:
+        """Weight values as float64; under fp8 storage the projections listed in
+        ``FP8_MATRICES`` are the values their E4M3 codes and row scales stand for."""
         if name not in self._cache:
-            self._cache[name] = decode(self.stored[name], self.dims.dtype)
+            v = decode(self.stored[name], self.dims.dtype)
+            if self.fp8 and is_fp8_matrix(name):
+                v = dequantize_fp8_rows(*quantize_fp8_rows(v.astype(np.float32)))
+            self._cache[name] = v
         return self._cache[name]
 
     def rows(self, name: str, idx) -> np.ndarray:
