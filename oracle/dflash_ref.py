@@ -105,23 +105,26 @@ def e4m3_values() -> np.ndarray:
 
 
 _E4M3 = e4m3_values()
-_E4M3_POS = _E4M3[:127]                    # codes 0..126: the finite non-negative values, increasing
 
 
 def e4m3_encode(x: np.ndarray) -> np.ndarray:
     """Codes of the E4M3 values nearest to x, ties to the even code (even mantissa),
-    magnitudes above 448 saturating to +-448; zero (of either sign) encodes as 0."""
-    x = np.asarray(x, dtype=np.float64)
-    a = np.minimum(np.abs(x), 448.0)
-    hi = np.searchsorted(_E4M3_POS, a, side="left")          # first grid value >= a
-    hi = np.minimum(hi, 126)
-    lo = np.maximum(hi - 1, 0)
-    dlo, dhi = a - _E4M3_POS[lo], _E4M3_POS[hi] - a
-    code = np.where(dhi < dlo, hi, lo)
-    tie = (dhi == dlo) & (hi != lo)
-    code = np.where(tie, np.where(hi % 2 == 0, hi, lo), code)
-    code = np.where(_E4M3_POS[hi] == a, hi, code)
-    code = code.astype(np.uint8)
+    magnitudes above 448 saturating to +-448; zero (of either sign) encodes as 0.
+
+    In the binade [2^E, 2^(E+1)) the grid spacing is 2^(E-3) (3 mantissa bits); below
+    2^-6 it stays 2^-9 (subnormals).  |x| / spacing is exact in float64 and ``np.rint``
+    rounds half to even, so the nearest multiple with an even last bit wins ties."""
+    x = np.asarray(x)
+    if x.dtype != np.float32:        # every step below is exact for float32 inputs
+        x = x.astype(np.float64)
+    a = np.minimum(np.abs(x), x.dtype.type(448.0))
+    _, e = np.frexp(a)                                   # a = f * 2^e, f in [0.5, 1)
+    spacing = np.ldexp(x.dtype.type(1.0), np.maximum(e - 1, -6) - 3)
+    v = np.minimum(np.rint(a / spacing) * spacing, x.dtype.type(448.0))
+    _, e2 = np.frexp(v)
+    normal = v >= 2.0 ** -6
+    mant = np.where(normal, np.ldexp(v, 4 - e2) - 8, 0)              # v = (8 + mant) * 2^(e2-4)
+    code = np.where(normal, (e2 - 1 + 7) * 8 + mant, v * 512).astype(np.uint8)
     neg = (x < 0) & (code != 0)
     return np.where(neg, code | np.uint8(0x80), code).astype(np.uint8)
 
@@ -146,8 +149,10 @@ def quantize_fp8_rows(w: np.ndarray):
     amax = np.abs(w).max(axis=1).astype(np.float32)
     scale = (amax / np.float32(448.0)).astype(np.float32)
     safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
-    x = (w / safe[:, None]).astype(np.float32)
-    codes = e4m3_encode(x)
+    codes = np.empty(w.shape, dtype=np.uint8)
+    for r0 in range(0, w.shape[0], 2048):                 # row blocks bound the temporaries
+        x = (w[r0:r0 + 2048] / safe[r0:r0 + 2048, None]).astype(np.float32)
+        codes[r0:r0 + 2048] = e4m3_encode(x)
     codes[scale == 0] = 0
     return codes, scale
 
