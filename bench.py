@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--sampled-steps", type=int, default=20,
                     help="also time this many steps of the sampling variant (sampled path choice and "
                          "verification by rejection sampling, temperature 0.8) and report them apart")
+    ap.add_argument("--fp8-steps", type=int, default=20,
+                    help="also time this many steps with the streamed projections in FP8 storage (E4M3 codes, "
+                         "a float32 scale per row) and report them apart (bf16 workloads)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the step, run a plain fp32 elementwise copy (torch.neg) of this many MiB "
                          "three times: a kernel of known traffic that calibrates HBM byte counters")
@@ -59,37 +62,44 @@ def parse():
 
 # ------------------------------------------------------------------ algorithmic work per probed kernel
 
-def kernel_work(dims, batch, ctx_lens):
-    """(bytes, flops) each probed kernel must move / compute at minimum, per launch."""
+def kernel_work(dims, batch, ctx_lens, fp8=False):
+    """(bytes, flops) each probed kernel must move / compute at minimum, per launch.  With
+    fp8, the streamed projections are read in FP8 storage (cols + 16 bytes per row)."""
     e = 2 if dims.dtype == "bf16" else 4
     d, H, Hkv, hd, F, V = dims.d, dims.n_heads, dims.n_kv_heads, dims.head_dim, dims.d_ffn, dims.vocab
     M = 16 * batch
     hq, hk = H * hd, Hkv * hd
     kv_rows = sum(ctx_lens)
+
+    def wb(rows, cols):
+        return rows * (cols + 16) if fp8 else rows * cols * e
     w = {
-        "lm_head": (V * d * e + M * d * e + M * V * 4, 2 * M * V * d),
-        "qkv": ((hq + 2 * hk) * d * e + M * d * e + M * (hq + 2 * hk) * e, 2 * M * (hq + 2 * hk) * d),
-        "o": (d * hq * e + M * hq * e + 2 * M * d * 4, 2 * M * d * hq),
-        "gate_up": (2 * F * d * e + M * d * e + M * F * e, 2 * M * 2 * F * d),
-        "down": (d * F * e + M * F * e + 2 * M * d * 4, 2 * M * d * F),
+        "lm_head": (wb(V, d) + M * d * e + M * V * 4, 2 * M * V * d),
+        "qkv": (wb(hq + 2 * hk, d) + M * d * e + M * (hq + 2 * hk) * e, 2 * M * (hq + 2 * hk) * d),
+        "o": (wb(d, hq) + M * hq * e + 2 * M * d * 4, 2 * M * d * hq),
+        "gate_up": (wb(2 * F, d) + M * d * e + M * F * e, 2 * M * 2 * F * d),
+        "down": (wb(d, F) + M * F * e + 2 * M * d * 4, 2 * M * d * F),
         # block attention of one layer: every context K and V row once, plus q, block k/v, o
         "attn": (2 * kv_rows * hk * e + M * hq * e * 2 + 2 * M * hk * e,
                  2 * 2 * batch * 16 * H * hd * (sum(ctx_lens) / max(batch, 1) + 16)),
         "topk": (M * V * 4, 0),
-        "inject_fc": (d * dims.d_cat * e + M * dims.d_cat * e + M * d * 4, 2 * M * d * dims.d_cat),
-        "inject_kv": (dims.n_layers * 2 * hk * d * e + M * d * e + M * dims.n_layers * 2 * hk * e,
+        "inject_fc": (wb(d, dims.d_cat) + M * dims.d_cat * e + M * d * 4, 2 * M * d * dims.d_cat),
+        "inject_kv": (dims.n_layers * wb(2 * hk, d) + M * d * e + M * dims.n_layers * 2 * hk * e,
                       2 * M * dims.n_layers * 2 * hk * d),
     }
     return w
 
 
-def step_bytes(dims, batch, ctx_lens):
+def step_bytes(dims, batch, ctx_lens, fp8=False):
     """Algorithmic HBM bytes of one whole step (weights once, KV once per layer, target logits)."""
     e = 2 if dims.dtype == "bf16" else 4
     d, H, Hkv, hd, F, V, L = dims.d, dims.n_heads, dims.n_kv_heads, dims.head_dim, dims.d_ffn, dims.vocab, dims.n_layers
-    per_layer = ((H + 2 * Hkv) * hd * d + d * H * hd + 3 * F * d) * e
+
+    def wb(rows, cols):
+        return rows * (cols + 16) if fp8 else rows * cols * e
+    per_layer = wb((H + 2 * Hkv) * hd, d) + wb(d, H * hd) + wb(3 * F, d)
     conv = (4 * (2 * (d // 16) * d + 2 * d) * e) if dims.use_conv else 0
-    weights = L * (per_layer + conv) + V * d * e + d * dims.d_cat * e + (3 * dims.ps_dim * d + 2 * dims.ps_rank * dims.ps_dim) * e
+    weights = L * (per_layer + conv) + wb(V, d) + wb(d, dims.d_cat) + (3 * dims.ps_dim * d + 2 * dims.ps_rank * dims.ps_dim) * e
     kv = L * 2 * sum(ctx_lens) * Hkv * hd * e
     tgt = batch * 16 * V * e
     return weights + kv + tgt
@@ -414,6 +424,46 @@ def main():
                    "blocks_per_s": round(B * 1000.0 / ms_s, 2), "temperature": temp,
                    "path": "sampled over the pair scores", "verify": "rejection sampling"}
 
+    fp8 = None
+    if args.fp8_steps > 0 and dims.dtype == "bf16":
+        dr8 = D.Drafter(dims, dr.t, fp8=True)       # quantized on the device from the bf16 copies
+
+        def step8(probes=None):
+            D.dflash_inject_context(dr8.cfg, dr8.w, cache.kv, new_hid, 16 * B, row_off, pos0, n_new, B, ws_i, nb_i,
+                                    probes=probes.struct if probes else None)
+            D.dflash_draft_block(dr8.cfg, dr8.w, cache.kv, ctx_t, ids_t, B, ci, cl, fh, None, ws_d, nb_d,
+                                 probes=probes.struct if probes else None)
+            D.dflash_select_path(dr8.cfg, dr8.w, ci, cl, fh, ids_t, 1, D.DFLASH_PATH_GREEDY, B, pidx, pids, None,
+                                 ws_p, nb_p)
+            D.dflash_verify(pids, T, tdt, B, 15, dims.vocab, acc, bon, ws_v, nb_v)
+
+        live8 = {k: D.Probes(("lm_head", "attn")) for k in range(0, args.fp8_steps, PROBE_EVERY)}
+        for _ in range(3):
+            step8()
+        torch.cuda.synchronize()
+        start.record()
+        for k in range(args.fp8_steps):
+            step8(live8.get(k))
+        stop.record()
+        torch.cuda.synchronize()
+        ms8 = start.elapsed_time(stop) / args.fp8_steps
+        w8 = kernel_work(dims, B, wl.ctx_lens, fp8=True)
+        lm_ms = float(np.mean([p.ms("lm_head") for p in live8.values()]))
+        lm_bytes = w8["lm_head"][0]
+        sb8 = step_bytes(dims, B, wl.ctx_lens, fp8=True)
+        log(f"[bench] fp8 weights: {ms8:.3f} ms/step, {B * 1000.0 / ms8:.1f} blocks/s, LM head {lm_ms * 1e3:.1f} us")
+        fp8 = {"steps": args.fp8_steps, "ms_per_step": round(ms8, 4), "blocks_per_s": round(B * 1000.0 / ms8, 2),
+               "weights": "E4M3 codes + float32 scale per row for the streamed projections; bf16 activations and "
+                          "bf16 matrix-core products (codes widened exactly), fp32 accumulation",
+               "lm_head": {"bound": "hbm", "achieved": round(lm_bytes / (lm_ms * 1e-3) / 1e9, 1),
+                           "peak": HBM_PEAK / 1e9, "unit": "GB/s",
+                           "frac": round(lm_bytes / (lm_ms * 1e-3) / HBM_PEAK, 4),
+                           "algorithmic_bytes_per_launch": int(lm_bytes), "ms_per_launch": round(lm_ms, 4)},
+               "step_roofline": {"algorithmic_bytes": int(sb8), "hbm_bound_ms": round(sb8 / HBM_PEAK * 1e3, 4),
+                                 "frac": round(sb8 / HBM_PEAK * 1e3 / ms8, 4)},
+               "weight_bytes_on_device": int(dr8.nbytes())}
+        del dr8
+
     cycle = None
     if args.cycles > 0:
         cycle = run_cycles(args.cycles, D, torch, np, synth, wl, dr, new_hid, row_off, tdt, log)
@@ -455,6 +505,8 @@ def main():
     }
     if sampled is not None:
         out["sampled"] = sampled
+    if fp8 is not None:
+        out["fp8_weights"] = fp8
     if cycle is not None:
         out["cycle"] = cycle
     print(json.dumps(out), flush=True)

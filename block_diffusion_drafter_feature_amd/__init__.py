@@ -27,6 +27,8 @@ DFLASH_E_UNSUPPORTED = -2
 DFLASH_E_WORKSPACE = -3
 DFLASH_E_CAPACITY = -4
 DFLASH_E_HIP = -5
+DFLASH_WEIGHTS_DTYPE = 0
+DFLASH_WEIGHTS_FP8 = 1
 DFLASH_F32 = 0
 DFLASH_BF16 = 1
 DFLASH_PATH_GREEDY = 0
@@ -38,7 +40,7 @@ N_PROBES = len(PROBES)
 
 EXPORTED = (
     "dflash_inject_context", "dflash_draft_block", "dflash_select_path", "dflash_verify", "dflash_advance",
-    "dflash_sample_path", "dflash_verify_sampled",
+    "dflash_sample_path", "dflash_verify_sampled", "dflash_quantize_fp8",
     "dflash_inject_workspace_bytes", "dflash_draft_workspace_bytes", "dflash_path_workspace_bytes",
     "dflash_verify_workspace_bytes", "dflash_verify_sampled_workspace_bytes", "dflash_check_config",
     "dflash_status_string",
@@ -62,7 +64,7 @@ class dflash_config(ctypes.Structure):
                 ("head_dim", _i32), ("d_ffn", _i32), ("n_layers", _i32), ("n_feat_layers", _i32),
                 ("d_target", _i32), ("vocab", _i32), ("ps_dim", _i32), ("ps_rank", _i32),
                 ("use_conv", _i32), ("use_gate", _i32), ("rms_eps", ctypes.c_float),
-                ("rope_theta", ctypes.c_float)]
+                ("rope_theta", ctypes.c_float), ("weight_format", _i32)]
 
 
 class dflash_layer_weights(ctypes.Structure):
@@ -113,6 +115,7 @@ def lib() -> ctypes.CDLL:
             "dflash_verify_sampled": ([_vp, _vp, ctypes.c_int64, _vp, _vp, _i32, _i32, _i32, _i32, ctypes.c_float,
                                        _vp, _vp, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
             "dflash_verify_sampled_workspace_bytes": ([_i32, _i32, _i32], PC),
+            "dflash_quantize_fp8": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
             "dflash_inject_workspace_bytes": ([cfgp, _i32], PC),
             "dflash_draft_workspace_bytes": ([cfgp, _i32, _i32], PC),
             "dflash_path_workspace_bytes": ([cfgp, _i32], PC),
@@ -299,9 +302,10 @@ class Probes:
 
 # ------------------------------------------------------------------ memory helpers (allocation / layout only)
 
-def make_config(dims) -> dflash_config:
-    """A ``dflash_config`` from an object with the attributes of ``synth.Dims``."""
-    return dflash_config(
+def make_config(dims, fp8: bool = False) -> dflash_config:
+    """A ``dflash_config`` from an object with the attributes of ``synth.Dims``; ``fp8``
+    selects FP8 storage of the streamed projections."""
+    return dflash_config(weight_format=DFLASH_WEIGHTS_FP8 if fp8 else DFLASH_WEIGHTS_DTYPE,
         dtype=DFLASH_BF16 if dims.dtype == "bf16" else DFLASH_F32, d_model=dims.d, n_heads=dims.n_heads,
         n_kv_heads=dims.n_kv_heads, head_dim=dims.head_dim, d_ffn=dims.d_ffn, n_layers=dims.n_layers,
         n_feat_layers=dims.n_feat_layers, d_target=dims.d_target, vocab=dims.vocab, ps_dim=dims.ps_dim,
@@ -324,13 +328,34 @@ def to_device(arr, dims, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
-class Drafter:
-    """Device copies of a drafter's weights and the structs that point at them."""
+def dflash_quantize_fp8(w, rows: int, cols: int, out, stream=None) -> None:
+    _check("dflash_quantize_fp8", lib().dflash_quantize_fp8(_ptr(w), rows, cols, _ptr(out), _stream(stream)))
 
-    def __init__(self, dims, weights: Dict[str, "object"], device: str = "cuda"):
+
+FP8_MATRICES = ("w_fc", "lm_head", "w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down")
+
+
+class Drafter:
+    """Device copies of a drafter's weights and the structs that point at them.  With
+    ``fp8=True`` the streamed projections are uploaded in bf16 and turned into FP8
+    storage (E4M3 rows with a float32 scale) by ``dflash_quantize_fp8``."""
+
+    def __init__(self, dims, weights: Dict[str, "object"], device: str = "cuda", fp8: bool = False):
+        import torch
         self.dims = dims
-        self.t = {k: to_device(v, dims, device) for k, v in weights.items()}
-        self.cfg = make_config(dims)
+        self.fp8 = fp8
+        self.t = {}
+        for k, v in weights.items():
+            # device tensors are used as they are (shared), host arrays uploaded
+            t = v if isinstance(v, torch.Tensor) and v.is_cuda else to_device(v, dims, device)
+            if fp8 and k.split(".")[-1] in FP8_MATRICES:
+                rows, cols = t.shape
+                q = torch.empty(rows * (cols + 16), dtype=torch.uint8, device=device)
+                dflash_quantize_fp8(t, rows, cols, q)
+                torch.cuda.synchronize()
+                t = q
+            self.t[k] = t
+        self.cfg = make_config(dims, fp8)
         st = dflash_check_config(self.cfg)
         if st != DFLASH_OK:
             raise DflashError("dflash_check_config", st)

@@ -186,4 +186,27 @@ __device__ __forceinline__ bool better(float va, int ia, float vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
+// 16 E4M3 codes (bytes in k order) widened to two fragments of 8 bf16 values: exact,
+// every E4M3 value being a bf16 value.  Each 32-bit word holds 4 codes; the conversion
+// takes them two at a time (low half-word first).
+__device__ __forceinline__ void fp8x16_to_bf16(u32x4_t raw, bf16x8_t& lo, bf16x8_t& hi) {
+  u32x4_t a, b;
+  a[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, false));
+  a[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[0], 1.0f, true));
+  a[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, false));
+  a[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[1], 1.0f, true));
+  b[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[2], 1.0f, false));
+  b[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[2], 1.0f, true));
+  b[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[3], 1.0f, false));
+  b[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[3], 1.0f, true));
+  lo = __builtin_bit_cast(bf16x8_t, a);
+  hi = __builtin_bit_cast(bf16x8_t, b);
+}
+
+// Scale of an FP8-storage weight row: the float32 stored right after its cols codes.
+template <typename T>
+__device__ __forceinline__ float fp8_row_scale(const T* row, int cols) {
+  return row ? *reinterpret_cast<const float*>(reinterpret_cast<const char*>(row) + cols) : 0.f;
+}
+
 }  // namespace dflash

@@ -60,6 +60,8 @@ int check_config(const dflash_config* c) {
   if (c->vocab % 16 || c->vocab < 16) return DFLASH_E_UNSUPPORTED;
   if (c->vocab > 256 * kTopkChunk) return DFLASH_E_UNSUPPORTED;     // top-k merges <= 256 chunk lists
   if (c->ps_dim % 64 || c->ps_rank > 256) return DFLASH_E_UNSUPPORTED;
+  if (c->weight_format != DFLASH_WEIGHTS_DTYPE && c->weight_format != DFLASH_WEIGHTS_FP8) return DFLASH_E_INVAL;
+  if (c->weight_format == DFLASH_WEIGHTS_FP8 && c->dtype != DFLASH_BF16) return DFLASH_E_UNSUPPORTED;
   return DFLASH_OK;
 }
 
@@ -252,10 +254,17 @@ struct Probe {
   do {                                             \
     if (hipGetLastError() != hipSuccess) return DFLASH_E_HIP; \
   } while (0)
-#define GEMM_CHECK(expr)                           \
-  do {                                             \
-    if ((expr) != hipSuccess) return DFLASH_E_HIP; \
+#define GEMM_CHECK(expr)                                      \
+  do {                                                        \
+    const hipError_t e_ = (expr);                             \
+    if (e_ == hipErrorNotSupported) return DFLASH_E_UNSUPPORTED; \
+    if (e_ != hipSuccess) return DFLASH_E_HIP;                \
   } while (0)
+
+// FP8 storage of the streamed projections: W rows are K codes + 16 bytes, so the row
+// stride the epilogues step by (in T elements) is (K + 16) / 2.
+bool fp8w(const dflash_config* c) { return c->weight_format == DFLASH_WEIGHTS_FP8; }
+int wstride(const dflash_config* c, int K) { return fp8w(c) ? (K + 16) / 2 : K; }
 
 template <typename T>
 SegW<T> seg1(const void* p, int rows, int K) {
@@ -278,10 +287,10 @@ int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv
   InjectWs<T> W = carve_inject<T>(cv, c, rows);
   const int d = c->d_model, dcat = c->n_feat_layers * c->d_target;
   {
-    EpiStore<T> e{seg1<T>(w->w_fc, d, dcat), W.hf, d, STORE};
+    EpiStore<T> e{seg1<T>(w->w_fc, d, wstride(c, dcat)), W.hf, d, STORE};
     pr.begin(DFLASH_PROBE_INJECT_FC);
     GEMM_CHECK((run_gemm<T, T>(static_cast<const T*>(hidden), dcat, nullptr, rows, dcat, (d + 15) / 16, e, s,
-                               W.scratch, W.scratch_bytes)));
+                               W.scratch, W.scratch_bytes, 0, fp8w(c))));
     pr.end(DFLASH_PROBE_INJECT_FC);
   }
   rmsnorm_kernel<T><<<rows, 256, 0, s>>>(W.hf, static_cast<const T*>(w->g_fc), d, c->rms_eps, W.f, nullptr);
@@ -293,7 +302,7 @@ int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv
     e.kc[l] = static_cast<T*>(kv->k[l]);
     e.vtc[l] = static_cast<T*>(kv->vt[l]);
   }
-  e.K = d;
+  e.K = wstride(c, d);
   e.L = c->n_layers;
   e.Hkv = c->n_kv_heads;
   e.hd = c->head_dim;
@@ -305,7 +314,7 @@ int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv
   e.n_new = n_new;
   const int nvt = c->n_layers * 2 * c->n_kv_heads * c->head_dim / 16;
   pr.begin(DFLASH_PROBE_INJECT_KV);
-  GEMM_CHECK((run_gemm<T, T>(W.f, d, nullptr, rows, d, nvt, e, s, W.scratch, W.scratch_bytes)));
+  GEMM_CHECK((run_gemm<T, T>(W.f, d, nullptr, rows, d, nvt, e, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
   pr.end(DFLASH_PROBE_INJECT_KV);
   return DFLASH_OK;
 }
@@ -380,15 +389,15 @@ int post_sublayer(const dflash_config* c, const dflash_layer_weights& L, int sit
                   int K, int M, DraftWs<T>& W, const Probe& pr, int probe, hipStream_t s) {
   const int d = c->d_model;
   if (!c->use_conv) {
-    EpiStore<T> e{seg1<T>(wmat, d, K), W.x, d, ADD};
+    EpiStore<T> e{seg1<T>(wmat, d, wstride(c, K)), W.x, d, ADD};
     pr.begin(probe);
-    GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s, W.scratch, W.scratch_bytes)));
+    GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
     pr.end(probe);
     return DFLASH_OK;
   }
-  EpiStore<T> e{seg1<T>(wmat, d, K), W.uf, d, STORE};
+  EpiStore<T> e{seg1<T>(wmat, d, wstride(c, K)), W.uf, d, STORE};
   pr.begin(probe);
-  GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s, W.scratch, W.scratch_bytes)));
+  GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
   pr.end(probe);
   EpiStore<T> g{seg1<T>(L.conv_gen[site], 2 * (d / 16), d), W.delta, 2 * (d / 16), STORE};
   GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, g, s, W.scratch,
@@ -417,10 +426,11 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
                               l == 0 ? block_ids : nullptr)))
       return rc;
     EpiQKV<T> eq{static_cast<const T*>(L.w_q), static_cast<const T*>(L.w_k), static_cast<const T*>(L.w_v),
-                 d, H, Hkv, hd, std::log(static_cast<double>(c->rope_theta)), ctx_len, W.q, W.kb, W.vbt};
+                 wstride(c, d), H, Hkv, hd, std::log(static_cast<double>(c->rope_theta)), ctx_len, W.q, W.kb,
+                 W.vbt};
     pr.begin(DFLASH_PROBE_QKV);
     GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, (hq + 2 * Hkv * hd) / 16, eq, s, W.scratch,
-                               W.scratch_bytes)));
+                               W.scratch_bytes, 0, fp8w(c))));
     pr.end(DFLASH_PROBE_QKV);
     AttnArgs<T> aa{W.q, W.kb, W.vbt, static_cast<const T*>(kv->k[l]), static_cast<const T*>(kv->vt[l]), ctx_len,
                    W.part_o, W.part_ml, W.o, H, Hkv, kv->cap, W.S, 1.4426950408889634f / sqrtf(static_cast<float>(hd))};
@@ -430,18 +440,19 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
     if ((rc = post_sublayer<T, T>(c, L, 1, L.w_o, W.o, hq, M, W, pr, DFLASH_PROBE_O, s))) return rc;
     // feed-forward sublayer
     if ((rc = pre_sublayer<T>(c, L, 2, L.g_ffn, M, W, s))) return rc;
-    EpiSwiGLU<T> ef{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), d, F, W.h};
+    EpiSwiGLU<T> ef{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), wstride(c, d), F, W.h};
     pr.begin(DFLASH_PROBE_GATE_UP);
-    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, 2 * (F / 16), ef, s, W.scratch, W.scratch_bytes)));
+    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, 2 * (F / 16), ef, s, W.scratch, W.scratch_bytes, 0,
+                               fp8w(c))));
     pr.end(DFLASH_PROBE_GATE_UP);
     if ((rc = post_sublayer<T, T>(c, L, 3, L.w_down, W.h, F, M, W, pr, DFLASH_PROBE_DOWN, s))) return rc;
   }
   rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(w->g_final), d, c->rms_eps, W.ut, final_hidden);
   LAUNCH_CHECK();
   float* lg = logits ? logits : W.logits;
-  EpiLogits<T> el{{seg1<T>(w->lm_head, V, d), lg, V, STORE}};
+  EpiLogits<T> el{{seg1<T>(w->lm_head, V, wstride(c, d)), lg, V, STORE}};
   P0.begin(DFLASH_PROBE_LM_HEAD);
-  GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, V / 16, el, s, W.scratch, W.scratch_bytes)));
+  GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, V / 16, el, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
   P0.end(DFLASH_PROBE_LM_HEAD);
   const int nch = (V + kTopkChunk - 1) / kTopkChunk;
   P0.begin(DFLASH_PROBE_TOPK);
@@ -561,6 +572,10 @@ int dflash_inject_context(const dflash_config* cfg, const dflash_weights* w, con
   if ((rc = check_kv(cfg, kv, batch))) return rc;
   if (!hidden || !row_off || !pos0 || !n_new || !workspace) return DFLASH_E_INVAL;
   if (workspace_bytes < dflash_inject_workspace_bytes(cfg, n_rows)) return DFLASH_E_WORKSPACE;
+  // FP8 storage streams through kernels that address A with 32-bit byte offsets
+  if (fp8w(cfg) && static_cast<int64_t>(n_rows) * std::max<int64_t>(cfg->n_feat_layers * int64_t{cfg->d_target},
+                                                                      cfg->d_model) * 2 >= (int64_t{1} << 31))
+    return DFLASH_E_UNSUPPORTED;
   const Probe pr{probes, stream};
   if (cfg->dtype == DFLASH_BF16)
     return inject_impl<bf16_t>(cfg, w, kv, hidden, n_rows, row_off, pos0, n_new, batch, workspace, pr, stream);
@@ -578,6 +593,10 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const 
   if ((rc = check_kv(cfg, kv, batch))) return rc;
   if (!ctx_len || !block_ids || !cand_ids || !cand_logits || !final_hidden || !workspace) return DFLASH_E_INVAL;
   if (workspace_bytes < dflash_draft_workspace_bytes(cfg, batch, kv->cap)) return DFLASH_E_WORKSPACE;
+  if (fp8w(cfg) && int64_t{16} * batch *
+                           std::max<int64_t>({cfg->d_model, int64_t{cfg->n_heads} * cfg->head_dim, cfg->d_ffn}) * 2 >=
+                       (int64_t{1} << 31))
+    return DFLASH_E_UNSUPPORTED;
   if (cfg->dtype == DFLASH_BF16)
     return draft_impl<bf16_t>(cfg, w, kv, ctx_len, block_ids, batch, cand_ids, cand_logits, final_hidden, logits,
                               workspace, probes, stream);
@@ -692,6 +711,14 @@ int dflash_verify_sampled(const int32_t* draft, const int32_t* q_ids, int64_t q_
     LAUNCH_CHECK();
     bonus_kernel<float><<<batch, 256, 0, stream>>>(T, vocab, k2, n_draft, q_ids, qs, q_probs, W.sel, bonus);
   }
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+int dflash_quantize_fp8(const void* w, int32_t rows, int32_t cols, void* out, hipStream_t stream) {
+  if (!w || !out || rows <= 0 || cols <= 0 || cols % 64) return DFLASH_E_INVAL;
+  if (reinterpret_cast<uintptr_t>(out) % 16) return DFLASH_E_INVAL;
+  quantize_fp8_kernel<<<rows, 256, 0, stream>>>(static_cast<const bf16_t*>(w), cols, static_cast<uint8_t*>(out));
   LAUNCH_CHECK();
   return DFLASH_OK;
 }

@@ -83,4 +83,48 @@ __global__ __launch_bounds__(256) void conv_apply_kernel(const float* __restrict
   }
 }
 
+// ------------------------------------------------------------------ FP8 weight storage
+
+// E4M3 code of the value nearest to x (ties to the even mantissa), magnitudes saturating
+// at 448; zero encodes as 0.  Below 2^-6 the grid is the multiples of 2^-9 (code = the
+// multiple, 8 being the smallest normal); above, 3 mantissa bits rounded from float32's
+// 23, a carry moving into the exponent field.
+__device__ __forceinline__ uint32_t e4m3_code(float x) {
+  const uint32_t sign = __float_as_uint(x) >> 31;
+  const float a = fminf(fabsf(x), 448.f);
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = static_cast<uint32_t>(rintf(a * 512.f));
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t e = (b >> 23) - 120u;          // biased E4M3 exponent, 1 .. 15
+    const uint32_t keep = (b >> 20) & 7u, rem = b & 0xFFFFFu;
+    const uint32_t up = (rem > 0x80000u || (rem == 0x80000u && (keep & 1u))) ? 1u : 0u;
+    code = (e << 3) + keep + up;
+    code = code > 0x7Eu ? 0x7Eu : code;
+  }
+  return code ? (code | (sign << 7)) : 0u;
+}
+
+// One row per work-group: row scale = max |w| / 448, codes of w / scale, then the scale
+// and 12 zero bytes (row stride cols + 16 bytes).
+__global__ __launch_bounds__(256) void quantize_fp8_kernel(const bf16_t* __restrict__ w, int cols,
+                                                           uint8_t* __restrict__ out) {
+  __shared__ float red[4];
+  const bf16_t* row = w + static_cast<size_t>(blockIdx.x) * cols;
+  uint8_t* o = out + static_cast<size_t>(blockIdx.x) * (cols + 16);
+  float amax = 0.f;
+  for (int j = threadIdx.x; j < cols; j += 256) amax = fmaxf(amax, fabsf(bf2f(row[j])));
+#pragma unroll
+  for (int k = 32; k > 0; k >>= 1) amax = fmaxf(amax, __shfl_xor(amax, k, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  const float scale = amax / 448.f;
+  for (int j = threadIdx.x; j < cols; j += 256)
+    o[j] = scale > 0.f ? static_cast<uint8_t>(e4m3_code(bf2f(row[j]) / scale)) : uint8_t{0};
+  if (threadIdx.x < 4)
+    reinterpret_cast<float*>(o + cols)[threadIdx.x] = threadIdx.x == 0 ? scale : 0.f;
+}
+
 }  // namespace dflash

@@ -172,6 +172,105 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
   epilogue_tile(epi, &tile[0][0], TW + 1, 0, ROWS, vt0, NT, M, rinfo);
 }
 
+// FP8-weight variant (one drafted block: M <= 16, A in bf16).  W rows hold E4M3 codes
+// followed by the row's float32 scale.  Each lane loads 16 codes, k = 16g .. 16g+15 of a
+// 64-wide k group, and widens them to two bf16 fragments when the stage is consumed (not
+// when it is loaded, so the loads of the next stage stay in flight); the A fragments
+// follow the same k order (k-step 2u takes k 16g .. 16g+7 of group u, k-step 2u+1 takes
+// 16g+8 .. 16g+15), so each product pairs equal k.  The row scale multiplies the
+// accumulator before the fixed-order reduction.
+template <typename T, int NT, int NW, int U, class Epi>
+__global__ __launch_bounds__(64 * NW) void gemm_skinny_w8_kernel(const T* __restrict__ A, int lda,
+                                                                 const int32_t* __restrict__ arows, int M, int K,
+                                                                 Epi epi) {
+  typedef Frag<T> F;
+  typedef typename F::type frag_t;
+  static_assert(U % 2 == 0, "k-steps come in pairs");
+  constexpr int TW = 16 * NT, UG = U / 2;
+  __shared__ float red[NW][NT * 256];
+  __shared__ float tile[16][TW + 1];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int vt0 = blockIdx.x * NT;
+  const int kw = K / NW;
+  const int k0 = wave * kw;
+  __amdgpu_buffer_rsrc_t rw[NT];
+  uint32_t vw[NT];
+  float sc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const T* base;
+    uint32_t bytes;
+    epi.wseg(vt0 + nt, base, bytes);
+    rw[nt] = make_rsrc(base, bytes);
+    const T* p = epi.wrow(vt0 + nt, r16);
+    vw[nt] = p ? static_cast<uint32_t>((p - base) * sizeof(T)) + g * 16 + k0 : bytes;
+    sc[nt] = fp8_row_scale(p, K);
+  }
+  const int ar = r16 < M ? (arows ? arows[r16] : r16) : (arows ? arows[0] : 0);
+  const T* ap = A + static_cast<size_t>(ar) * lda + g * 16 + k0;
+
+  f32x4_t acc[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) acc[nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  constexpr int STEP = 32 * U;   // K elements per register stage
+  auto load = [&](u32x4_t (&w)[UG][NT], frag_t (&a)[U], int kb) {
+#pragma unroll
+    for (int u = 0; u < UG; ++u) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) w[u][nt] = __builtin_amdgcn_raw_buffer_load_b128(rw[nt], vw[nt] + 64 * u, kb, 0);
+      a[2 * u] = F::load(ap + kb + 64 * u);
+      a[2 * u + 1] = F::load(ap + kb + 64 * u + 8);
+    }
+  };
+  auto mma = [&](u32x4_t (&w)[UG][NT], frag_t (&a)[U]) {
+#pragma unroll
+    for (int u = 0; u < UG; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        frag_t lo, hi;
+        fp8x16_to_bf16(w[u][nt], lo, hi);
+        acc[nt] = F::mma(acc[nt], a[2 * u], lo);
+        acc[nt] = F::mma(acc[nt], a[2 * u + 1], hi);
+      }
+  };
+
+  const int nst = kw / STEP;
+  u32x4_t wc[UG][NT];
+  frag_t ac[U];
+  load(wc, ac, 0);
+  for (int st = 1; st < nst; ++st) {
+    u32x4_t wn[UG][NT];
+    frag_t an[U];
+    load(wn, an, st * STEP);
+    mma(wc, ac);
+#pragma unroll
+    for (int u = 0; u < UG; ++u)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) wc[u][nt] = wn[u][nt];
+#pragma unroll
+    for (int u = 0; u < U; ++u) ac[u] = an[u];
+  }
+  mma(wc, ac);
+
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][(nt * 64 + lane) * 4 + i] = acc[nt][i] * sc[nt];
+  __syncthreads();
+  for (int e = threadIdx.x; e < NT * 256; e += 64 * NW) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s += red[w][e];
+    const int i = e & 3, l = (e >> 2) & 63, nt = e >> 8;
+    tile[4 * (l >> 4) + i][nt * 16 + (l & 15)] = s;
+  }
+  __shared__ typename Epi::Row rinfo[16];
+  epilogue_tile(epi, &tile[0][0], TW + 1, 0, 16, vt0, NT, M, rinfo);
+}
+
 // ---------------------------------------------------------------------------------
 // tiled GEMM (M > 64)
 // ---------------------------------------------------------------------------------
@@ -350,7 +449,7 @@ __device__ __forceinline__ void pipe_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <typename T, int BM, int BN, int NS, class Epi>
+template <typename T, int BM, int BN, int NS, class Epi, bool W8>
 __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A, int lda,
                                                        const int32_t* __restrict__ arows, int M, int K, Epi epi,
                                                        int tiles_m, int kslice, float* __restrict__ partial,
@@ -360,10 +459,11 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
   static_assert(sizeof(T) == 2, "bf16 operands");
   static_assert(NS >= 2 && NS <= 4, "ring of 2..4 slots");
   constexpr int TM = BM / 32, TN = BN / 32;        // 16x16 tiles per wave
-  constexpr int LA = BM / 32, LB = BN / 32;        // direct loads per thread per slab
+  // direct loads per thread per slab (W rows of 64 E4M3 codes are half as long)
+  constexpr int LA = BM / 32, LB = W8 ? BN / 64 : BN / 32;
   constexpr int LPS = LA + LB;
-  constexpr int STAGE = (BM + BN) * 64;            // elements per slot
-  constexpr int EPR = 32;                          // epilogue rows per LDS pass
+  constexpr int STAGE = (BM + (W8 ? BN / 2 : BN)) * 64;      // T elements per slot
+  constexpr int EPR = 32 * (BN + 1) * 4 <= STAGE * 2 ? 32 : 16;   // epilogue rows per LDS pass
   static_assert(EPR * (BN + 1) * 4 <= STAGE * 2, "epilogue pass must fit in one slot");
   static_assert((NS - 2) * LPS < 64, "vmcnt range");
 
@@ -377,8 +477,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
   // this lane's source chunk for each of its direct loads: LDS block (8 rows) j*4 + wave,
   // row block*8 + lane/8, position lane%8 <- chunk (lane%8) ^ ((row >> 1) & 7).
   // A: byte offsets from A (rows past M clamped); W: row pointers (past the end: row 0).
+  // W8: 16 rows of 4 chunks per LDS block, chunk c of row r at position c ^ ((r >> 2) & 3).
   uint32_t aoff[LA];
-  const T* wsrc[LB];
+  const char* wsrc[LB];
   const T* w0 = epi.wrow(vt0, 0);
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
@@ -389,10 +490,17 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
   }
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
-    const int row = (j * 4 + wave) * 8 + (lane >> 3);
-    const int ck = (lane & 7) ^ ((row >> 1) & 7);
-    const T* wr = epi.wrow(vt0 + row / 16, row % 16);
-    wsrc[j] = (wr ? wr : w0) + ck * 8;
+    if constexpr (W8) {
+      const int row = (j * 4 + wave) * 16 + (lane >> 2);
+      const int ck = (lane & 3) ^ ((row >> 2) & 3);
+      const T* wr = epi.wrow(vt0 + row / 16, row % 16);
+      wsrc[j] = reinterpret_cast<const char*>(wr ? wr : w0) + ck * 16;
+    } else {
+      const int row = (j * 4 + wave) * 8 + (lane >> 3);
+      const int ck = (lane & 7) ^ ((row >> 1) & 7);
+      const T* wr = epi.wrow(vt0 + row / 16, row % 16);
+      wsrc[j] = reinterpret_cast<const char*>((wr ? wr : w0) + ck * 8);
+    }
   }
   auto issue = [&](const T* slot, int k0) {
     const uint32_t base = lds_addr(slot);
@@ -400,7 +508,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
 #pragma unroll
     for (int j = 0; j < LA; ++j) dma16(ak + aoff[j], base + (j * 4 + wave) * 1024);
 #pragma unroll
-    for (int j = 0; j < LB; ++j) dma16(wsrc[j] + k0, base + (BM / 8 + j * 4 + wave) * 1024);
+    for (int j = 0; j < LB; ++j) dma16(wsrc[j] + k0 * (W8 ? 1 : sizeof(T)), base + (BM / 8 + j * 4 + wave) * 1024);
   };
 
   f32x4_t acc[TM][TN];
@@ -413,13 +521,28 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
     const T* As = slot + (wm * (BM / 2) + r16) * 64;
     const T* Bs = slot + (BM + wn * (BN / 2) + r16) * 64;
     frag_t af[2][TM], bf[2][TN];
+    if constexpr (W8) {
+      // k-step ks of lane group g covers k 16g + 8ks .. +7 (the order of the widened codes)
+      const uint8_t* Bs8 = reinterpret_cast<const uint8_t*>(slot + BM * 64) + (wn * (BN / 2) + r16) * 64 +
+                           ((g ^ ((r16 >> 2) & 3)) * 16);
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int pos = ((4 * ks + g) ^ sw) * 8;
+      for (int ks = 0; ks < 2; ++ks) {
+        const int pos = ((2 * g + ks) ^ sw) * 8;
 #pragma unroll
-      for (int i = 0; i < TM; ++i) af[ks][i] = F::load(As + i * 16 * 64 + pos);
+        for (int i = 0; i < TM; ++i) af[ks][i] = F::load(As + i * 16 * 64 + pos);
+      }
 #pragma unroll
-      for (int j = 0; j < TN; ++j) bf[ks][j] = F::load(Bs + j * 16 * 64 + pos);
+      for (int j = 0; j < TN; ++j)
+        fp8x16_to_bf16(*reinterpret_cast<const u32x4_t*>(Bs8 + j * 16 * 64), bf[0][j], bf[1][j]);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int pos = ((4 * ks + g) ^ sw) * 8;
+#pragma unroll
+        for (int i = 0; i < TM; ++i) af[ks][i] = F::load(As + i * 16 * 64 + pos);
+#pragma unroll
+        for (int j = 0; j < TN; ++j) bf[ks][j] = F::load(Bs + j * 16 * 64 + pos);
+      }
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
@@ -450,6 +573,14 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
     }
   }
   pipe_barrier<0>();   // drain the tail re-reads before the slots are reused
+  if constexpr (W8) {   // row scales of this lane's columns
+#pragma unroll
+    for (int j = 0; j < TN; ++j) {
+      const float sc = fp8_row_scale(epi.wrow(vt0 + wn * (BN / 32) + j, r16), K);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) acc[i][j] *= sc;
+    }
+  }
 
   if (partial) {
     float* pz = partial + static_cast<size_t>(blockIdx.y) * M * ldp;
@@ -645,32 +776,62 @@ static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks,
   }
 }
 
-template <typename T, int BM, int BN, int NS, class Epi>
+template <typename T, int BM, int BN, int NS, bool W8, class Epi>
 static hipError_t launch_pipe_shape(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
                                     const Epi& epi, int ks, float* scratch, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (n_vtiles * 16 + BN - 1) / BN, ldp = tn * BN;
-  gemm_pipe_kernel<T, BM, BN, NS, Epi><<<dim3(tm * tn, ks), 256, 0, s>>>(A, lda, arows, M, K, epi, tm, K / ks,
-                                                                        ks > 1 ? scratch : nullptr, ldp);
+  gemm_pipe_kernel<T, BM, BN, NS, Epi, W8><<<dim3(tm * tn, ks), 256, 0, s>>>(A, lda, arows, M, K, epi, tm, K / ks,
+                                                                            ks > 1 ? scratch : nullptr, ldp);
   if (ks > 1) launch_splitk_epilogue(scratch, M, ldp, ks, n_vtiles, epi, s);
   return hipGetLastError();
 }
 
-template <typename T, class Epi>
+template <typename T, bool W8, class Epi>
 static hipError_t launch_big(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
                              hipStream_t s, float* scratch, size_t scratch_bytes) {
   BigPlan p = big_plan(M, K, n_vtiles);
   const size_t ldp = static_cast<size_t>((n_vtiles * 16 + p.bn - 1) / p.bn) * p.bn;
   if (p.ks > 1 && (!scratch || scratch_bytes < static_cast<size_t>(p.ks) * M * ldp * sizeof(float))) p.ks = 1;
-  if (p.bm == 64) return launch_pipe_shape<T, 64, 128, 3>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
-  if (p.bm == 256) return launch_pipe_shape<T, 256, 128, 3>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
-  return launch_pipe_shape<T, 128, 128, 2>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 64) return launch_pipe_shape<T, 64, 128, 3, W8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 256) return launch_pipe_shape<T, 256, 128, 3, W8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  return launch_pipe_shape<T, 128, 128, 2, W8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+}
+
+template <typename T, int NT, int NW, int U, class Epi>
+static bool try_skinny_w8(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
+                          hipStream_t s) {
+  if (K % (NW * 32 * U) || n_vtiles % NT) return false;
+  gemm_skinny_w8_kernel<T, NT, NW, U, Epi><<<n_vtiles / NT, 64 * NW, 0, s>>>(A, lda, arows, M, K, epi);
+  return true;
+}
+
+template <typename T, class Epi>
+static hipError_t launch_skinny_w8(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
+                                   const Epi& epi, hipStream_t s) {
+  const bool wide = n_vtiles / 2 >= 192 && K <= 8192;
+  constexpr int NTP = Epi::PX ? 2 : 1;
+  bool ok = false;
+  // E4M3 rows are half as long: K over two waves gives each wave as many stages as the
+  // bf16 kernel's four
+  if (wide || Epi::PX) ok = try_skinny_w8<T, 2, 2, 16>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok && (wide || Epi::PX)) ok = try_skinny_w8<T, 2, 4, 16>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok && !Epi::PX) ok = try_skinny_w8<T, 1, 4, 16>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok) ok = try_skinny_w8<T, NTP, 4, 8>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok) ok = try_skinny_w8<T, NTP, 4, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok) ok = try_skinny_w8<T, NTP, 1, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
+  if (!ok) return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 // n_vtiles: number of virtual 16-column tiles (multiple of 2 when Epi::PX == 1).
 // K: multiple of 64.  scratch: split-K partials (>= splitk_scratch_bytes, or nullptr: no split).
+// w8: W in FP8 storage (E4M3 rows with a float32 scale; the epilogue's row stride covers
+// the K codes and the 16-byte scale field).  Supported with bf16 A, K a multiple of 64
+// and the pipelined kernel's 2 GiB A span, through gemm_pipe or gemm_skinny_w8 (M <= 16).
 template <typename T, typename AS, class Epi>
 static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, int K, int n_vtiles, const Epi& epi,
-                           hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0, size_t a_rows = 0) {
+                           hipStream_t s, float* scratch = nullptr, size_t scratch_bytes = 0, size_t a_rows = 0,
+                           bool w8 = false) {
   if (M <= 0 || n_vtiles <= 0) return hipSuccess;
   if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value) {
     // gemm_pipe addresses A with 32-bit byte offsets: the rows A spans (M, or the a_rows of
@@ -678,9 +839,16 @@ static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, in
     const size_t span = arows ? a_rows : static_cast<size_t>(M);
     // (at M <= 16 only for long K, where its split-K streams the weights faster than
     // gemm_skinny: 16 x 4096 x 20480 cold, 44 -> 39 us)
-    if ((M > 16 || K >= 16384) && K % 64 == 0 && span > 0 && span * lda * sizeof(T) < (size_t{1} << 31))
-      return launch_big<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
+    const bool pipe_ok = K % 64 == 0 && span > 0 && span * lda * sizeof(T) < (size_t{1} << 31);
+    if (w8) {
+      if (M <= 16 && K % 64 == 0) return launch_skinny_w8<T, Epi>(A, lda, arows, M, K, n_vtiles, epi, s);
+      if (pipe_ok) return launch_big<T, true, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
+      return hipErrorNotSupported;
+    }
+    if ((M > 16 || K >= 16384) && pipe_ok)
+      return launch_big<T, false, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
   }
+  if (w8) return hipErrorNotSupported;
   if (M <= 16) return launch_skinny<T, AS, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 32) return launch_skinny<T, AS, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 64) return launch_skinny<T, AS, 4>(A, lda, arows, M, K, n_vtiles, epi, s);

@@ -62,6 +62,13 @@ extern "C" {
 #define DFLASH_F32   0
 #define DFLASH_BF16  1
 
+/* weight storage of the streamed projections (dflash_config.weight_format) */
+#define DFLASH_WEIGHTS_DTYPE 0     /* in the storage type dtype                              */
+#define DFLASH_WEIGHTS_FP8   1     /* E4M3 codes with a float32 scale per row (bf16 only)    */
+
+/* bytes of one row of a [rows, cols] matrix in FP8 storage */
+#define DFLASH_FP8_ROW_BYTES(cols) ((size_t)(cols) + 16)
+
 /* path choice */
 #define DFLASH_PATH_GREEDY 0       /* greedy walk over the pair scores (the method's rule) */
 #define DFLASH_PATH_EXACT  1       /* maximum total score (dynamic programming)             */
@@ -88,6 +95,7 @@ typedef struct dflash_config {
   int32_t use_gate;       /* 0/1: context gate in the Path Selector                           */
   float   rms_eps;        /* RMSNorm epsilon (1e-6)                                           */
   float   rope_theta;     /* rotary base (1e6)                                                */
+  int32_t weight_format;  /* DFLASH_WEIGHTS_DTYPE or DFLASH_WEIGHTS_FP8 (see dflash_weights)   */
 } dflash_config;
 
 typedef struct dflash_layer_weights {
@@ -105,6 +113,15 @@ typedef struct dflash_layer_weights {
   const void* conv_w1[DFLASH_CONV_SITES];   /* [d] static tap on the previous row (use_conv)  */
 } dflash_layer_weights;
 
+/* Weights.  Matrices are row-major [rows, cols] in the storage type, except under
+ * weight_format == DFLASH_WEIGHTS_FP8 ("DFlash 2 ...", layer/technology table: draft
+ * quantization enabled; bf16 drafters only), where the streamed projections w_fc, w_q,
+ * w_k, w_v, w_o, w_gate, w_up, w_down and lm_head are in FP8 storage: row n occupies
+ * DFLASH_FP8_ROW_BYTES(cols) = cols + 16 bytes at byte offset n * (cols + 16), holding
+ * cols E4M3 codes (the OCP 8-bit format with 4 exponent bits, bias 7, no infinities),
+ * then the row's float32 scale, then 12 zero bytes; the row stands for code value times
+ * scale.  dflash_quantize_fp8 writes that layout.  The embedding, conv generators and
+ * taps, Path Selector factors and norm gains stay in the storage type. */
 typedef struct dflash_weights {
   const void* embed;      /* [V, d] token embedding shared with the target                    */
   const void* lm_head;    /* [V, d] LM head shared with the target                            */
@@ -316,6 +333,17 @@ int dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batc
                    int32_t* ctx_len, int32_t* pos0, int32_t* n_new, int32_t* block_ids, hipStream_t stream);
 
 /* Workspace sizes in bytes (0 when the arguments are invalid). */
+/* FP8 storage of one weight matrix (see dflash_weights).
+ *
+ * w   : device bf16 [rows, cols], row-major.
+ * out : device, rows * DFLASH_FP8_ROW_BYTES(cols) bytes, 16-byte aligned; written.
+ * Per row: scale = (largest |w|) / 448, code = the E4M3 value nearest to w / scale (both
+ * divisions in float32; ties to the even code; magnitudes above 448 saturate); a row of
+ * zeros gets scale 0 and codes 0.  rows > 0 and cols a positive multiple of 64, else
+ * DFLASH_E_INVAL.  Enqueued on stream; no workspace.
+ */
+int dflash_quantize_fp8(const void* w, int32_t rows, int32_t cols, void* out, hipStream_t stream);
+
 size_t dflash_inject_workspace_bytes(const dflash_config* cfg, int32_t n_rows);
 size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t cap);
 size_t dflash_path_workspace_bytes(const dflash_config* cfg, int32_t batch);

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     lib = ctypes.CDLL(D.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -169,3 +169,17 @@ def test_sampling_calls_reject_bad_arguments():
     assert bad(u_bonus=None) == D.DFLASH_E_INVAL
     assert bad(nb=ws_v - 1) == D.DFLASH_E_WORKSPACE
     assert bad(batch=0) == D.DFLASH_E_INVAL
+
+
+def test_fp8_storage_arguments():
+    cfg = D.make_config(synth.workload("t_f32").dims, fp8=True)
+    assert D.dflash_check_config(cfg) == D.DFLASH_E_UNSUPPORTED
+    cfg = D.make_config(synth.workload("t_small").dims, fp8=True)
+    assert D.dflash_check_config(cfg) == D.DFLASH_OK
+    cfg.weight_format = 2
+    assert D.dflash_check_config(cfg) == D.DFLASH_E_INVAL
+    q = D.dflash_quantize_fp8
+    assert _status(q, FAKE, 4, 100, FAKE, 1) == D.DFLASH_E_INVAL       # cols not a multiple of 64
+    assert _status(q, FAKE, 0, 64, FAKE, 1) == D.DFLASH_E_INVAL
+    assert _status(q, None, 4, 64, FAKE, 1) == D.DFLASH_E_INVAL
+    assert _status(q, FAKE, 4, 64, FAKE + 8, 1) == D.DFLASH_E_INVAL    # output not 16-byte aligned

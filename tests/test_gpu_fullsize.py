@@ -38,9 +38,10 @@ def ws(n):
 _STATE = {}
 
 
-def drafter_for(name, conv_scale):
+def drafter_for(name, conv_scale, fp8=False):
     """Weights, oracle model and device drafter for a workload (shared by workloads of equal
-    shape; a different conv scale redraws only the conv tensors)."""
+    shape; a different conv scale redraws only the conv tensors; fp8 selects FP8 storage of
+    the streamed projections on both sides)."""
     wl = synth.workload(name)
     key = (wl.dims.use_conv, wl.dims.use_gate)
     if key not in _STATE:
@@ -48,32 +49,36 @@ def drafter_for(name, conv_scale):
         torch.cuda.empty_cache()
         _STATE[key] = {"W": synth.make_weights(wl.dims, 77, conv_scale=conv_scale), "scale": conv_scale}
     st = _STATE[key]
-    if st["scale"] != conv_scale or "dr" not in st:
+    if st["scale"] != conv_scale or "dr" not in st or st.get("fp8") != fp8:
         if st["scale"] != conv_scale:
             conv = [n for n in st["W"] if ".conv" in n]
             st["W"].update(synth.make_weights(wl.dims, 77, conv_scale=conv_scale, names=conv))
             st["scale"] = conv_scale
         st.pop("dr", None)
         torch.cuda.empty_cache()
-        st["m"] = oracle.Model(wl.dims, st["W"])
-        st["dr"] = D.Drafter(wl.dims, st["W"])
+        st["m"] = oracle.Model(wl.dims, st["W"], fp8=fp8)
+        st["dr"] = D.Drafter(wl.dims, st["W"], fp8=fp8)
+        st["fp8"] = fp8
     return wl, (st["W"], st["m"], st["dr"])
 
 
 # (workload, sampled sequences, conv scale).  c5 runs at the workload's own random-init
 # scale and at a milder one; at its own scale the conv corrections are O(1.3) per channel
 # and the computation is ill-conditioned (the tolerance follows the measured conditioning).
-CASES = [("c2", (0,), "config"), ("c3", (0, 31), "config"), ("c4", (3,), "config"),
-         ("c5", (0, 15), "config"), ("c5", (15,), "mild")]
+# FP8 storage cases: c2 (one block: weight-streaming kernels) and c4 (4 blocks: the
+# pipelined kernel at 64 rows).
+CASES = [("c2", (0,), "config", False), ("c3", (0, 31), "config", False), ("c4", (3,), "config", False),
+         ("c5", (0, 15), "config", False), ("c5", (15,), "mild", False), ("c2", (0,), "config", True),
+         ("c4", (1,), "config", True)]
 
 
-@pytest.mark.parametrize("name,sample,conv_scale", CASES)
-def test_fullsize_step(name, sample, conv_scale):
-    wl, (W, m, dr) = drafter_for(name, conv_scale)
+@pytest.mark.parametrize("name,sample,conv_scale,fp8", CASES)
+def test_fullsize_step(name, sample, conv_scale, fp8):
+    wl, (W, m, dr) = drafter_for(name, conv_scale, fp8)
     dims = wl.dims
     B, cap = wl.batch, wl.cap
     ctx = np.asarray(wl.ctx_lens, dtype=np.int32)
-    say(f"fullsize {name} (conv {conv_scale}): batch {B}, contexts {ctx.min()}..{ctx.max()}, sampled {sample}")
+    say(f"fullsize {name} (conv {conv_scale}{', fp8 weights' if fp8 else ''}): batch {B}, contexts {ctx.min()}..{ctx.max()}, sampled {sample}")
     gen = torch.Generator(device="cuda")
     gen.manual_seed(123)
     cache = D.KVCache(dims, B, cap, fill=None)
