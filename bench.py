@@ -51,6 +51,9 @@ def parse():
     ap.add_argument("--fp8-steps", type=int, default=20,
                     help="also time this many steps with the streamed projections in FP8 storage (E4M3 codes, "
                          "a float32 scale per row) and report them apart (bf16 workloads)")
+    ap.add_argument("--block-sizes", default="8,5",
+                    help="also time the step with these smaller drafted blocks (dynamic block size; comma list, "
+                         "empty to skip)")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the step, run a plain fp32 elementwise copy (torch.neg) of this many MiB "
                          "three times: a kernel of known traffic that calibrates HBM byte counters")
@@ -464,6 +467,38 @@ def main():
                "weight_bytes_on_device": int(dr8.nbytes())}
         del dr8
 
+    smaller = {}
+    for bs in [int(x) for x in args.block_sizes.split(",") if x.strip()]:
+        if not 2 <= bs <= 16:
+            continue
+        drb = D.Drafter(dims, dr.t, block_size=bs)
+        Tb = T[:, :bs].contiguous()
+        nb_vb = D.dflash_verify_workspace_bytes(B, bs - 1, dims.vocab)
+        ws_vb = torch.empty(nb_vb, dtype=torch.uint8, device="cuda")
+        idx_b = torch.zeros((B, bs - 1), dtype=torch.int32, device="cuda")
+        ids_b = torch.zeros((B, bs - 1), dtype=torch.int32, device="cuda")
+
+        def step_b():
+            D.dflash_inject_context(drb.cfg, drb.w, cache.kv, new_hid, 16 * B, row_off, pos0, n_new, B, ws_i, nb_i)
+            D.dflash_draft_block(drb.cfg, drb.w, cache.kv, ctx_t, ids_t, B, ci, cl, fh, None, ws_d, nb_d)
+            D.dflash_select_path(drb.cfg, drb.w, ci, cl, fh, ids_t, 1, D.DFLASH_PATH_GREEDY, B, idx_b, ids_b, None,
+                                 ws_p, nb_p)
+            D.dflash_verify(ids_b, Tb, tdt, B, bs - 1, dims.vocab, acc, bon, ws_vb, nb_vb)
+
+        for _ in range(3):
+            step_b()
+        torch.cuda.synchronize()
+        nsteps = max(1, args.steps // 2)
+        start.record()
+        for _ in range(nsteps):
+            step_b()
+        stop.record()
+        torch.cuda.synchronize()
+        msb = start.elapsed_time(stop) / nsteps
+        log(f"[bench] block size {bs}: {msb:.3f} ms/step")
+        smaller[str(bs)] = {"steps": nsteps, "ms_per_step": round(msb, 4), "blocks_per_s": round(B * 1000.0 / msb, 2)}
+        del drb
+
     cycle = None
     if args.cycles > 0:
         cycle = run_cycles(args.cycles, D, torch, np, synth, wl, dr, new_hid, row_off, tdt, log)
@@ -507,6 +542,8 @@ def main():
         out["sampled"] = sampled
     if fp8 is not None:
         out["fp8_weights"] = fp8
+    if smaller:
+        out["smaller_blocks"] = smaller
     if cycle is not None:
         out["cycle"] = cycle
     print(json.dumps(out), flush=True)

@@ -35,6 +35,7 @@ DFLASH_PATH_GREEDY = 0
 DFLASH_PATH_EXACT = 1
 MAX_LAYERS = 16
 CONV_SITES = 4
+BLOCK = 16
 PROBES = ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv")
 N_PROBES = len(PROBES)
 
@@ -64,7 +65,7 @@ class dflash_config(ctypes.Structure):
                 ("head_dim", _i32), ("d_ffn", _i32), ("n_layers", _i32), ("n_feat_layers", _i32),
                 ("d_target", _i32), ("vocab", _i32), ("ps_dim", _i32), ("ps_rank", _i32),
                 ("use_conv", _i32), ("use_gate", _i32), ("rms_eps", ctypes.c_float),
-                ("rope_theta", ctypes.c_float), ("weight_format", _i32)]
+                ("rope_theta", ctypes.c_float), ("weight_format", _i32), ("block_size", _i32)]
 
 
 class dflash_layer_weights(ctypes.Structure):
@@ -302,10 +303,12 @@ class Probes:
 
 # ------------------------------------------------------------------ memory helpers (allocation / layout only)
 
-def make_config(dims, fp8: bool = False) -> dflash_config:
+def make_config(dims, fp8: bool = False, block_size: Optional[int] = None) -> dflash_config:
     """A ``dflash_config`` from an object with the attributes of ``synth.Dims``; ``fp8``
-    selects FP8 storage of the streamed projections."""
+    selects FP8 storage of the streamed projections, ``block_size`` the rows of the drafted
+    block (default: the full block of 16)."""
     return dflash_config(weight_format=DFLASH_WEIGHTS_FP8 if fp8 else DFLASH_WEIGHTS_DTYPE,
+        block_size=block_size or getattr(dims, "block", BLOCK),
         dtype=DFLASH_BF16 if dims.dtype == "bf16" else DFLASH_F32, d_model=dims.d, n_heads=dims.n_heads,
         n_kv_heads=dims.n_kv_heads, head_dim=dims.head_dim, d_ffn=dims.d_ffn, n_layers=dims.n_layers,
         n_feat_layers=dims.n_feat_layers, d_target=dims.d_target, vocab=dims.vocab, ps_dim=dims.ps_dim,
@@ -340,7 +343,8 @@ class Drafter:
     ``fp8=True`` the streamed projections are uploaded in bf16 and turned into FP8
     storage (E4M3 rows with a float32 scale) by ``dflash_quantize_fp8``."""
 
-    def __init__(self, dims, weights: Dict[str, "object"], device: str = "cuda", fp8: bool = False):
+    def __init__(self, dims, weights: Dict[str, "object"], device: str = "cuda", fp8: bool = False,
+                 block_size: Optional[int] = None):
         import torch
         self.dims = dims
         self.fp8 = fp8
@@ -355,7 +359,7 @@ class Drafter:
                 torch.cuda.synchronize()
                 t = q
             self.t[k] = t
-        self.cfg = make_config(dims, fp8)
+        self.cfg = make_config(dims, fp8, block_size)
         st = dflash_check_config(self.cfg)
         if st != DFLASH_OK:
             raise DflashError("dflash_check_config", st)

@@ -49,6 +49,7 @@ struct AttnArgs {
   float* part_ml;    // [B][Hkv][S][G][16][2]
   T* out;            // [B*16][H*hd]             (S == 1)
   int H, Hkv, cap, S;
+  int bs;            // block rows that are keys (dynamic block size); rows >= bs are padding
   float scale_log2;  // log2(e) / sqrt(hd)
 };
 
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       vf[dt] = lg < 2 ? F::load(a.vbt + (kv_base * HD + dt * 16 + r16) * 16 + 8 * lg) : F::zero();
-    slab(kf, vf, 16);
+    slab(kf, vf, a.bs);   // padding rows of a smaller block are no keys
   }
 
   lsum += __shfl_xor(lsum, 16, 64);

@@ -62,6 +62,7 @@ int check_config(const dflash_config* c) {
   if (c->ps_dim % 64 || c->ps_rank > 256) return DFLASH_E_UNSUPPORTED;
   if (c->weight_format != DFLASH_WEIGHTS_DTYPE && c->weight_format != DFLASH_WEIGHTS_FP8) return DFLASH_E_INVAL;
   if (c->weight_format == DFLASH_WEIGHTS_FP8 && c->dtype != DFLASH_BF16) return DFLASH_E_UNSUPPORTED;
+  if (c->block_size < 1 || c->block_size > DFLASH_BLOCK) return DFLASH_E_INVAL;
   return DFLASH_OK;
 }
 
@@ -433,7 +434,8 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
                                W.scratch_bytes, 0, fp8w(c))));
     pr.end(DFLASH_PROBE_QKV);
     AttnArgs<T> aa{W.q, W.kb, W.vbt, static_cast<const T*>(kv->k[l]), static_cast<const T*>(kv->vt[l]), ctx_len,
-                   W.part_o, W.part_ml, W.o, H, Hkv, kv->cap, W.S, 1.4426950408889634f / sqrtf(static_cast<float>(hd))};
+                   W.part_o, W.part_ml, W.o, H, Hkv, kv->cap, W.S, c->block_size,
+                   1.4426950408889634f / sqrtf(static_cast<float>(hd))};
     pr.begin(DFLASH_PROBE_ATTN);
     GEMM_CHECK(run_attention<T>(c, aa, B, s));
     pr.end(DFLASH_PROBE_ATTN);
@@ -473,8 +475,8 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
               const float* uniforms = nullptr, float* path_q = nullptr) {
   Carver cv(ws);
   PathWs W = carve_path<T>(cv, c, B);
-  const int d = c->d_model, PD = c->ps_dim, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
-  path_tokens_kernel<<<B, 256, 0, s>>>(cand_ids, block_ids, n_fixed, W.tokens);
+  const int d = c->d_model, PD = c->ps_dim, P = c->block_size - n_fixed, Tn = 16 * P + n_fixed;
+  path_tokens_kernel<<<B, 256, 0, s>>>(cand_ids, block_ids, n_fixed, P, W.tokens);
   LAUNCH_CHECK();
   {
     SegW<T> sw{};
@@ -497,13 +499,13 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
   const size_t smem = 2 * 16 * (c->ps_rank + 1) * sizeof(float);
   path_scores_kernel<T><<<dim3(P, B), 256, smem, s>>>(W.z, c->use_gate ? W.gamma : nullptr,
                                                       static_cast<const T*>(w->ps_u), static_cast<const T*>(w->ps_v),
-                                                      PD, c->ps_rank, n_fixed, W.S, pair_scores);
+                                                      PD, c->ps_rank, n_fixed, P, W.S, pair_scores);
   LAUNCH_CHECK();
   if (uniforms)
-    path_sample_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, k2, uniforms, path_idx, path_ids,
+    path_sample_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, P, k2, uniforms, path_idx, path_ids,
                                         path_q);
   else
-    path_walk_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, mode, path_idx, path_ids);
+    path_walk_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, P, mode, path_idx, path_ids);
   LAUNCH_CHECK();
   return DFLASH_OK;
 }
@@ -611,7 +613,7 @@ int dflash_select_path(const dflash_config* cfg, const dflash_weights* w, const 
   int rc;
   if ((rc = check_config(cfg))) return rc;
   if ((rc = check_weights(cfg, w, false, false, true))) return rc;
-  if (batch <= 0 || (n_fixed != 0 && n_fixed != 1)) return DFLASH_E_INVAL;
+  if (batch <= 0 || (n_fixed != 0 && n_fixed != 1) || cfg->block_size - n_fixed < 1) return DFLASH_E_INVAL;
   if (mode != DFLASH_PATH_GREEDY && mode != DFLASH_PATH_EXACT) return DFLASH_E_INVAL;
   if (!cand_ids || !cand_logits || !block_ids || !path_idx || !path_ids || !workspace) return DFLASH_E_INVAL;
   if (cfg->use_gate && !final_hidden) return DFLASH_E_INVAL;
@@ -655,7 +657,7 @@ int dflash_sample_path(const dflash_config* cfg, const dflash_weights* w, const 
   int rc;
   if ((rc = check_config(cfg))) return rc;
   if ((rc = check_weights(cfg, w, false, false, true))) return rc;
-  if (batch <= 0 || (n_fixed != 0 && n_fixed != 1)) return DFLASH_E_INVAL;
+  if (batch <= 0 || (n_fixed != 0 && n_fixed != 1) || cfg->block_size - n_fixed < 1) return DFLASH_E_INVAL;
   const float k2 = temp_scale(temperature);
   if (k2 == 0.f) return DFLASH_E_INVAL;
   if (!cand_ids || !cand_logits || !block_ids || !uniforms || !path_idx || !path_ids || !path_q || !workspace)

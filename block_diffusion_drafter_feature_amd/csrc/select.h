@@ -571,8 +571,8 @@ __global__ __launch_bounds__(64) void advance_kernel(const int32_t* __restrict__
 // Tokens whose 256-d embeddings are needed, per sequence: the 16 candidates of each
 // drafted position p (slot 16p + j), then the anchor (slot 16P) when n_fixed = 1.
 __global__ void path_tokens_kernel(const int32_t* __restrict__ cand_ids, const int32_t* __restrict__ block_ids,
-                                   int n_fixed, int32_t* __restrict__ tokens) {
-  const int b = blockIdx.x, P = 16 - n_fixed, T = 16 * P + n_fixed;
+                                   int n_fixed, int P, int32_t* __restrict__ tokens) {
+  const int b = blockIdx.x, T = 16 * P + n_fixed;
   for (int t = threadIdx.x; t < T; t += blockDim.x) {
     const int v = t < 16 * P ? cand_ids[(static_cast<size_t>(b) * 16 + n_fixed + t / 16) * 16 + (t % 16)]
                              : block_ids[static_cast<size_t>(b) * 16];
@@ -606,12 +606,12 @@ __device__ __forceinline__ f32x8_t load8_as_f32(const T* p) {
 template <typename T>
 __global__ __launch_bounds__(256) void path_scores_kernel(const float* __restrict__ z, const float* __restrict__ gamma,
                                                           const T* __restrict__ U, const T* __restrict__ Vf, int PD,
-                                                          int r, int n_fixed, float* __restrict__ S_out,
+                                                          int r, int n_fixed, int P, float* __restrict__ S_out,
                                                           float* __restrict__ pair_scores) {
   extern __shared__ float sm[];
   float* lam = sm;                  // [16][r + 1]
   float* rho = sm + 16 * (r + 1);   // [16][r + 1]
-  const int p = blockIdx.x, b = blockIdx.y, P = 16 - n_fixed, Tn = 16 * P + n_fixed;
+  const int p = blockIdx.x, b = blockIdx.y, Tn = 16 * P + n_fixed;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r16 = lane & 15, g = lane >> 4;
   const bool has_left = p >= 1 || n_fixed == 1;
   float* So = S_out + ((static_cast<size_t>(b) * P + p) * 16) * 16;
@@ -669,12 +669,13 @@ __global__ __launch_bounds__(256) void path_scores_kernel(const float* __restric
 // fp32, in exactly this order; ties to the lowest index.
 __global__ __launch_bounds__(64) void path_walk_kernel(const float* __restrict__ S_in,
                                                        const int32_t* __restrict__ cand_ids,
-                                                       const float* __restrict__ cand_logits, int n_fixed, int mode,
-                                                       int32_t* __restrict__ path_idx, int32_t* __restrict__ path_ids) {
+                                                       const float* __restrict__ cand_logits, int n_fixed, int P,
+                                                       int mode, int32_t* __restrict__ path_idx,
+                                                       int32_t* __restrict__ path_ids) {
   __shared__ float best[16];
   __shared__ int back[16][16];
   __shared__ int chosen[16];
-  const int b = blockIdx.x, P = 16 - n_fixed;
+  const int b = blockIdx.x;
   if (threadIdx.x >= 16) return;
   const int j = threadIdx.x;
   const float* S = S_in + static_cast<size_t>(b) * P * 256;
@@ -748,12 +749,13 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const float* __restrict__
 // threads (lanes 0..15 hold one candidate each).
 __global__ __launch_bounds__(64) void path_sample_kernel(const float* __restrict__ S_in,
                                                          const int32_t* __restrict__ cand_ids,
-                                                         const float* __restrict__ cand_logits, int n_fixed, float k2,
+                                                         const float* __restrict__ cand_logits, int n_fixed, int P,
+                                                         float k2,
                                                          const float* __restrict__ uniforms,
                                                          int32_t* __restrict__ path_idx,
                                                          int32_t* __restrict__ path_ids,
                                                          float* __restrict__ path_q) {
-  const int b = blockIdx.x, P = 16 - n_fixed;
+  const int b = blockIdx.x;
   if (threadIdx.x >= 16) return;
   const int j = threadIdx.x;
   const float* S = S_in + static_cast<size_t>(b) * P * 256;

@@ -96,6 +96,7 @@ typedef struct dflash_config {
   float   rms_eps;        /* RMSNorm epsilon (1e-6)                                           */
   float   rope_theta;     /* rotary base (1e6)                                                */
   int32_t weight_format;  /* DFLASH_WEIGHTS_DTYPE or DFLASH_WEIGHTS_FP8 (see dflash_weights)   */
+  int32_t block_size;     /* rows of the drafted block, 1 .. DFLASH_BLOCK (dynamic block size)  */
 } dflash_config;
 
 typedef struct dflash_layer_weights {

@@ -354,7 +354,7 @@ def block_attention(q: np.ndarray, k_ctx: np.ndarray, v_ctx: np.ndarray,
 
 def draft_block(m: Model, k_cache: Sequence[np.ndarray], v_cache: Sequence[np.ndarray],
                 ctx_len: int, block_ids: np.ndarray) -> Dict[str, np.ndarray]:
-    """One parallel forward pass of the drafter over a block of 16 tokens.
+    """One parallel forward pass of the drafter over a block of up to 16 tokens.
 
     [DFlash] section 2.2: the block (a clean anchor followed by mask tokens, section 2.3)
     is predicted in a single forward pass; every layer attends to the injected context
@@ -363,12 +363,14 @@ def draft_block(m: Model, k_cache: Sequence[np.ndarray], v_cache: Sequence[np.nd
     after the attention and the FFN sublayer of every layer.
 
     k_cache, v_cache: per layer ``[Hkv, >=ctx_len, hd]`` float64 (rows beyond ctx_len are
-    never read).  block_ids: [16] ints.  Positions: context rows 0..ctx_len-1, block rows
-    ctx_len..ctx_len+15.  Returns the fp64 logits ``[16, V]``, the final normed hidden
-    ``xhat [16, d]`` and per-layer residual streams.
+    never read).  block_ids: [nb] ints, nb = 16 or, under dynamic block-size scheduling,
+    fewer ([DFlash] sections 3 and 4: a drafter trained on blocks of 16 drafts smaller
+    blocks at inference; the block is then just nb rows).  Positions: context rows
+    0..ctx_len-1, block rows ctx_len..ctx_len+nb-1.  Returns the fp64 logits ``[nb, V]``,
+    the final normed hidden ``xhat [nb, d]`` and per-layer residual streams.
     """
     D = m.dims
-    nb = D.block
+    nb = len(block_ids)
     pos = ctx_len + np.arange(nb)
     x = m.rows("embed", np.asarray(block_ids))                 # [16, d]
     stream = [x.copy()]
@@ -449,17 +451,18 @@ def path_pair_scores(m: Model, cand_ids: np.ndarray, xhat: np.ndarray, block_ids
     map of the right position's final hidden state; the bilinear form is rank r:
         phi_i(a, b) = (U z_l(a)) . (V (gamma_i * z_r(b))).
 
-    cand_ids: [16, 16] candidates per block row; xhat: [16, d]; block_ids: [16].
-    Drafted positions are rows n_fixed..15, renumbered p = 0..P-1.  Returns S [P, 16, 16]:
+    cand_ids: [>=nb, 16] candidates per block row; xhat: [>=nb, d]; block_ids: [nb] (nb =
+    the block size).  Drafted positions are rows n_fixed..nb-1, renumbered p = 0..P-1.  Returns S [P, 16, 16]:
     for p >= 1, S[p, a, j] = phi(cand[p-1][a], cand[p][j]); for p = 0 row a = 0 holds
     phi(anchor, cand[0][j]) when there is an anchor (n_fixed = 1), everything else 0.
     """
     D = m.dims
-    P = D.block - n_fixed
+    nb = len(block_ids)
+    P = nb - n_fixed
     K = cand_ids.shape[-1]
     Pl, Pr = m.w("ps_left"), m.w("ps_right")
     U, Vf = m.w("ps_u"), m.w("ps_v")
-    rows = np.arange(n_fixed, D.block)
+    rows = np.arange(n_fixed, nb)
     cands = np.asarray(cand_ids)[rows]                                 # [P, K]
     if D.use_gate:
         gamma = sigmoid(m.rb(np.asarray(xhat, dtype=np.float64)[rows]) @ m.w("ps_gate").T)   # [P, 256]
@@ -678,7 +681,7 @@ def drafting_step(m: Model, k_cache: List[np.ndarray], v_cache: List[np.ndarray]
     ids, vals = topk(out["logits"], D.topk)
     S = path_pair_scores(m, ids, out["xhat"], block_ids, n_fixed)
     idx, _ = select_path(vals[n_fixed:], S, n_fixed == 1, mode)
-    path_ids = ids[np.arange(n_fixed, D.block), idx]
+    path_ids = ids[np.arange(n_fixed, len(block_ids)), idx]
     a, bonus = verify(path_ids, target_logits)
     return {"cand_ids": ids, "cand_logits": vals, "xhat": out["xhat"], "logits": out["logits"],
             "pair_scores": S, "path_idx": idx, "path_ids": path_ids, "accept_len": a, "bonus": bonus}
@@ -727,10 +730,10 @@ def drafting_cycles(m: Model, k_cache: List[np.ndarray], v_cache: List[np.ndarra
         ids, vals = topk(d["logits"], D.topk)
         S = path_pair_scores(m, ids, d["xhat"], block_ids, 1)
         idx, _ = select_path(vals[1:], S, True, mode)
-        path_ids = ids[np.arange(1, D.block), idx]
+        path_ids = ids[np.arange(1, len(block_ids)), idx]
         T = logits_fn(c, path_ids)
         a, bonus = verify(path_ids, T)
-        nxt = advance(a, bonus, ctx_len, D.mask_id, cap, D.block)
+        nxt = advance(a, bonus, ctx_len, D.mask_id, cap, len(block_ids))
         out.append({"cand_ids": ids, "logits": d["logits"], "path_ids": path_ids, "target_logits": T,
                     "accept_len": a, "bonus": bonus, "emitted": list(path_ids[:a]) + [bonus],
                     "ctx_len": ctx_len, "pos0": pos0, "n_new": n_new, "next": nxt})

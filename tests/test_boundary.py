@@ -183,3 +183,18 @@ def test_fp8_storage_arguments():
     assert _status(q, FAKE, 0, 64, FAKE, 1) == D.DFLASH_E_INVAL
     assert _status(q, None, 4, 64, FAKE, 1) == D.DFLASH_E_INVAL
     assert _status(q, FAKE, 4, 64, FAKE + 8, 1) == D.DFLASH_E_INVAL    # output not 16-byte aligned
+
+
+def test_block_size_arguments():
+    dims = synth.workload("t_small").dims
+    cfg = D.make_config(dims, block_size=5)
+    assert cfg.block_size == 5 and D.dflash_check_config(cfg) == D.DFLASH_OK
+    assert D.make_config(dims).block_size == 16
+    for bad in (0, 17, -1):
+        cfg.block_size = bad
+        assert D.dflash_check_config(cfg) == D.DFLASH_E_INVAL
+    # a one-row block with an anchor leaves nothing to choose
+    cfg, w, kv = _fake_structs(dims)
+    cfg.block_size = 1
+    ws_p = D.dflash_path_workspace_bytes(cfg, 2)
+    assert _status(D.dflash_select_path, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 0, 2, FAKE, FAKE, None, FAKE, ws_p, 1) == D.DFLASH_E_INVAL

@@ -429,3 +429,48 @@ def test_verify_brute_force_and_invariants():
         T2 = T.copy()
         full = np.array(greedy[:P])
         assert oracle.verify(full, T2) == (P, greedy[P])
+
+
+# ------------------------------------------------------------------ dynamic block size
+
+@pytest.mark.parametrize("nq", [5, 8, 16])
+def test_attention_any_block_size_is_library_sdpa(nq):
+    """A block of nq rows attends to the whole context and its own nq rows: textbook
+    attention over the concatenated keys (library routine, GQA by repeating kv heads)."""
+    q, kc, vc, kb, vb = _rand_attn(40 + nq, 23, nq=nq)
+    got = oracle.block_attention(q, kc, vc, kb, vb)
+    assert got.shape == (nq, 4, 8)
+    tq = torch.from_numpy(q).permute(1, 0, 2)                                   # [H, nq, hd]
+    keys = np.concatenate([kc, kb.transpose(1, 0, 2)], axis=1)                 # [Hkv, L + nq, hd]
+    vals = np.concatenate([vc, vb.transpose(1, 0, 2)], axis=1)
+    tk = torch.from_numpy(keys).repeat_interleave(2, dim=0)
+    tv = torch.from_numpy(vals).repeat_interleave(2, dim=0)
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, is_causal=False)
+    np.testing.assert_allclose(got, want.permute(1, 0, 2).numpy(), rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("nb", [2, 5, 8])
+def test_smaller_block_shapes_and_local_pair_scores(nb):
+    """A block of nb < 16 rows drafts nb rows (positions L..L+nb-1), and its pair scores are
+    those of the same positions in a 16-row block: each score reads only the candidates of
+    its own and the previous position and the gate of its own row."""
+    dims, m = _ps_model()
+    ids, lg, xh = synth.make_candidates(dims, 1, 41)
+    bids = np.full(16, dims.mask_id)
+    bids[0] = 7
+    S16 = oracle.path_pair_scores(m, ids[0], xh[0], bids, 1)
+    Sn = oracle.path_pair_scores(m, ids[0][:nb], xh[0][:nb], bids[:nb], 1)
+    assert Sn.shape == (nb - 1, 16, 16)
+    np.testing.assert_allclose(Sn, S16[:nb - 1], rtol=1e-13, atol=1e-13)
+    # the forward pass over nb rows: shapes, and the anchor row's positions start at L
+    dims2 = tiny_dims(n_layers=1)
+    m2 = oracle.Model(dims2, synth.make_weights(dims2, 3))
+    K, V = synth.make_cache(dims2, [9], 64, 5)
+    kc = [oracle.decode(K[0, 0], dims2.dtype)]
+    vc = [oracle.decode(V[0, 0], dims2.dtype)]
+    out = oracle.draft_block(m2, kc, vc, 9, bids[:nb])
+    assert out["logits"].shape == (nb, dims2.vocab) and out["xhat"].shape == (nb, dims2.d)
+    # attention inside the block is bidirectional at any size: a second row changes row 0
+    one = oracle.draft_block(m2, kc, vc, 9, bids[:1])["logits"]
+    two = oracle.draft_block(m2, kc, vc, 9, bids[:2])["logits"]
+    assert np.abs(two[0] - one[0]).max() > 1e-9
