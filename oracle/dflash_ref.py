@@ -49,7 +49,7 @@ __all__ = [
     "path_pair_scores", "select_path", "verify", "conv_param_count",
     "path_selector_param_count", "drafting_step", "advance", "drafting_cycles",
     "sample_path", "verify_sampled", "e4m3_values", "e4m3_encode", "e4m3_decode", "quantize_fp8_rows",
-    "dequantize_fp8_rows", "FP8_MATRICES", "is_fp8_matrix",
+    "dequantize_fp8_rows", "FP8_MATRICES", "is_fp8_matrix", "calibrate",
 ]
 
 
@@ -572,6 +572,31 @@ def _inverse_cdf(w: np.ndarray, u: float) -> int:
         if target < run:
             return i
     return int(np.flatnonzero(w > 0)[-1])
+
+
+# ----------------------------------------------------------------------------------
+# bonus-guided calibration of the drafted logits
+# ----------------------------------------------------------------------------------
+
+def calibrate(m: Model, xhat: np.ndarray, bonus: int, logits: np.ndarray) -> np.ndarray:
+    """Logits of a drafted block after bonus-guided calibration.
+
+    [FlexDraft] "Calibración Guiada por Bono": a light MLP after the LM head takes the
+    concatenation of the resolved bonus token's embedding and the hidden state of a mask
+    position and returns an additive bias for that position's drafted logits (the block
+    was drafted before verification had fixed the bonus token).  Reading: one hidden layer
+    of width c with SiLU and no biases,
+        bias_i = W2 bf16(silu(W1 [bf16(E[bonus]); bf16(xhat_i)])),
+    W1 [c, 2d] ("cal_w1"), W2 [V, c] ("cal_w2"); the hidden state is the final normed
+    hidden state the LM head reads; the bias is added to the fp32 logits.
+
+    xhat: [nb, d]; logits: [nb, V].  Returns the calibrated logits [nb, V] (float64).
+    """
+    x = np.asarray(xhat, dtype=np.float64)
+    e = m.rows("embed", np.asarray([int(bonus)]))[0]
+    a = np.concatenate([np.broadcast_to(m.rb(e), x.shape), m.rb(x)], axis=1)    # [nb, 2d]
+    h = m.rb(silu(a @ m.w("cal_w1").T))
+    return np.asarray(logits, dtype=np.float64) + h @ m.w("cal_w2").T
 
 
 # ----------------------------------------------------------------------------------

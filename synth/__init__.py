@@ -313,6 +313,13 @@ def make_weights(dims: Dims, seed: int, ps_scale: str = "config", conv_scale: st
     return out
 
 
+def make_cal_weights(dims: Dims, seed: int, cal_dim: int, std: float = 0.02) -> Dict[str, np.ndarray]:
+    """Weights of the bonus-calibration MLP: ``cal_w1 [cal_dim, 2d]``, ``cal_w2 [V, cal_dim]``,
+    N(0, std^2) in the storage type (drawn apart from the drafter's own weights)."""
+    return {"cal_w1": normal((cal_dim, 2 * dims.d), std, seed, 9001, dims.dtype),
+            "cal_w2": normal((dims.vocab, cal_dim), std, seed, 9002, dims.dtype)}
+
+
 # --------------------------------------------------------------------------------------
 # activations, caches, ids, logits
 # --------------------------------------------------------------------------------------

@@ -474,3 +474,69 @@ def test_smaller_block_shapes_and_local_pair_scores(nb):
     one = oracle.draft_block(m2, kc, vc, 9, bids[:1])["logits"]
     two = oracle.draft_block(m2, kc, vc, 9, bids[:2])["logits"]
     assert np.abs(two[0] - one[0]).max() > 1e-9
+
+
+# ------------------------------------------------------------------ bonus-guided calibration
+
+def _cal_model(cal_dim=8, seed=50, **kw):
+    dims = tiny_dims(**kw)
+    W = synth.make_weights(dims, seed)
+    W.update(synth.make_cal_weights(dims, seed, cal_dim, std=0.3))
+    return dims, W
+
+
+def test_calibration_zero_output_layer_is_identity():
+    dims, W = _cal_model()
+    W["cal_w2"] = synth.const(W["cal_w2"].shape, 0.0, dims.dtype)
+    m = oracle.Model(dims, W)
+    r = rng(51)
+    xh, lg = r.standard_normal((16, dims.d)), r.standard_normal((16, dims.vocab))
+    np.testing.assert_array_equal(oracle.calibrate(m, xh, 3, lg), lg)
+
+
+def test_calibration_structure_against_library_silu():
+    """W1 picking single input coordinates and W2 routing hidden unit k to token k: the
+    bias of token k is silu of that coordinate (library silu).  Unit 0 reads the bonus
+    embedding's first coordinate, unit 1 the row's own first hidden coordinate: this fixes
+    the concatenation order [embedding; hidden]."""
+    dims, W = _cal_model(cal_dim=4, dtype="f32")
+    d = dims.d
+    w1 = np.zeros((4, 2 * d), dtype=np.float32)
+    w1[0, 0] = 1.0          # bonus embedding, coordinate 0
+    w1[1, d] = 1.0          # hidden state, coordinate 0
+    w1[2, d + 5] = -2.0     # hidden state, coordinate 5
+    w2 = np.zeros((dims.vocab, 4), dtype=np.float32)
+    w2[10, 0] = w2[11, 1] = w2[12, 2] = 1.0
+    W["cal_w1"], W["cal_w2"] = w1, w2
+    m = oracle.Model(dims, W)
+    r = rng(52)
+    xh = r.standard_normal((5, d))
+    lg = np.zeros((5, dims.vocab))
+    out = oracle.calibrate(m, xh, 7, lg)
+    silu = torch.nn.functional.silu
+    e = oracle.decode(W["embed"][7], "f32")
+    np.testing.assert_allclose(out[:, 10], silu(torch.tensor(e[0])).item(), rtol=1e-12)
+    np.testing.assert_allclose(out[:, 11], silu(torch.from_numpy(xh[:, 0])).numpy(), rtol=1e-12)
+    np.testing.assert_allclose(out[:, 12], silu(torch.from_numpy(-2.0 * xh[:, 5])).numpy(), rtol=1e-12)
+    assert (out[:, 13:] == 0).all() and (out[:, :10] == 0).all()
+
+
+def test_calibration_rows_are_independent_and_bonus_enters_by_embedding():
+    dims, W = _cal_model()
+    m = oracle.Model(dims, W)
+    r = rng(53)
+    xh, lg = r.standard_normal((16, dims.d)), r.standard_normal((16, dims.vocab))
+    base = oracle.calibrate(m, xh, 3, lg)
+    xh2 = xh.copy()
+    xh2[4] += 1.0
+    out = oracle.calibrate(m, xh2, 3, lg)
+    changed = np.abs(out - base).max(axis=1) > 1e-9
+    assert changed[4] and not changed[np.arange(16) != 4].any()
+    # two bonus tokens with equal embedding rows calibrate alike; a different row does not
+    W2 = dict(W)
+    emb = W["embed"].copy()
+    emb[9] = emb[3]
+    W2["embed"] = emb
+    m2 = oracle.Model(dims, W2)
+    np.testing.assert_array_equal(oracle.calibrate(m2, xh, 9, lg), oracle.calibrate(m2, xh, 3, lg))
+    assert np.abs(oracle.calibrate(m, xh, 4, lg) - base).max() > 1e-6
