@@ -54,6 +54,9 @@ def parse():
     ap.add_argument("--block-sizes", default="8,5",
                     help="also time the step with these smaller drafted blocks (dynamic block size; comma list, "
                          "empty to skip)")
+    ap.add_argument("--cal-dim", type=int, default=256,
+                    help="also time the bonus-guided calibration (MLP of this hidden width, device-drawn "
+                         "N(0, 0.02^2) weights) on the step's drafted block; 0 to skip")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the step, run a plain fp32 elementwise copy (torch.neg) of this many MiB "
                          "three times: a kernel of known traffic that calibrates HBM byte counters")
@@ -499,6 +502,40 @@ def main():
         smaller[str(bs)] = {"steps": nsteps, "ms_per_step": round(msb, 4), "blocks_per_s": round(B * 1000.0 / msb, 2)}
         del drb
 
+    calib = None
+    if args.cal_dim > 0:
+        C, V, d = args.cal_dim, dims.vocab, dims.d
+        gcal = torch.Generator(device="cuda")
+        gcal.manual_seed(wl.seed + 31)
+        cw = {"cal_w1": (torch.randn((C, 2 * d), generator=gcal, device="cuda") * 0.02).to(dt_t),
+              "cal_w2": (torch.randn((V, C), generator=gcal, device="cuda") * 0.02).to(dt_t)}
+        drc = D.Drafter(dims, {**dr.t, **cw})
+        lg_full = torch.zeros((B, 16, V), dtype=torch.float32, device="cuda")
+        D.dflash_draft_block(dr.cfg, dr.w, cache.kv, ctx_t, ids_t, B, ci, cl, fh, lg_full, ws_d, nb_d)
+        nb_c = D.dflash_calibrate_workspace_bytes(drc.cfg, B)
+        ws_c = torch.empty(nb_c, dtype=torch.uint8, device="cuda")
+        ci_c = torch.zeros_like(ci)
+        cl_c = torch.zeros_like(cl)
+        for _ in range(3):
+            D.dflash_calibrate(drc.cfg, drc.w, fh, bon, B, lg_full, ci_c, cl_c, ws_c, nb_c)
+        torch.cuda.synchronize()
+        ncal = max(10, args.steps)
+        start.record()
+        for _ in range(ncal):
+            D.dflash_calibrate(drc.cfg, drc.w, fh, bon, B, lg_full, ci_c, cl_c, ws_c, nb_c)
+        stop.record()
+        torch.cuda.synchronize()
+        msc = start.elapsed_time(stop) / ncal
+        e = 2 if dims.dtype == "bf16" else 4
+        M = 16 * B
+        cal_bytes = V * C * e + C * 2 * d * e + M * 2 * d * e + 3 * M * V * 4
+        log(f"[bench] calibration (width {C}): {msc * 1e3:.1f} us per block batch")
+        calib = {"calls": ncal, "ms_per_call": round(msc, 4), "cal_dim": C,
+                 "algorithmic_bytes": int(cal_bytes),
+                 "hbm_frac": round(cal_bytes / (msc * 1e-3) / HBM_PEAK, 4),
+                 "includes": "input gather, MLP input GEMM (SiLU), output GEMM adding into the logits, top-16"}
+        del drc, cw
+
     cycle = None
     if args.cycles > 0:
         cycle = run_cycles(args.cycles, D, torch, np, synth, wl, dr, new_hid, row_off, tdt, log)
@@ -544,6 +581,8 @@ def main():
         out["fp8_weights"] = fp8
     if smaller:
         out["smaller_blocks"] = smaller
+    if calib is not None:
+        out["calibration"] = calib
     if cycle is not None:
         out["cycle"] = cycle
     print(json.dumps(out), flush=True)

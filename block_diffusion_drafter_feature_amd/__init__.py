@@ -41,7 +41,8 @@ N_PROBES = len(PROBES)
 
 EXPORTED = (
     "dflash_inject_context", "dflash_draft_block", "dflash_select_path", "dflash_verify", "dflash_advance",
-    "dflash_sample_path", "dflash_verify_sampled", "dflash_quantize_fp8",
+    "dflash_sample_path", "dflash_verify_sampled", "dflash_quantize_fp8", "dflash_calibrate",
+    "dflash_calibrate_workspace_bytes",
     "dflash_inject_workspace_bytes", "dflash_draft_workspace_bytes", "dflash_path_workspace_bytes",
     "dflash_verify_workspace_bytes", "dflash_verify_sampled_workspace_bytes", "dflash_check_config",
     "dflash_status_string",
@@ -65,7 +66,8 @@ class dflash_config(ctypes.Structure):
                 ("head_dim", _i32), ("d_ffn", _i32), ("n_layers", _i32), ("n_feat_layers", _i32),
                 ("d_target", _i32), ("vocab", _i32), ("ps_dim", _i32), ("ps_rank", _i32),
                 ("use_conv", _i32), ("use_gate", _i32), ("rms_eps", ctypes.c_float),
-                ("rope_theta", ctypes.c_float), ("weight_format", _i32), ("block_size", _i32)]
+                ("rope_theta", ctypes.c_float), ("weight_format", _i32), ("block_size", _i32),
+                ("cal_dim", _i32)]
 
 
 class dflash_layer_weights(ctypes.Structure):
@@ -77,7 +79,7 @@ class dflash_layer_weights(ctypes.Structure):
 class dflash_weights(ctypes.Structure):
     _fields_ = [("embed", _vp), ("lm_head", _vp), ("w_fc", _vp), ("g_fc", _vp), ("g_final", _vp),
                 ("ps_left", _vp), ("ps_right", _vp), ("ps_gate", _vp), ("ps_u", _vp), ("ps_v", _vp),
-                ("layers", dflash_layer_weights * MAX_LAYERS)]
+                ("layers", dflash_layer_weights * MAX_LAYERS), ("cal_w1", _vp), ("cal_w2", _vp)]
 
 
 class dflash_probes(ctypes.Structure):
@@ -117,6 +119,8 @@ def lib() -> ctypes.CDLL:
                                        _vp, _vp, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
             "dflash_verify_sampled_workspace_bytes": ([_i32, _i32, _i32], PC),
             "dflash_quantize_fp8": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
+            "dflash_calibrate": ([cfgp, wp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
+            "dflash_calibrate_workspace_bytes": ([cfgp, _i32], PC),
             "dflash_inject_workspace_bytes": ([cfgp, _i32], PC),
             "dflash_draft_workspace_bytes": ([cfgp, _i32, _i32], PC),
             "dflash_path_workspace_bytes": ([cfgp, _i32], PC),
@@ -331,6 +335,17 @@ def to_device(arr, dims, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
+def dflash_calibrate_workspace_bytes(cfg, batch: int) -> int:
+    return lib().dflash_calibrate_workspace_bytes(ctypes.byref(cfg), batch)
+
+
+def dflash_calibrate(cfg, w, final_hidden, bonus, batch, logits, cand_ids, cand_logits, workspace, workspace_bytes,
+                     stream=None) -> None:
+    _check("dflash_calibrate", lib().dflash_calibrate(
+        ctypes.byref(cfg), ctypes.byref(w), _ptr(final_hidden), _ptr(bonus), batch, _ptr(logits), _ptr(cand_ids),
+        _ptr(cand_logits), _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
 def dflash_quantize_fp8(w, rows: int, cols: int, out, stream=None) -> None:
     _check("dflash_quantize_fp8", lib().dflash_quantize_fp8(_ptr(w), rows, cols, _ptr(out), _stream(stream)))
 
@@ -365,8 +380,11 @@ class Drafter:
             raise DflashError("dflash_check_config", st)
         w = dflash_weights()
         p = lambda k: self.t[k].data_ptr() if k in self.t else None  # noqa: E731
-        for k in ("embed", "lm_head", "w_fc", "g_fc", "g_final", "ps_left", "ps_right", "ps_gate", "ps_u", "ps_v"):
+        for k in ("embed", "lm_head", "w_fc", "g_fc", "g_final", "ps_left", "ps_right", "ps_gate", "ps_u", "ps_v",
+                  "cal_w1", "cal_w2"):
             setattr(w, k, p(k))
+        if "cal_w1" in self.t:
+            self.cfg.cal_dim = self.t["cal_w1"].shape[0]
         for l in range(dims.n_layers):
             L = w.layers[l]
             for k in ("w_q", "w_k", "w_v", "w_o", "w_gate", "w_up", "w_down", "g_attn", "g_ffn"):

@@ -63,6 +63,7 @@ int check_config(const dflash_config* c) {
   if (c->weight_format != DFLASH_WEIGHTS_DTYPE && c->weight_format != DFLASH_WEIGHTS_FP8) return DFLASH_E_INVAL;
   if (c->weight_format == DFLASH_WEIGHTS_FP8 && c->dtype != DFLASH_BF16) return DFLASH_E_UNSUPPORTED;
   if (c->block_size < 1 || c->block_size > DFLASH_BLOCK) return DFLASH_E_INVAL;
+  if (c->cal_dim < 0 || c->cal_dim % 64) return DFLASH_E_INVAL;
   return DFLASH_OK;
 }
 
@@ -216,6 +217,29 @@ VerifyWs carve_verify(Carver& cv, int B, int n_draft, int V) {
   const size_t nch = (V + kArgmaxChunk - 1) / kArgmaxChunk;
   w.pv = cv.take<float>(static_cast<size_t>(B) * (n_draft + 1) * nch);
   w.pi = cv.take<int32_t>(static_cast<size_t>(B) * (n_draft + 1) * nch);
+  return w;
+}
+
+template <typename T>
+struct CalWs {
+  T* a;          // [M][2d] MLP input
+  float* h;      // [M][cal_dim] hidden layer
+  float* tk_v;   // [M][n_chunks][16]
+  int32_t* tk_i;
+  float* scratch;
+  size_t scratch_bytes;
+};
+template <typename T>
+CalWs<T> carve_cal(Carver& cv, const dflash_config* c, int B) {
+  CalWs<T> w;
+  const size_t M = static_cast<size_t>(16) * B, d = c->d_model, nch = (c->vocab + kTopkChunk - 1) / kTopkChunk;
+  w.a = cv.take<T>(M * 2 * d);
+  w.h = cv.take<float>(M * c->cal_dim);
+  w.tk_v = cv.take<float>(M * nch * 16);
+  w.tk_i = cv.take<int32_t>(M * nch * 16);
+  w.scratch_bytes = std::max(splitk_scratch_bytes<T>(static_cast<int>(M), 2 * c->d_model, c->cal_dim / 16),
+                             splitk_scratch_bytes<T>(static_cast<int>(M), c->cal_dim, c->vocab / 16));
+  w.scratch = cv.take<float>(w.scratch_bytes / sizeof(float) + 1);
   return w;
 }
 
@@ -510,6 +534,32 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
   return DFLASH_OK;
 }
 
+// ------------------------------------------------------------------ bonus calibration
+
+template <typename T>
+int calibrate_impl(const dflash_config* c, const dflash_weights* w, const float* xhat, const int32_t* bonus, int B,
+                   float* logits, int32_t* cand_ids, float* cand_logits, void* ws, hipStream_t s) {
+  Carver cv(ws);
+  CalWs<T> W = carve_cal<T>(cv, c, B);
+  const int M = 16 * B, d = c->d_model, C = c->cal_dim, V = c->vocab;
+  cal_input_kernel<T><<<M, 256, 0, s>>>(static_cast<const T*>(w->embed), bonus, xhat, d, W.a);
+  LAUNCH_CHECK();
+  {
+    EpiStore<T> e{seg1<T>(w->cal_w1, C, 2 * d), W.h, C, SILU};
+    GEMM_CHECK((run_gemm<T, T>(W.a, 2 * d, nullptr, M, 2 * d, C / 16, e, s, W.scratch, W.scratch_bytes)));
+  }
+  {
+    EpiStore<T> e{seg1<T>(w->cal_w2, V, C), logits, V, ADD};
+    GEMM_CHECK((run_gemm<T, float>(W.h, C, nullptr, M, C, V / 16, e, s, W.scratch, W.scratch_bytes)));
+  }
+  const int nch = (V + kTopkChunk - 1) / kTopkChunk;
+  topk_partial_kernel<<<dim3(nch, M), 64, 0, s>>>(logits, V, V, W.tk_v, W.tk_i);
+  LAUNCH_CHECK();
+  topk_final_kernel<<<M, 64, 0, s>>>(W.tk_v, W.tk_i, nch, cand_ids, cand_logits);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
 }  // namespace
 
 // =====================================================================================
@@ -715,6 +765,29 @@ int dflash_verify_sampled(const int32_t* draft, const int32_t* q_ids, int64_t q_
   }
   LAUNCH_CHECK();
   return DFLASH_OK;
+}
+
+size_t dflash_calibrate_workspace_bytes(const dflash_config* cfg, int32_t batch) {
+  if (check_config(cfg) != DFLASH_OK || batch <= 0 || cfg->cal_dim <= 0) return 0;
+  Carver cv(nullptr);
+  if (cfg->dtype == DFLASH_BF16) carve_cal<bf16_t>(cv, cfg, batch);
+  else carve_cal<float>(cv, cfg, batch);
+  return cv.off;
+}
+
+int dflash_calibrate(const dflash_config* cfg, const dflash_weights* w, const float* final_hidden,
+                     const int32_t* bonus, int32_t batch, float* logits, int32_t* cand_ids, float* cand_logits,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if (!w || cfg->cal_dim <= 0 || !w->cal_w1 || !w->cal_w2 || !w->embed) return DFLASH_E_INVAL;
+  if (batch <= 0 || !final_hidden || !bonus || !logits || !cand_ids || !cand_logits || !workspace)
+    return DFLASH_E_INVAL;
+  if (workspace_bytes < dflash_calibrate_workspace_bytes(cfg, batch)) return DFLASH_E_WORKSPACE;
+  if (cfg->dtype == DFLASH_BF16)
+    return calibrate_impl<bf16_t>(cfg, w, final_hidden, bonus, batch, logits, cand_ids, cand_logits, workspace,
+                                  stream);
+  return calibrate_impl<float>(cfg, w, final_hidden, bonus, batch, logits, cand_ids, cand_logits, workspace, stream);
 }
 
 int dflash_quantize_fp8(const void* w, int32_t rows, int32_t cols, void* out, hipStream_t stream) {

@@ -83,6 +83,23 @@ __global__ __launch_bounds__(256) void conv_apply_kernel(const float* __restrict
   }
 }
 
+// ------------------------------------------------------------------ bonus calibration input
+
+// Row m of the calibration MLP's input: [E[bonus of m's sequence] ; xhat_m rounded to T].
+// One work-group per row (16 rows per sequence).
+template <typename T>
+__global__ __launch_bounds__(256) void cal_input_kernel(const T* __restrict__ emb, const int32_t* __restrict__ bonus,
+                                                        const float* __restrict__ xhat, int d, T* __restrict__ out) {
+  const int m = blockIdx.x;
+  const T* e = emb + static_cast<size_t>(bonus[m >> 4]) * d;
+  const float* x = xhat + static_cast<size_t>(m) * d;
+  T* o = out + static_cast<size_t>(m) * 2 * d;
+  for (int j = threadIdx.x; j < d; j += 256) {
+    o[j] = e[j];
+    o[d + j] = from_f<T>(x[j]);
+  }
+}
+
 // ------------------------------------------------------------------ FP8 weight storage
 
 // E4M3 code of the value nearest to x (ties to the even mantissa), magnitudes saturating

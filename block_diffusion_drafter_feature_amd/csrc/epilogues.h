@@ -39,7 +39,7 @@ __device__ __forceinline__ int rope_dim(int tt, int c, int hd) {
 
 // ------------------------------------------------------------------ plain store / residual / sigmoid
 
-enum StoreMode { STORE = 0, ADD = 1, SIGMOID = 2 };
+enum StoreMode { STORE = 0, ADD = 1, SIGMOID = 2, SILU = 3 };
 
 template <typename T>
 struct EpiStore {
@@ -75,6 +75,7 @@ struct EpiStore {
     float* o = out + static_cast<size_t>(m) * ldo + n;
     if (mode == ADD) *o += v;
     else if (mode == SIGMOID) *o = 1.f / (1.f + expf(-v));
+    else if (mode == SILU) *o = v / (1.f + expf(-v));
     else *o = v;
   }
 };

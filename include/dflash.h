@@ -97,6 +97,8 @@ typedef struct dflash_config {
   float   rope_theta;     /* rotary base (1e6)                                                */
   int32_t weight_format;  /* DFLASH_WEIGHTS_DTYPE or DFLASH_WEIGHTS_FP8 (see dflash_weights)   */
   int32_t block_size;     /* rows of the drafted block, 1 .. DFLASH_BLOCK (dynamic block size)  */
+  int32_t cal_dim;        /* hidden width c of the bonus-calibration MLP; 0: none; else a
+                             multiple of 64                                                   */
 } dflash_config;
 
 typedef struct dflash_layer_weights {
@@ -135,6 +137,8 @@ typedef struct dflash_weights {
   const void* ps_u;       /* [r, ps_dim] left factor of the bilinear form                      */
   const void* ps_v;       /* [r, ps_dim] right factor                                          */
   dflash_layer_weights layers[DFLASH_MAX_LAYERS];
+  const void* cal_w1;     /* [cal_dim, 2d] bonus-calibration MLP, input layer (cal_dim > 0)    */
+  const void* cal_w2;     /* [V, cal_dim]  its output layer                                    */
 } dflash_weights;
 
 /* The drafter's KV cache of injected context, one pair of arrays per layer.
@@ -257,6 +261,27 @@ int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtyp
                   int32_t n_draft, int32_t vocab, int32_t* accept_len, int32_t* bonus,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Bonus-guided calibration of a drafted block ("FlexDraft", "Metodología" item 2: a
+ * light MLP after the LM head turns the resolved bonus token's embedding and a mask
+ * position's hidden state into an additive bias of that position's drafted logits, for a
+ * block drafted before verification fixed the bonus token).
+ *
+ * For every row m of sequence b (rows 0..15; rows at or past block_size carry no meaning):
+ *   h_m      = silu(cal_w1 [E[bonus[b]] ; bf16(final_hidden_m)])   rounded to the storage type
+ *   logits_m += cal_w2 h_m
+ * then cand_ids / cand_logits are the top-16 of the calibrated logits (as dflash_draft_block
+ * orders them).  cfg->cal_dim > 0 and w->cal_w1, cal_w2, embed set, else DFLASH_E_INVAL.
+ *
+ * final_hidden : device float [batch, 16, d] (dflash_draft_block's output)
+ * bonus        : device int32 [batch]
+ * logits       : device float [batch, 16, V] (dflash_draft_block's logits), updated in place
+ * cand_ids, cand_logits : device [batch, 16, 16], written.
+ * Workspace: dflash_calibrate_workspace_bytes(cfg, batch).
+ */
+int dflash_calibrate(const dflash_config* cfg, const dflash_weights* w, const float* final_hidden,
+                     const int32_t* bonus, int32_t batch, float* logits, int32_t* cand_ids, float* cand_logits,
+                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Sampled path choice ("DFlash 2 ...", "Arquitectura del Sistema", item 1: the block can
  * be chosen by sampling over the precomputed scores instead of the greedy walk).
  *
@@ -350,6 +375,7 @@ size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch, int
 size_t dflash_path_workspace_bytes(const dflash_config* cfg, int32_t batch);
 size_t dflash_verify_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab);
 size_t dflash_verify_sampled_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab);
+size_t dflash_calibrate_workspace_bytes(const dflash_config* cfg, int32_t batch);
 
 /* Check a configuration against what the kernels support: DFLASH_OK, DFLASH_E_INVAL
  * or DFLASH_E_UNSUPPORTED. */

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 17
     lib = ctypes.CDLL(D.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -198,3 +198,19 @@ def test_block_size_arguments():
     cfg.block_size = 1
     ws_p = D.dflash_path_workspace_bytes(cfg, 2)
     assert _status(D.dflash_select_path, cfg, w, FAKE, FAKE, FAKE, FAKE, 1, 0, 2, FAKE, FAKE, None, FAKE, ws_p, 1) == D.DFLASH_E_INVAL
+
+
+def test_calibrate_arguments():
+    dims = synth.workload("t_small").dims
+    cfg, w, kv = _fake_structs(dims)
+    assert D.dflash_calibrate_workspace_bytes(cfg, 2) == 0          # no calibration MLP configured
+    assert _status(D.dflash_calibrate, cfg, w, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, 1 << 20, 1) == D.DFLASH_E_INVAL
+    cfg.cal_dim = 100
+    assert D.dflash_check_config(cfg) == D.DFLASH_E_INVAL
+    cfg.cal_dim = 64
+    nb = D.dflash_calibrate_workspace_bytes(cfg, 2)
+    assert nb > 0
+    assert _status(D.dflash_calibrate, cfg, w, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, nb, 1) == D.DFLASH_E_INVAL
+    w.cal_w1 = w.cal_w2 = FAKE
+    assert _status(D.dflash_calibrate, cfg, w, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, nb - 1, 1) == D.DFLASH_E_WORKSPACE
+    assert _status(D.dflash_calibrate, cfg, w, FAKE, None, 2, FAKE, FAKE, FAKE, FAKE, nb, 1) == D.DFLASH_E_INVAL
