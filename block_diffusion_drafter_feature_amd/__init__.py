@@ -42,7 +42,7 @@ N_PROBES = len(PROBES)
 EXPORTED = (
     "dflash_inject_context", "dflash_draft_block", "dflash_select_path", "dflash_verify", "dflash_advance",
     "dflash_sample_path", "dflash_verify_sampled", "dflash_quantize_fp8", "dflash_calibrate",
-    "dflash_calibrate_workspace_bytes",
+    "dflash_calibrate_workspace_bytes", "dflash_path_table_bytes", "dflash_build_path_table",
     "dflash_inject_workspace_bytes", "dflash_draft_workspace_bytes", "dflash_path_workspace_bytes",
     "dflash_verify_workspace_bytes", "dflash_verify_sampled_workspace_bytes", "dflash_check_config",
     "dflash_status_string",
@@ -79,7 +79,8 @@ class dflash_layer_weights(ctypes.Structure):
 class dflash_weights(ctypes.Structure):
     _fields_ = [("embed", _vp), ("lm_head", _vp), ("w_fc", _vp), ("g_fc", _vp), ("g_final", _vp),
                 ("ps_left", _vp), ("ps_right", _vp), ("ps_gate", _vp), ("ps_u", _vp), ("ps_v", _vp),
-                ("layers", dflash_layer_weights * MAX_LAYERS), ("cal_w1", _vp), ("cal_w2", _vp)]
+                ("layers", dflash_layer_weights * MAX_LAYERS), ("cal_w1", _vp), ("cal_w2", _vp),
+                ("ps_table", _vp)]
 
 
 class dflash_probes(ctypes.Structure):
@@ -121,6 +122,8 @@ def lib() -> ctypes.CDLL:
             "dflash_quantize_fp8": ([_vp, _i32, _i32, _vp, _vp], ctypes.c_int),
             "dflash_calibrate": ([cfgp, wp, _vp, _vp, _i32, _vp, _vp, _vp, _vp, PC, _vp], ctypes.c_int),
             "dflash_calibrate_workspace_bytes": ([cfgp, _i32], PC),
+            "dflash_path_table_bytes": ([cfgp], PC),
+            "dflash_build_path_table": ([cfgp, wp, _vp, _vp], ctypes.c_int),
             "dflash_inject_workspace_bytes": ([cfgp, _i32], PC),
             "dflash_draft_workspace_bytes": ([cfgp, _i32, _i32], PC),
             "dflash_path_workspace_bytes": ([cfgp, _i32], PC),
@@ -335,6 +338,15 @@ def to_device(arr, dims, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
+def dflash_path_table_bytes(cfg) -> int:
+    return lib().dflash_path_table_bytes(ctypes.byref(cfg))
+
+
+def dflash_build_path_table(cfg, w, table, stream=None) -> None:
+    _check("dflash_build_path_table", lib().dflash_build_path_table(ctypes.byref(cfg), ctypes.byref(w), _ptr(table),
+                                                                    _stream(stream)))
+
+
 def dflash_calibrate_workspace_bytes(cfg, batch: int) -> int:
     return lib().dflash_calibrate_workspace_bytes(ctypes.byref(cfg), batch)
 
@@ -359,7 +371,7 @@ class Drafter:
     storage (E4M3 rows with a float32 scale) by ``dflash_quantize_fp8``."""
 
     def __init__(self, dims, weights: Dict[str, "object"], device: str = "cuda", fp8: bool = False,
-                 block_size: Optional[int] = None):
+                 block_size: Optional[int] = None, path_table: bool = True):
         import torch
         self.dims = dims
         self.fp8 = fp8
@@ -395,6 +407,13 @@ class Drafter:
                     L.conv_w0[s] = p(f"l{l}.conv{s}.w0")
                     L.conv_w1[s] = p(f"l{l}.conv{s}.w1")
         self.w = w
+        self.table = None
+        if path_table and all(k in self.t for k in ("embed", "ps_left", "ps_right")):
+            # the Path Selector's per-token projections, built once on the device
+            self.table = torch.empty(dflash_path_table_bytes(self.cfg) // 4, dtype=torch.float32, device=device)
+            dflash_build_path_table(self.cfg, w, self.table)
+            torch.cuda.synchronize()
+            w.ps_table = self.table.data_ptr()
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in self.t.values())

@@ -500,9 +500,10 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
   Carver cv(ws);
   PathWs W = carve_path<T>(cv, c, B);
   const int d = c->d_model, PD = c->ps_dim, P = c->block_size - n_fixed, Tn = 16 * P + n_fixed;
-  path_tokens_kernel<<<B, 256, 0, s>>>(cand_ids, block_ids, n_fixed, P, W.tokens);
-  LAUNCH_CHECK();
-  {
+  const float* table = static_cast<const float*>(w->ps_table);
+  if (!table) {   // project the candidates' and the anchor's embeddings now
+    path_tokens_kernel<<<B, 256, 0, s>>>(cand_ids, block_ids, n_fixed, P, W.tokens);
+    LAUNCH_CHECK();
     SegW<T> sw{};
     sw.p[0] = static_cast<const T*>(w->ps_left);
     sw.p[1] = static_cast<const T*>(w->ps_right);
@@ -523,7 +524,8 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
   const size_t smem = 2 * 16 * (c->ps_rank + 1) * sizeof(float);
   path_scores_kernel<T><<<dim3(P, B), 256, smem, s>>>(W.z, c->use_gate ? W.gamma : nullptr,
                                                       static_cast<const T*>(w->ps_u), static_cast<const T*>(w->ps_v),
-                                                      PD, c->ps_rank, n_fixed, P, W.S, pair_scores);
+                                                      PD, c->ps_rank, n_fixed, P, W.S, pair_scores, table,
+                                                      cand_ids, block_ids, c->vocab);
   LAUNCH_CHECK();
   if (uniforms)
     path_sample_kernel<<<B, 64, 0, s>>>(W.S, cand_ids, cand_logits, n_fixed, P, k2, uniforms, path_idx, path_ids,
@@ -764,6 +766,43 @@ int dflash_verify_sampled(const int32_t* draft, const int32_t* q_ids, int64_t q_
     bonus_kernel<float><<<batch, 256, 0, stream>>>(T, vocab, k2, n_draft, q_ids, qs, q_probs, W.sel, bonus);
   }
   LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+size_t dflash_path_table_bytes(const dflash_config* cfg) {
+  if (check_config(cfg) != DFLASH_OK) return 0;
+  return static_cast<size_t>(cfg->vocab) * 2 * cfg->ps_dim * sizeof(float);
+}
+
+int dflash_build_path_table(const dflash_config* cfg, const dflash_weights* w, float* table, hipStream_t stream) {
+  int rc;
+  if ((rc = check_config(cfg))) return rc;
+  if (!w || !w->embed || !w->ps_left || !w->ps_right || !table) return DFLASH_E_INVAL;
+  const int d = cfg->d_model, PD = cfg->ps_dim, V = cfg->vocab;
+  if (cfg->dtype == DFLASH_BF16) {
+    SegW<bf16_t> sw{};
+    sw.p[0] = static_cast<const bf16_t*>(w->ps_left);
+    sw.p[1] = static_cast<const bf16_t*>(w->ps_right);
+    sw.off[0] = 0;
+    sw.off[1] = PD;
+    sw.off[2] = 2 * PD;
+    sw.n_seg = 2;
+    sw.K = d;
+    EpiStore<bf16_t> e{sw, table, 2 * PD, STORE};
+    GEMM_CHECK((run_gemm<bf16_t, bf16_t>(static_cast<const bf16_t*>(w->embed), d, nullptr, V, d, 2 * PD / 16, e,
+                                         stream)));
+  } else {
+    SegW<float> sw{};
+    sw.p[0] = static_cast<const float*>(w->ps_left);
+    sw.p[1] = static_cast<const float*>(w->ps_right);
+    sw.off[0] = 0;
+    sw.off[1] = PD;
+    sw.off[2] = 2 * PD;
+    sw.n_seg = 2;
+    sw.K = d;
+    EpiStore<float> e{sw, table, 2 * PD, STORE};
+    GEMM_CHECK((run_gemm<float, float>(static_cast<const float*>(w->embed), d, nullptr, V, d, 2 * PD / 16, e, stream)));
+  }
   return DFLASH_OK;
 }
 

@@ -602,12 +602,17 @@ __device__ __forceinline__ f32x8_t load8_as_f32(const T* p) {
 //   rho[j] = V (gamma_p (.) z_r(candidate j of p))
 //   S[p][a][j] = lam[a] . rho[j]
 // lam and rho are 16 x r products on the fp32 matrix cores (K = PD); S is a plain fp32 dot
-// product over r in order k = 0..r-1.  z: [B][Tn][2*PD] fp32 (left | right halves).
+// product over r in order k = 0..r-1.  z: [B][Tn][2*PD] fp32 (left | right halves), or with
+// table != nullptr the per-token table [V][2*PD] read at the tokens' ids (ids clamped to
+// the vocabulary).
 template <typename T>
 __global__ __launch_bounds__(256) void path_scores_kernel(const float* __restrict__ z, const float* __restrict__ gamma,
                                                           const T* __restrict__ U, const T* __restrict__ Vf, int PD,
                                                           int r, int n_fixed, int P, float* __restrict__ S_out,
-                                                          float* __restrict__ pair_scores) {
+                                                          float* __restrict__ pair_scores,
+                                                          const float* __restrict__ table,
+                                                          const int32_t* __restrict__ cand_ids,
+                                                          const int32_t* __restrict__ block_ids, int V) {
   extern __shared__ float sm[];
   float* lam = sm;                  // [16][r + 1]
   float* rho = sm + 16 * (r + 1);   // [16][r + 1]
@@ -623,12 +628,25 @@ __global__ __launch_bounds__(256) void path_scores_kernel(const float* __restric
     }
     return;
   }
-  const float* zb = z + static_cast<size_t>(b) * Tn * 2 * PD;
-  // left token slot of row a (p = 0: only row 0, the anchor), right token slot of row j
-  const int lslot = p >= 1 ? (p - 1) * 16 + r16 : 16 * P;
-  const int rslot = p * 16 + r16;
-  const float* zl = zb + static_cast<size_t>(lslot) * 2 * PD;
-  const float* zr = zb + static_cast<size_t>(rslot) * 2 * PD + PD;
+  const float* zl;
+  const float* zr;
+  if (table) {
+    // left token of row a (p = 0: only row 0, the anchor), right token of row j
+    const int32_t* cb = cand_ids + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
+    int tl = p >= 1 ? cb[(p - 1) * 16 + r16] : block_ids[static_cast<size_t>(b) * 16];
+    int tr = cb[p * 16 + r16];
+    tl = tl < 0 ? 0 : (tl >= V ? V - 1 : tl);
+    tr = tr < 0 ? 0 : (tr >= V ? V - 1 : tr);
+    zl = table + static_cast<size_t>(tl) * 2 * PD;
+    zr = table + static_cast<size_t>(tr) * 2 * PD + PD;
+  } else {
+    const float* zb = z + static_cast<size_t>(b) * Tn * 2 * PD;
+    // left token slot of row a (p = 0: only row 0, the anchor), right token slot of row j
+    const int lslot = p >= 1 ? (p - 1) * 16 + r16 : 16 * P;
+    const int rslot = p * 16 + r16;
+    zl = zb + static_cast<size_t>(lslot) * 2 * PD;
+    zr = zb + static_cast<size_t>(rslot) * 2 * PD + PD;
+  }
   const float* gm = gamma ? gamma + (static_cast<size_t>(b) * 16 + n_fixed + p) * PD : nullptr;
   const int ntiles = (r + 15) / 16;
   for (int job = wave; job < 2 * ntiles; job += 4) {

@@ -139,6 +139,10 @@ typedef struct dflash_weights {
   dflash_layer_weights layers[DFLASH_MAX_LAYERS];
   const void* cal_w1;     /* [cal_dim, 2d] bonus-calibration MLP, input layer (cal_dim > 0)    */
   const void* cal_w2;     /* [V, cal_dim]  its output layer                                    */
+  const void* ps_table;   /* optional float [V, 2*ps_dim]: every token's embedding projected by
+                             ps_left | ps_right (dflash_build_path_table); when set, the Path
+                             Selector reads its candidates' rows there instead of projecting
+                             their embeddings at each call                                      */
 } dflash_weights;
 
 /* The drafter's KV cache of injected context, one pair of arrays per layer.
@@ -260,6 +264,13 @@ int dflash_select_path(const dflash_config* cfg, const dflash_weights* w,
 int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch,
                   int32_t n_draft, int32_t vocab, int32_t* accept_len, int32_t* bonus,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* The Path Selector's per-token table (a cache of weights, not of activations): row t =
+ * [ps_left E[t] ; ps_right E[t]] in float (fp32 accumulation), for every token of the
+ * vocabulary.  table: device, dflash_path_table_bytes(cfg) bytes.  Needs embed, ps_left,
+ * ps_right.  Rebuild it when those weights change. */
+size_t dflash_path_table_bytes(const dflash_config* cfg);
+int dflash_build_path_table(const dflash_config* cfg, const dflash_weights* w, float* table, hipStream_t stream);
 
 /* Bonus-guided calibration of a drafted block ("FlexDraft", "Metodología" item 2: a
  * light MLP after the LM head turns the resolved bonus token's embedding and a mask

@@ -301,6 +301,35 @@ def test_path_parity(name, n_fixed, mode):
     say(f"  near-tie path differences: {moved}")
 
 
+@pytest.mark.parametrize("name", ["t_small", "t_conv"])
+def test_path_table_and_projection_agree(name):
+    """The per-token table (built once) and the projection of the candidates' embeddings
+    at each call give the same pair scores (fp32 sums in different orders) and paths."""
+    say(f"path table vs projection {name}")
+    wl = synth.workload(name)
+    dims = wl.dims
+    B = 4
+    W = synth.make_weights(dims, wl.seed, ps_scale="stress")
+    ids, lg, xh = synth.make_candidates(dims, B, wl.seed + 5)
+    bids = synth.make_block_ids(dims, B, wl.seed + 5, 1)
+    outs = []
+    for table in (True, False):
+        dr = D.Drafter(dims, W, path_table=table)
+        assert (dr.table is not None) == table
+        pidx = torch.zeros((B, 15), dtype=torch.int32, device="cuda")
+        pids = torch.zeros((B, 15), dtype=torch.int32, device="cuda")
+        ps = torch.zeros((B, 15, 16, 16), dtype=torch.float32, device="cuda")
+        nb = D.dflash_path_workspace_bytes(dr.cfg, B)
+        D.dflash_select_path(dr.cfg, dr.w, dev_i32(ids), torch.from_numpy(lg).cuda(), torch.from_numpy(xh).cuda(),
+                             dev_i32(bids), 1, D.DFLASH_PATH_GREEDY, B, pidx, pids, ps, ws_of(nb), nb)
+        torch.cuda.synchronize()
+        outs.append((pidx.cpu().numpy(), ps.cpu().numpy()))
+    assert H.rowwise_relerr(outs[0][1].reshape(-1, 16), outs[1][1].reshape(-1, 16)) < 1e-5
+    for b in range(B):
+        np.testing.assert_array_equal(outs[0][0][b], H.walk_f32(lg[b, 1:], outs[0][1][b], True, "greedy"))
+        np.testing.assert_array_equal(outs[1][0][b], H.walk_f32(lg[b, 1:], outs[1][1][b], True, "greedy"))
+
+
 # ------------------------------------------------------------------ whole step (tiny workload)
 
 @pytest.mark.parametrize("name", ["c1", "t_conv"])
