@@ -49,6 +49,7 @@ struct AttnArgs {
   float* part_ml;    // [B][Hkv][S][G][16][2]
   T* out;            // [B*16][H*hd]             (S == 1)
   int H, Hkv, cap, S;
+  int B;             // sequences (the split length follows the longest context)
   int bs;            // block rows that are keys (dynamic block size); rows >= bs are padding
   float scale_log2;  // log2(e) / sqrt(hd)
 };
@@ -81,6 +82,14 @@ __device__ __forceinline__ u32x4_t keep_first(u32x4_t v, int n) {
   return v;
 }
 
+// Keys per split: the longest context of the batch (clamped to cap) over S, rounded up to
+// whole tiles.  Computed alike by the attention and the combine kernels.
+__device__ __forceinline__ int split_chunk(const int32_t* ctx_len, int B, int cap, int S, int tk) {
+  int lmax = 0;
+  for (int i = 0; i < B; ++i) lmax = max(lmax, min(max(ctx_len[i], 0), cap));
+  return max(tk, ((lmax + S - 1) / S + tk - 1) / tk * tk);
+}
+
 template <typename T, int HD, int G>
 __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
   typedef Frag<T> F;
@@ -107,9 +116,13 @@ __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
 
   int L = a.ctx_len[b];
   L = L < 0 ? 0 : (L > cap ? cap : L);
-  const int chunk = (((L + S - 1) / S) + TL::TK - 1) / TL::TK * TL::TK;
+  // every sequence of the batch is cut into chunks of the same length (the longest context
+  // over S), so a ragged batch spreads its long contexts over more work-groups; a split
+  // with no context keys has no work unless it is the last (the block's own keys)
+  const int chunk = split_chunk(a.ctx_len, a.B, cap, S, TL::TK);
   const int kbeg = min(L, s * chunk);
   const int kend = min(L, kbeg + chunk);
+  if (kbeg == kend && s != S - 1) return;
   const int ntiles = (kend - kbeg + TL::TK - 1) / TL::TK;
 
   // query fragments of this wave's head
@@ -333,7 +346,8 @@ constexpr int kCombineMaxSplits = 64;
 template <typename T, int HD, int SG, int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, T* __restrict__ out,
-                                                           int H, int Hkv, int S) {
+                                                           int H, int Hkv, int S, const int32_t* __restrict__ ctx_len,
+                                                           int B, int cap, int tk) {
   constexpr int LPR = HD / 8;     // lanes per row
   constexpr int RPW = 64 / LPR;   // rows per wave
   constexpr int RG = 4 / SG;      // row groups per work-group
@@ -346,13 +360,20 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const int G = H / Hkv, kvh = head / G, hl = head % G;
   const size_t sstride = static_cast<size_t>(G) * 16;                                    // rows per split
   const size_t row0 = (static_cast<size_t>(b * Hkv + kvh) * S * G + hl) * 16 + q;        // split 0
+  // splits that wrote partials: those holding context keys, and the last
+  const int L = min(max(ctx_len[b], 0), cap);
+  const int chunk = split_chunk(ctx_len, B, cap, S, tk);
+  const int nctx = (L + chunk - 1) / chunk;
+  auto live = [&](int s) { return s < S && (s < nctx || s == S - 1); };
   float m[NS], l[NS];
   f32x4_t x0[NS], x1[NS];
   float mx = -INFINITY;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     const int s = p + SG * i;
-    if (s < S) {
+    m[i] = -INFINITY;
+    l[i] = 0.f;
+    if (live(s)) {
       const size_t r = row0 + s * sstride;
       m[i] = part_ml[r * 2];
       l[i] = part_ml[r * 2 + 1];
@@ -371,7 +392,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   for (int j = 0; j < 8; ++j) acc[j] = 0.f;
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
-    if (p + SG * i < S) {
+    if (live(p + SG * i)) {
       const float wt = m[i] == -INFINITY ? 0.f : exp2f(m[i] - M);
       den += wt * l[i];
 #pragma unroll

@@ -119,8 +119,14 @@ InjectWs<T> carve_inject(Carver& cv, const dflash_config* c, int rows) {
 // unit over the grid, each split at least two 64-key tiles (so the 32 KB of (O, m, l)
 // partials a split writes stay well below the K/V bytes it reads), at most 64 splits.
 int attn_splits(const dflash_config* c, int batch, int cap) {
+  // about 512 work-groups (two per CU), and at least 4 splits: with many sequences the
+  // longest contexts otherwise set the time (32 x 4096 keys: 2 splits 165 us, 4 splits 143 us)
+  // With 256+ (sequence, kv head) pairs, splits of at most ~1024 keys: every sequence is cut
+  // by the batch's longest context, so in a ragged batch the long contexts spread over more
+  // work-groups while short ones leave splits empty (they exit at once).
   const int pairs = batch * c->n_kv_heads;
-  const int want = (512 + pairs - 1) / pairs;
+  int want = std::max((512 + pairs - 1) / pairs, 4);
+  if (pairs >= 256) want = std::max(want, std::min(cap / 1024, 16));
   const int maxs = cap / 128;
   int s = want < maxs ? want : maxs;
   return s < 1 ? 1 : (s > kCombineMaxSplits ? kCombineMaxSplits : s);
@@ -357,8 +363,8 @@ hipError_t launch_attn(const AttnArgs<T>& a, int B, hipStream_t s) {
 template <typename T, int HD, int SG, int NS>
 hipError_t combine_grid(const AttnArgs<T>& a, int H, int Hkv, int B, hipStream_t s) {
   constexpr int rows_per_block = (64 / (HD / 8)) * (4 / SG);
-  attn_combine_kernel<T, HD, SG, NS><<<dim3(16 / rows_per_block, H, B), 256, 0, s>>>(a.part_o, a.part_ml, a.out, H,
-                                                                                     Hkv, a.S);
+  attn_combine_kernel<T, HD, SG, NS><<<dim3(16 / rows_per_block, H, B), 256, 0, s>>>(
+      a.part_o, a.part_ml, a.out, H, Hkv, a.S, a.ctx_len, B, a.cap, AttnTile<T, HD>::TK);
   return hipGetLastError();
 }
 template <typename T, int HD>
@@ -458,7 +464,7 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
                                W.scratch_bytes, 0, fp8w(c))));
     pr.end(DFLASH_PROBE_QKV);
     AttnArgs<T> aa{W.q, W.kb, W.vbt, static_cast<const T*>(kv->k[l]), static_cast<const T*>(kv->vt[l]), ctx_len,
-                   W.part_o, W.part_ml, W.o, H, Hkv, kv->cap, W.S, c->block_size,
+                   W.part_o, W.part_ml, W.o, H, Hkv, kv->cap, W.S, B, c->block_size,
                    1.4426950408889634f / sqrtf(static_cast<float>(hd))};
     pr.begin(DFLASH_PROBE_ATTN);
     GEMM_CHECK(run_attention<T>(c, aa, B, s));
