@@ -16,7 +16,7 @@
 //    (16 B per lane per fragment, two register stages in flight) and reduce
 //    through LDS in a fixed order.
 //  * gemm_pipe   : bf16 operands (A in bf16), M > 16 (and M <= 16 with K >= 16384).  64/128/256 x 128 output tiles per
-//    work-group of 2x2 waves; 64-wide K slabs stream from memory straight into a ring
+//    work-group of 2x2 or 4x2 waves; 64-wide K slabs stream from memory straight into a ring
 //    of LDS slots with several slabs in flight; tile shape and split-K per GEMM shape.
 //  * gemm_tiled  : M > 64 when gemm_pipe does not apply (fp32, or A given in fp32).
 //    128x128 output tile per work-group, A and W tiles staged through LDS (register
@@ -449,18 +449,21 @@ __device__ __forceinline__ void pipe_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
-template <typename T, int BM, int BN, int NS, class Epi, bool W8>
-__global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A, int lda,
-                                                       const int32_t* __restrict__ arows, int M, int K, Epi epi,
-                                                       int tiles_m, int kslice, float* __restrict__ partial,
-                                                       int ldp) {
+template <typename T, int BM, int BN, int NS, class Epi, bool W8, int NWV>
+__global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict__ A, int lda,
+                                                             const int32_t* __restrict__ arows, int M, int K, Epi epi,
+                                                             int tiles_m, int kslice, float* __restrict__ partial,
+                                                             int ldp) {
   typedef Frag<T> F;
   typedef typename F::type frag_t;
   static_assert(sizeof(T) == 2, "bf16 operands");
   static_assert(NS >= 2 && NS <= 4, "ring of 2..4 slots");
-  constexpr int TM = BM / 32, TN = BN / 32;        // 16x16 tiles per wave
+  static_assert(NWV == 4 || NWV == 8, "2x2 or 4x2 waves");
+  constexpr int WM = NWV / 2;                      // wave rows; 2 wave columns
+  constexpr int TM = BM / (16 * WM), TN = BN / 32; // 16x16 tiles per wave
   // direct loads per thread per slab (W rows of 64 E4M3 codes are half as long)
-  constexpr int LA = BM / 32, LB = W8 ? BN / 64 : BN / 32;
+  constexpr int LA = BM * 8 / (64 * NWV), LB = (W8 ? BN * 4 : BN * 8) / (64 * NWV);
+  static_assert(LA * 64 * NWV == BM * 8 && LB * 64 * NWV == (W8 ? BN * 4 : BN * 8), "loads must tile the slab");
   constexpr int LPS = LA + LB;
   constexpr int STAGE = (BM + (W8 ? BN / 2 : BN)) * 64;      // T elements per slot
   constexpr int EPR = 32 * (BN + 1) * 4 <= STAGE * 2 ? 32 : 16;   // epilogue rows per LDS pass
@@ -472,9 +475,10 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
   const int r16 = lane & 15, g = lane >> 4;
   const int wm = wave >> 1, wn = wave & 1;
   const int mt = blockIdx.x % tiles_m, nt = blockIdx.x / tiles_m;
+  constexpr int WR = BM / WM;                      // rows per wave
   const int m0 = mt * BM, vt0 = nt * (BN / 16);
 
-  // this lane's source chunk for each of its direct loads: LDS block (8 rows) j*4 + wave,
+  // this lane's source chunk for each of its direct loads: LDS block (8 rows) j*NWV + wave,
   // row block*8 + lane/8, position lane%8 <- chunk (lane%8) ^ ((row >> 1) & 7).
   // A: byte offsets from A (rows past M clamped); W: row pointers (past the end: row 0).
   // W8: 16 rows of 4 chunks per LDS block, chunk c of row r at position c ^ ((r >> 2) & 3).
@@ -483,7 +487,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
   const T* w0 = epi.wrow(vt0, 0);
 #pragma unroll
   for (int j = 0; j < LA; ++j) {
-    const int row = (j * 4 + wave) * 8 + (lane >> 3);
+    const int row = (j * NWV + wave) * 8 + (lane >> 3);
     const int ck = (lane & 7) ^ ((row >> 1) & 7);
     const int m = m0 + row < M ? m0 + row : M - 1;
     aoff[j] = static_cast<uint32_t>((static_cast<size_t>(arows ? arows[m] : m) * lda + ck * 8) * sizeof(T));
@@ -491,12 +495,12 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
 #pragma unroll
   for (int j = 0; j < LB; ++j) {
     if constexpr (W8) {
-      const int row = (j * 4 + wave) * 16 + (lane >> 2);
+      const int row = (j * NWV + wave) * 16 + (lane >> 2);
       const int ck = (lane & 3) ^ ((row >> 2) & 3);
       const T* wr = epi.wrow(vt0 + row / 16, row % 16);
       wsrc[j] = reinterpret_cast<const char*>(wr ? wr : w0) + ck * 16;
     } else {
-      const int row = (j * 4 + wave) * 8 + (lane >> 3);
+      const int row = (j * NWV + wave) * 8 + (lane >> 3);
       const int ck = (lane & 7) ^ ((row >> 1) & 7);
       const T* wr = epi.wrow(vt0 + row / 16, row % 16);
       wsrc[j] = reinterpret_cast<const char*>((wr ? wr : w0) + ck * 8);
@@ -506,9 +510,9 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
     const uint32_t base = lds_addr(slot);
     const char* ak = reinterpret_cast<const char*>(A + k0);
 #pragma unroll
-    for (int j = 0; j < LA; ++j) dma16(ak + aoff[j], base + (j * 4 + wave) * 1024);
+    for (int j = 0; j < LA; ++j) dma16(ak + aoff[j], base + (j * NWV + wave) * 1024);
 #pragma unroll
-    for (int j = 0; j < LB; ++j) dma16(wsrc[j] + k0 * (W8 ? 1 : sizeof(T)), base + (BM / 8 + j * 4 + wave) * 1024);
+    for (int j = 0; j < LB; ++j) dma16(wsrc[j] + k0 * (W8 ? 1 : sizeof(T)), base + (BM / 8 + j * NWV + wave) * 1024);
   };
 
   f32x4_t acc[TM][TN];
@@ -518,7 +522,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   const int sw = (r16 >> 1) & 7;
   auto compute = [&](const T* slot) {
-    const T* As = slot + (wm * (BM / 2) + r16) * 64;
+    const T* As = slot + (wm * WR + r16) * 64;
     const T* Bs = slot + (BM + wn * (BN / 2) + r16) * 64;
     frag_t af[2][TM], bf[2][TN];
     if constexpr (W8) {
@@ -590,7 +594,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
       for (int j = 0; j < TN; ++j)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int m = m0 + wm * (BM / 2) + i * 16 + 4 * g + e;
+          const int m = m0 + wm * WR + i * 16 + 4 * g + e;
           if (m < M) pz[static_cast<size_t>(m) * ldp + vt0 * 16 + wn * (BN / 2) + j * 16 + r16] = acc[i][j][e];
         }
     return;
@@ -601,7 +605,7 @@ __global__ __launch_bounds__(256) void gemm_pipe_kernel(const T* __restrict__ A,
   for (int h = 0; h < BM / EPR; ++h) {
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
-      const int r0 = wm * (BM / 2) + i * 16 - h * EPR;
+      const int r0 = wm * WR + i * 16 - h * EPR;
       if (r0 >= 0 && r0 < EPR) {
 #pragma unroll
         for (int j = 0; j < TN; ++j)
@@ -717,7 +721,7 @@ inline BigPlan big_plan(int M, int K, int n_vtiles) {
     return {64, 128, 3, split(tiles, M <= 16 ? 256 : 128, 4)};
   }
   const long t256 = static_cast<long>((M + 255) / 256) * ((N + 127) / 128);
-  if (M >= 384 && t256 >= 256) return {256, 128, 3, 1};
+  if (M >= 256 && t256 >= 256) return {256, 128, 3, 1};
   return {128, 128, 2, t128 >= 256 ? 1 : split(t128, 512, 16)};
 }
 
@@ -780,12 +784,12 @@ static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks,
   }
 }
 
-template <typename T, int BM, int BN, int NS, bool W8, class Epi>
+template <typename T, int BM, int BN, int NS, bool W8, class Epi, int NWV = 4>
 static hipError_t launch_pipe_shape(const T* A, int lda, const int32_t* arows, int M, int K, int n_vtiles,
                                     const Epi& epi, int ks, float* scratch, hipStream_t s) {
   const int tm = (M + BM - 1) / BM, tn = (n_vtiles * 16 + BN - 1) / BN, ldp = tn * BN;
-  gemm_pipe_kernel<T, BM, BN, NS, Epi, W8><<<dim3(tm * tn, ks), 256, 0, s>>>(A, lda, arows, M, K, epi, tm, K / ks,
-                                                                            ks > 1 ? scratch : nullptr, ldp);
+  gemm_pipe_kernel<T, BM, BN, NS, Epi, W8, NWV><<<dim3(tm * tn, ks), 64 * NWV, 0, s>>>(
+      A, lda, arows, M, K, epi, tm, K / ks, ks > 1 ? scratch : nullptr, ldp);
   if (ks > 1) launch_splitk_epilogue(scratch, M, ldp, ks, n_vtiles, epi, s);
   return hipGetLastError();
 }
@@ -796,8 +800,13 @@ static hipError_t launch_big(const T* A, int lda, const int32_t* arows, int M, i
   BigPlan p = big_plan(M, K, n_vtiles);
   const size_t ldp = static_cast<size_t>((n_vtiles * 16 + p.bn - 1) / p.bn) * p.bn;
   if (p.ks > 1 && (!scratch || scratch_bytes < static_cast<size_t>(p.ks) * M * ldp * sizeof(float))) p.ks = 1;
-  if (p.bm == 64) return launch_pipe_shape<T, 64, 128, 3, W8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
-  if (p.bm == 256) return launch_pipe_shape<T, 256, 128, 3, W8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  // 64- and 256-row tiles run 8 waves (two per SIMD: one issues matrix-core work while the
+  // other waits on LDS); warm sweeps at 512 x 151936 x 4096: 1020 -> 826 us, and at
+  // 64 x 24576 x 4096: 41.6 -> 35.6 us
+  if (p.bm == 64)
+    return launch_pipe_shape<T, 64, 128, 3, W8, Epi, 8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 256)
+    return launch_pipe_shape<T, 256, 128, 3, W8, Epi, 8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
   return launch_pipe_shape<T, 128, 128, 2, W8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
 }
 
