@@ -61,6 +61,15 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, const float* Ct, i
   }
 }
 
+// wait until at most N of this wave's memory loads are outstanding and its LDS accesses
+// are done, then a work-group barrier that carries no memory fence
+template <int N>
+__device__ __forceinline__ void pipe_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
+  asm volatile("s_barrier" ::: "memory");
+}
+
 // ---------------------------------------------------------------------------------
 // skinny GEMM
 // ---------------------------------------------------------------------------------
@@ -170,6 +179,82 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
   }
   __shared__ typename Epi::Row rinfo[ROWS];
   epilogue_tile(epi, &tile[0][0], TW + 1, 0, ROWS, vt0, NT, M, rinfo);
+}
+
+// Persistent weight streaming for very wide plain outputs (M <= 16, bf16, K = NW * 32 * KS):
+// one work-group of NW waves per compute unit walks a contiguous range of 16-column tiles.
+// Each wave holds its K slice of A (16 rows x 32 KS) in registers for the whole launch,
+// so the only memory traffic per tile is the weight stream itself (re-reading A for every
+// tile from the caches costs as many load instructions as the weights at one tile per
+// work-group).  Two register buffers of W alternate across tiles: the next tile's loads
+// are in flight while the current one is consumed, reduced over the waves (fixed order,
+// through LDS) and stored.  The barriers carry no memory fence, so tile loads stay in
+// flight across them.  Epilogues: plain per-element ones over a single weight matrix
+// (EpiStore, EpiLogits: epi.w holds one segment).
+template <typename T, int NW, int KS, class Epi>
+__global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restrict__ A, int lda, int M, int n_vtiles,
+                                                              Epi epi) {
+  typedef Frag<T> F;
+  typedef typename F::type frag_t;
+  static_assert(Epi::kDirect && Epi::PX == 0 && Epi::PC == 0, "per-element epilogues only");
+  static_assert(NW * 64 >= 256, "one thread per output of a tile");
+  __shared__ float red[2][NW][256];
+
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r16 = lane & 15, g = lane >> 4;
+  const int k0 = wave * 32 * KS;
+  const int t_beg = static_cast<int>(static_cast<long>(n_vtiles) * blockIdx.x / gridDim.x);
+  const int t_end = static_cast<int>(static_cast<long>(n_vtiles) * (blockIdx.x + 1) / gridDim.x);
+  if (t_beg >= t_end) return;
+
+  // this wave's K slice of A, kept for every tile (rows past M read row 0; never stored)
+  frag_t a[KS];
+  {
+    const T* ap = A + static_cast<size_t>(r16 < M ? r16 : 0) * lda + g * 8 + k0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = F::load(ap + 32 * ks);
+  }
+  // W (one matrix, rows of ldw elements) through one buffer descriptor; tiles past this
+  // range and rows past the matrix read nothing (offset past the descriptor's end)
+  const T* const wbase = epi.w.p[0];
+  const int wrows = epi.w.off[1], ldw = epi.w.K;
+  const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(wrows) * ldw * sizeof(T));
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase, wbytes);
+  auto load = [&](frag_t (&w)[KS], int vt) {
+    const int n = vt * 16 + r16;
+    const uint32_t vo =
+        (vt < t_end && n < wrows) ? static_cast<uint32_t>((static_cast<size_t>(n) * ldw + g * 8 + k0) * sizeof(T)) : wbytes;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) w[ks] = F::load_buf(rw, vo + 32 * ks * sizeof(T), 0);
+  };
+  auto finish = [&](frag_t (&w)[KS], int vt, int par) {
+    f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) acc = F::mma(acc, a[ks], w[ks]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[par][wave][lane * 4 + i] = acc[i];
+    pipe_barrier<63>();
+    if (threadIdx.x < 256) {
+      const int e = threadIdx.x, l = e >> 2, i = e & 3;
+      float s = 0.f;
+#pragma unroll
+      for (int w2 = 0; w2 < NW; ++w2) s += red[par][w2][e];
+      const int m = 4 * (l >> 4) + i;
+      if (m < M) epi.apply(vt, m, typename Epi::Row{}, l & 15, s, 0.f);
+    }
+  };
+  frag_t w0[KS], w1[KS];
+  load(w0, t_beg);
+  load(w1, t_beg + 1);
+  int vt = t_beg;
+  for (; vt + 2 < t_end; vt += 2) {
+    finish(w0, vt, 0);
+    load(w0, vt + 2);
+    finish(w1, vt + 1, 1);
+    load(w1, vt + 3);
+  }
+  finish(w0, vt, 0);
+  if (vt + 1 < t_end) finish(w1, vt + 1, 1);
 }
 
 // FP8-weight variant (one drafted block: M <= 16, A in bf16).  W rows hold E4M3 codes
@@ -438,15 +523,6 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 16 bytes per lane from global address g into LDS at (wave-uniform) byte address lds + 16 * lane
 __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
   asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
-
-// wait until at most N of this wave's memory loads are outstanding and its LDS accesses
-// are done, then a work-group barrier that carries no memory fence
-template <int N>
-__device__ __forceinline__ void pipe_barrier() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (0 << 8));
-  asm volatile("s_barrier" ::: "memory");
 }
 
 template <typename T, int BM, int BN, int NS, class Epi, bool W8, int NWV>
@@ -836,6 +912,19 @@ static hipError_t launch_skinny_w8(const T* A, int lda, const int32_t* arows, in
   return hipGetLastError();
 }
 
+// Work-groups of the persistent streaming kernel: one per compute unit of the current
+// device (queried once per device), never more than there are tiles.
+inline int stream_grid(int n_vtiles) {
+  static int cus[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
+  }
+  return n_vtiles < cus[dev] ? n_vtiles : cus[dev];
+}
+
 // n_vtiles: number of virtual 16-column tiles (multiple of 2 when Epi::PX == 1).
 // K: multiple of 64.  scratch: split-K partials (>= splitk_scratch_bytes, or nullptr: no split).
 // w8: W in FP8 storage (E4M3 rows with a float32 scale; the epilogue's row stride covers
@@ -862,6 +951,15 @@ static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, in
       return launch_big<T, false, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
   }
   if (w8) return hipErrorNotSupported;
+  if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value && Epi::kDirect && Epi::PX == 0 &&
+                Epi::PC == 0) {
+    // very wide plain outputs (the LM head): persistent streaming with A resident in registers
+    if (M <= 16 && !arows && K == 8 * 32 * 16 && n_vtiles >= 2048 && epi.w.n_seg == 1 &&
+        static_cast<size_t>(epi.w.off[1]) * epi.w.K * sizeof(T) < (size_t{1} << 32) - 4096) {
+      gemm_stream_kernel<T, 8, 16, Epi><<<stream_grid(n_vtiles), 512, 0, s>>>(A, lda, M, n_vtiles, epi);
+      return hipGetLastError();
+    }
+  }
   if (M <= 16) return launch_skinny<T, AS, 1>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 32) return launch_skinny<T, AS, 2>(A, lda, arows, M, K, n_vtiles, epi, s);
   if (M <= 64) return launch_skinny<T, AS, 4>(A, lda, arows, M, K, n_vtiles, epi, s);
