@@ -383,7 +383,9 @@ def main():
         except Exception:
             traffic = None
     roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
-    roofline.update({"traffic": traffic, "kernel": f"{dominant} GEMM (gemm_skinny_kernel<..., EpiLogits>)",
+    kname = ("gemm_skinny_kernel" if dims.dtype != "bf16" else
+             "gemm_stream_kernel" if wl.batch == 1 else "gemm_pipe_kernel")
+    roofline.update({"traffic": traffic, "kernel": f"{dominant} GEMM ({kname}<..., EpiLogits>)",
                      "algorithmic_bytes_per_launch": dom.get("algorithmic_bytes"), "ms_per_launch": dom["ms"]})
 
     breakdown = {}

@@ -181,30 +181,42 @@ __global__ __launch_bounds__(64 * NW) void gemm_skinny_kernel(const AS* __restri
   epilogue_tile(epi, &tile[0][0], TW + 1, 0, ROWS, vt0, NT, M, rinfo);
 }
 
-// Persistent weight streaming for very wide plain outputs (M <= 16, bf16, K = NW * 32 * KS):
-// one work-group of NW waves per compute unit walks a contiguous range of 16-column tiles.
-// Each wave holds its K slice of A (16 rows x 32 KS) in registers for the whole launch,
-// so the only memory traffic per tile is the weight stream itself (re-reading A for every
-// tile from the caches costs as many load instructions as the weights at one tile per
-// work-group).  Two register buffers of W alternate across tiles: the next tile's loads
-// are in flight while the current one is consumed, reduced over the waves (fixed order,
-// through LDS) and stored.  The barriers carry no memory fence, so tile loads stay in
-// flight across them.  Epilogues: plain per-element ones over a single weight matrix
-// (EpiStore, EpiLogits: epi.w holds one segment).
+// Persistent weight streaming (M <= 16, bf16, K = NW * 32 * KS): one work-group of NW
+// waves per compute unit walks a contiguous range of 16-column tiles.  Each wave holds its
+// K slice of A (16 rows x 32 KS) in registers for the whole launch, so the only memory
+// traffic per tile is the weight stream itself (re-reading A for every tile from the
+// caches costs as many load instructions as the weights at one tile per work-group).  Two
+// register buffers of W alternate across tiles: the next tile's loads are in flight while
+// the current one is consumed, reduced over the waves (fixed order, through LDS) and
+// handed to the epilogue.  The barriers carry no memory fence, so tile loads stay in
+// flight across them.  The per-row facts of the epilogue are worked out once (the rows do
+// not change from tile to tile).  Plain per-element epilogues over one weight matrix
+// (EpiStore, EpiLogits) apply each sum directly; the others go through an LDS tile that
+// holds each output's partner (a RoPE pair in the tile; with Epi::PX the gate/up pair of
+// two consecutive tiles, so ranges start at even tiles).
+template <class Epi>
+struct StreamPlain {
+  static constexpr bool value = Epi::kDirect && Epi::PX == 0 && Epi::PC == 0;
+};
+
 template <typename T, int NW, int KS, class Epi>
 __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restrict__ A, int lda, int M, int n_vtiles,
                                                               Epi epi) {
   typedef Frag<T> F;
   typedef typename F::type frag_t;
-  static_assert(Epi::kDirect && Epi::PX == 0 && Epi::PC == 0, "per-element epilogues only");
+  constexpr bool kPlain = StreamPlain<Epi>::value;
+  static_assert(Epi::PX == 0 || Epi::PX == 1, "partner tile: none or the pair");
   static_assert(NW * 64 >= 256, "one thread per output of a tile");
   __shared__ float red[2][NW][256];
+  __shared__ float ct[2][16][17];
+  __shared__ typename Epi::Row rinfo[16];
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r16 = lane & 15, g = lane >> 4;
   const int k0 = wave * 32 * KS;
-  const int t_beg = static_cast<int>(static_cast<long>(n_vtiles) * blockIdx.x / gridDim.x);
-  const int t_end = static_cast<int>(static_cast<long>(n_vtiles) * (blockIdx.x + 1) / gridDim.x);
+  const int units = Epi::PX ? n_vtiles / 2 : n_vtiles;
+  const int t_beg = static_cast<int>(static_cast<long>(units) * blockIdx.x / gridDim.x) << Epi::PX;
+  const int t_end = static_cast<int>(static_cast<long>(units) * (blockIdx.x + 1) / gridDim.x) << Epi::PX;
   if (t_beg >= t_end) return;
 
   // this wave's K slice of A, kept for every tile (rows past M read row 0; never stored)
@@ -214,16 +226,32 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) a[ks] = F::load(ap + 32 * ks);
   }
-  // W (one matrix, rows of ldw elements) through one buffer descriptor; tiles past this
-  // range and rows past the matrix read nothing (offset past the descriptor's end)
-  const T* const wbase = epi.w.p[0];
-  const int wrows = epi.w.off[1], ldw = epi.w.K;
-  const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(wrows) * ldw * sizeof(T));
-  const __amdgpu_buffer_rsrc_t rw = make_rsrc(wbase, wbytes);
+  if constexpr (!kPlain) {
+    if (threadIdx.x < 16) rinfo[threadIdx.x] = epi.row(threadIdx.x < M ? threadIdx.x : M - 1);
+    __syncthreads();
+  }
+
+  // W of tile vt through a buffer descriptor over its matrix; tiles past this range and
+  // rows past the matrix read nothing (offset past the descriptor's end)
   auto load = [&](frag_t (&w)[KS], int vt) {
-    const int n = vt * 16 + r16;
-    const uint32_t vo =
-        (vt < t_end && n < wrows) ? static_cast<uint32_t>((static_cast<size_t>(n) * ldw + g * 8 + k0) * sizeof(T)) : wbytes;
+    __amdgpu_buffer_rsrc_t rw;
+    uint32_t vo;
+    if constexpr (kPlain) {
+      const int wrows = epi.w.off[1], ldw = epi.w.K;
+      const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(wrows) * ldw * sizeof(T));
+      rw = make_rsrc(epi.w.p[0], wbytes);
+      const int n = vt * 16 + r16;
+      vo = (vt < t_end && n < wrows) ? static_cast<uint32_t>((static_cast<size_t>(n) * ldw + g * 8 + k0) * sizeof(T))
+                                     : wbytes;
+    } else {
+      const int v = vt < t_end ? vt : t_beg;
+      const T* base;
+      uint32_t bytes;
+      epi.wseg(v, base, bytes);
+      rw = make_rsrc(base, bytes);
+      const T* p = epi.wrow(v, r16);
+      vo = (p && vt < t_end) ? static_cast<uint32_t>((p - base + g * 8 + k0) * sizeof(T)) : bytes;
+    }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) w[ks] = F::load_buf(rw, vo + 32 * ks * sizeof(T), 0);
   };
@@ -234,13 +262,28 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[par][wave][lane * 4 + i] = acc[i];
     pipe_barrier<63>();
-    if (threadIdx.x < 256) {
-      const int e = threadIdx.x, l = e >> 2, i = e & 3;
-      float s = 0.f;
+    const int e = threadIdx.x, l = e >> 2, i = e & 3;
+    float sum = 0.f;
+    if (e < 256) {
 #pragma unroll
-      for (int w2 = 0; w2 < NW; ++w2) s += red[par][w2][e];
+      for (int w2 = 0; w2 < NW; ++w2) sum += red[par][w2][e];
+    }
+    if constexpr (kPlain) {
       const int m = 4 * (l >> 4) + i;
-      if (m < M) epi.apply(vt, m, typename Epi::Row{}, l & 15, s, 0.f);
+      if (e < 256 && m < M) epi.apply(vt, m, typename Epi::Row{}, l & 15, sum, 0.f);
+    } else {
+      if (e < 256) ct[par][4 * (l >> 4) + i][l & 15] = sum;
+      if (Epi::PX && !(vt & 1)) return;   // the gate tile waits for its up tile
+      pipe_barrier<63>();
+      if (e < 256) {
+        const int u = Epi::PX ? vt - 1 : vt;   // the tile the epilogue is called for
+        const bool cm = epi.colmajor(u);
+        const int r = cm ? (e & 15) : (e >> 4), c = cm ? (e >> 4) : (e & 15);
+        if (r < M) {
+          if (Epi::PX) epi.apply(u, r, rinfo[r], c, ct[0][r][c], ct[1][r][c]);
+          else epi.apply(u, r, rinfo[r], c, ct[par][r][c], ct[par][r][c ^ Epi::PC]);
+        }
+      }
     }
   };
   frag_t w0[KS], w1[KS];
@@ -913,7 +956,7 @@ static hipError_t launch_skinny_w8(const T* A, int lda, const int32_t* arows, in
 }
 
 // Work-groups of the persistent streaming kernel: one per compute unit of the current
-// device (queried once per device), never more than there are tiles.
+// device (queried once per device), never more than there are work units.
 inline int stream_grid(int n_vtiles) {
   static int cus[64] = {0};
   int dev = 0;
@@ -951,12 +994,15 @@ static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, in
       return launch_big<T, false, Epi>(A, lda, arows, M, K, n_vtiles, epi, s, scratch, scratch_bytes);
   }
   if (w8) return hipErrorNotSupported;
-  if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value && Epi::kDirect && Epi::PX == 0 &&
-                Epi::PC == 0) {
-    // very wide plain outputs (the LM head): persistent streaming with A resident in registers
-    if (M <= 16 && !arows && K == 8 * 32 * 16 && n_vtiles >= 2048 && epi.w.n_seg == 1 &&
-        static_cast<size_t>(epi.w.off[1]) * epi.w.K * sizeof(T) < (size_t{1} << 32) - 4096) {
-      gemm_stream_kernel<T, 8, 16, Epi><<<stream_grid(n_vtiles), 512, 0, s>>>(A, lda, M, n_vtiles, epi);
+  if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value) {
+    // one drafted block against a wide weight stream (QKV, K/V injection, gate/up, LM head):
+    // persistent streaming with A resident in registers
+    bool ok = M <= 16 && !arows && K == 8 * 32 * 16 && n_vtiles >= 384 && n_vtiles % (Epi::PX + 1) == 0;
+    if constexpr (StreamPlain<Epi>::value)
+      ok = ok && epi.w.n_seg == 1 &&
+           static_cast<size_t>(epi.w.off[1]) * epi.w.K * sizeof(T) < (size_t{1} << 32) - 4096;
+    if (ok) {
+      gemm_stream_kernel<T, 8, 16, Epi><<<stream_grid(n_vtiles >> Epi::PX), 512, 0, s>>>(A, lda, M, n_vtiles, epi);
       return hipGetLastError();
     }
   }
