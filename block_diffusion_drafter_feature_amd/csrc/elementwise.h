@@ -6,9 +6,34 @@
 
 namespace dflash {
 
+// 4 consecutive elements of T as floats / stored from floats (8-byte bf16 or 16-byte fp32
+// accesses; p is 4-element aligned)
+template <typename T>
+__device__ __forceinline__ f32x4_t load4(const T* p) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const f32x4_t*>(p);
+  } else {
+    const uint2 v = *reinterpret_cast<const uint2*>(p);
+    return f32x4_t{__uint_as_float(v.x << 16), __uint_as_float(v.x & 0xffff0000u), __uint_as_float(v.y << 16),
+                   __uint_as_float(v.y & 0xffff0000u)};
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store4(T* p, const float (&u)[4]) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<f32x4_t*>(p) = f32x4_t{u[0], u[1], u[2], u[3]};
+  } else {
+    uint2 v;
+    v.x = static_cast<uint32_t>(from_f<T>(u[0])) | (static_cast<uint32_t>(from_f<T>(u[1])) << 16);
+    v.y = static_cast<uint32_t>(from_f<T>(u[2])) | (static_cast<uint32_t>(from_f<T>(u[3])) << 16);
+    *reinterpret_cast<uint2*>(p) = v;
+  }
+}
+
 // u = x / sqrt(mean(x^2) + eps) * g.  Writes u rounded to T (out_t) and/or in fp32 (out_f).
 // One work-group per row; each thread owns 4-float groups c = tid, tid + 256, ... and issues
-// all of its row loads before reducing (d <= 256 * 4 * 16 per row in one pass of registers).
+// all of its row loads, and the loads of its gains, before reducing (d <= 256 * 4 * 16 per
+// row in one pass of registers), so the row costs one memory round trip before the stores.
 // With emb != nullptr the row is first gathered: x[m] = E[ids[m]] widened to fp32 (and
 // stored to x), then normalised -- the embedding step and the first norm in one pass.
 template <typename T>
@@ -24,17 +49,18 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, con
   const T* er = emb ? emb + static_cast<size_t>(ids[m]) * d : nullptr;
   auto src = [&](int c) {
     if (!er) return xr[c];
-    const f32x4_t t{to_f<T>(er[4 * c]), to_f<T>(er[4 * c + 1]), to_f<T>(er[4 * c + 2]), to_f<T>(er[4 * c + 3])};
+    const f32x4_t t = load4<T>(er + 4 * c);
     xw[c] = t;
     return t;
   };
   const int nv = d >> 2;
-  f32x4_t v[MAXV];
+  f32x4_t v[MAXV], gv[MAXV];
   float ss = 0.f;
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int c = threadIdx.x + 256 * i;
     v[i] = c < nv ? src(c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    gv[i] = c < nv ? load4<T>(g + 4 * c) : f32x4_t{0.f, 0.f, 0.f, 0.f};
   }
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
@@ -44,22 +70,19 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, con
   }
   ss = block_sum(ss, red);
   const float inv = 1.f / sqrtf(ss / d + eps);
-  auto emit = [&](int c, const f32x4_t& t) {
+  auto emit = [&](int c, const f32x4_t& t, const f32x4_t& gg) {
     float u[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) u[e] = t[e] * inv * to_f<T>(g[4 * c + e]);
-    if (out_t) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) out_t[static_cast<size_t>(m) * d + 4 * c + e] = from_f<T>(u[e]);
-    }
+    for (int e = 0; e < 4; ++e) u[e] = t[e] * inv * gg[e];
+    if (out_t) store4<T>(out_t + static_cast<size_t>(m) * d + 4 * c, u);
     if (out_f) *reinterpret_cast<f32x4_t*>(out_f + static_cast<size_t>(m) * d + 4 * c) = f32x4_t{u[0], u[1], u[2], u[3]};
   };
 #pragma unroll
   for (int i = 0; i < MAXV; ++i) {
     const int c = threadIdx.x + 256 * i;
-    if (c < nv) emit(c, v[i]);
+    if (c < nv) emit(c, v[i], gv[i]);
   }
-  for (int c = threadIdx.x + 256 * MAXV; c < nv; c += 256) emit(c, xr[c]);
+  for (int c = threadIdx.x + 256 * MAXV; c < nv; c += 256) emit(c, xr[c], load4<T>(g + 4 * c));
 }
 
 // Dynamic short conv, apply step, for block rows m (row j = m % 16 of its block):
