@@ -213,7 +213,8 @@ __global__ __launch_bounds__(64) void topk_partial_kernel(const float* __restric
 }
 
 // Stage 2: merge the per-chunk lists of each row.  grid (rows), one wave; lane l takes
-// lists l, l + 64, ... (at most 4 per lane).
+// lists l, l + 64, ... (at most 4 per lane), each read as four 16-byte loads.  Whole lists
+// per lane keep the lane maxima high, so few candidates survive the threshold.
 __global__ __launch_bounds__(64) void topk_final_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
                                                         int n_chunks, int32_t* __restrict__ out_ids,
                                                         float* __restrict__ out_vals) {
@@ -228,12 +229,17 @@ __global__ __launch_bounds__(64) void topk_final_kernel(const float* __restrict_
 #pragma unroll
   for (int q = 0; q < LPL; ++q) {
     const int c = lane + 64 * q;
+    const bool ok = c < n_chunks;
+    const size_t o = (static_cast<size_t>(m) * n_chunks + (ok ? c : 0)) * 16;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const bool ok = c < n_chunks;
-      const size_t o = (static_cast<size_t>(m) * n_chunks + (ok ? c : 0)) * 16 + k;
-      v[q * 16 + k] = ok ? pv[o] : -INFINITY;
-      id[q * 16 + k] = ok ? pi[o] : INT_MAX;
+    for (int k4 = 0; k4 < 4; ++k4) {
+      const f32x4_t fv = *reinterpret_cast<const f32x4_t*>(pv + o + 4 * k4);
+      const u32x4_t iv = *reinterpret_cast<const u32x4_t*>(pi + o + 4 * k4);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[q * 16 + 4 * k4 + k] = ok ? fv[k] : -INFINITY;
+        id[q * 16 + 4 * k4 + k] = ok ? static_cast<int>(iv[k]) : INT_MAX;
+      }
     }
   }
   wave_select16<16 * LPL, 512>(v, id, sv, si, ov, oi);
@@ -655,6 +661,8 @@ __global__ __launch_bounds__(256) void path_scores_kernel(const float* __restric
     const int n = nt * 16 + r16;                       // output column (factor index) of this lane
     const T* wrow = (left ? U : Vf) + static_cast<size_t>(n < r ? n : 0) * PD;
     f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+    // unrolled so the loads of several k steps are in flight together (PD = 256: one batch)
+#pragma unroll 8
     for (int k0 = 0; k0 < PD; k0 += 32) {
       const int k = k0 + 8 * g;
       f32x8_t a = Frag<float>::load(left ? zl + k : zr + k);
@@ -674,11 +682,38 @@ __global__ __launch_bounds__(256) void path_scores_kernel(const float* __restric
   {
     const int a = threadIdx.x >> 4, j = threadIdx.x & 15;
     float s = 0.f;
+    // (unrolled so the LDS reads of several k are in flight together; the sum stays in order)
     if (p >= 1 || a == 0)
+#pragma unroll 16
       for (int k = 0; k < r; ++k) s += lam[a * (r + 1) + k] * rho[j * (r + 1) + k];
     So[a * 16 + j] = s;
     if (Po) Po[a * 16 + j] = s;
   }
+}
+
+// The pair scores and candidate logits of sequence b, staged in LDS by the 64 threads of
+// the work-group: every load is issued before the first LDS store (P <= 16 float4 of S and
+// 4 logits per thread), so the staging costs one memory round trip, and the walks then
+// follow their chain of choices through LDS.  Ss: [P][16][16], ls: [P][16].  Ends with a
+// work-group barrier.
+__device__ __forceinline__ void stage_walk(const float* __restrict__ S, const float* __restrict__ lg, int P,
+                                           float* Ss, float* ls) {
+  const int t = threadIdx.x;   // blockDim.x == 64
+  f32x4_t v[16];
+  float l[4];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < P) v[i] = reinterpret_cast<const f32x4_t*>(S)[t + 64 * i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (t + 64 * i < P * 16) l[i] = lg[t + 64 * i];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    if (i < P) reinterpret_cast<f32x4_t*>(Ss)[t + 64 * i] = v[i];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (t + 64 * i < P * 16) ls[t + 64 * i] = l[i];
+  __syncthreads();
 }
 
 // The walk over the pair scores.  grid (B), 64 threads (lanes 0..15 hold one candidate each).
@@ -693,11 +728,13 @@ __global__ __launch_bounds__(64) void path_walk_kernel(const float* __restrict__
   __shared__ float best[16];
   __shared__ int back[16][16];
   __shared__ int chosen[16];
+  __shared__ __align__(16) float S[16 * 256];
+  __shared__ float lg[16 * 16];
   const int b = blockIdx.x;
+  stage_walk(S_in + static_cast<size_t>(b) * P * 256, cand_logits + (static_cast<size_t>(b) * 16 + n_fixed) * 16, P,
+             S, lg);
   if (threadIdx.x >= 16) return;
   const int j = threadIdx.x;
-  const float* S = S_in + static_cast<size_t>(b) * P * 256;
-  const float* lg = cand_logits + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
   const int32_t* ci = cand_ids + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
   auto argmax16 = [&](float v, int& bi) {
     float bv = v;
@@ -773,11 +810,13 @@ __global__ __launch_bounds__(64) void path_sample_kernel(const float* __restrict
                                                          int32_t* __restrict__ path_idx,
                                                          int32_t* __restrict__ path_ids,
                                                          float* __restrict__ path_q) {
+  __shared__ __align__(16) float S[16 * 256];
+  __shared__ float lg[16 * 16];
   const int b = blockIdx.x;
+  stage_walk(S_in + static_cast<size_t>(b) * P * 256, cand_logits + (static_cast<size_t>(b) * 16 + n_fixed) * 16, P,
+             S, lg);
   if (threadIdx.x >= 16) return;
   const int j = threadIdx.x;
-  const float* S = S_in + static_cast<size_t>(b) * P * 256;
-  const float* lg = cand_logits + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
   const int32_t* ci = cand_ids + (static_cast<size_t>(b) * 16 + n_fixed) * 16;
   int c = 0;
   for (int p = 0; p < P; ++p) {
