@@ -529,7 +529,7 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
                                    W.scratch_bytes)));
   }
   const size_t smem = 2 * 16 * (c->ps_rank + 1) * sizeof(float);
-  path_scores_kernel<T><<<dim3(P, B), 256, smem, s>>>(W.z, c->use_gate ? W.gamma : nullptr,
+  path_scores_kernel<T><<<dim3(P, B), 512, smem, s>>>(W.z, c->use_gate ? W.gamma : nullptr,
                                                       static_cast<const T*>(w->ps_u), static_cast<const T*>(w->ps_v),
                                                       PD, c->ps_rank, n_fixed, P, W.S, pair_scores, table,
                                                       cand_ids, block_ids, c->vocab);

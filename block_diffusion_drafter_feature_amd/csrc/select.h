@@ -603,7 +603,8 @@ __device__ __forceinline__ f32x8_t load8_as_f32(const T* p) {
   }
 }
 
-// Pair scores of one drafted position p of one sequence.  grid (P, B), 256 threads.
+// Pair scores of one drafted position p of one sequence.  grid (P, B), 512 threads (8 waves:
+// one 16-factor tile of U or V per wave at rank 64, so the factor loads are one round trip).
 //   lam[a] = U z_l(left token a)                 (left tokens: candidates of p-1, or the anchor at p = 0)
 //   rho[j] = V (gamma_p (.) z_r(candidate j of p))
 //   S[p][a][j] = lam[a] . rho[j]
@@ -612,7 +613,7 @@ __device__ __forceinline__ f32x8_t load8_as_f32(const T* p) {
 // table != nullptr the per-token table [V][2*PD] read at the tokens' ids (ids clamped to
 // the vocabulary).
 template <typename T>
-__global__ __launch_bounds__(256) void path_scores_kernel(const float* __restrict__ z, const float* __restrict__ gamma,
+__global__ __launch_bounds__(512) void path_scores_kernel(const float* __restrict__ z, const float* __restrict__ gamma,
                                                           const T* __restrict__ U, const T* __restrict__ Vf, int PD,
                                                           int r, int n_fixed, int P, float* __restrict__ S_out,
                                                           float* __restrict__ pair_scores,
@@ -655,7 +656,8 @@ __global__ __launch_bounds__(256) void path_scores_kernel(const float* __restric
   }
   const float* gm = gamma ? gamma + (static_cast<size_t>(b) * 16 + n_fixed + p) * PD : nullptr;
   const int ntiles = (r + 15) / 16;
-  for (int job = wave; job < 2 * ntiles; job += 4) {
+  const int nwaves = blockDim.x >> 6;   // 8: one 16-factor tile per wave at rank 64
+  for (int job = wave; job < 2 * ntiles; job += nwaves) {
     const bool left = job < ntiles;
     const int nt = left ? job : job - ntiles;
     const int n = nt * 16 + r16;                       // output column (factor index) of this lane
@@ -683,11 +685,13 @@ __global__ __launch_bounds__(256) void path_scores_kernel(const float* __restric
     const int a = threadIdx.x >> 4, j = threadIdx.x & 15;
     float s = 0.f;
     // (unrolled so the LDS reads of several k are in flight together; the sum stays in order)
-    if (p >= 1 || a == 0)
+    if (a < 16 && (p >= 1 || a == 0))
 #pragma unroll 16
       for (int k = 0; k < r; ++k) s += lam[a * (r + 1) + k] * rho[j * (r + 1) + k];
-    So[a * 16 + j] = s;
-    if (Po) Po[a * 16 + j] = s;
+    if (a < 16) {
+      So[a * 16 + j] = s;
+      if (Po) Po[a * 16 + j] = s;
+    }
   }
 }
 
