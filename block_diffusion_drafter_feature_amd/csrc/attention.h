@@ -5,8 +5,8 @@
 // full over the context; cache rows >= L_b are never read into the result).
 //
 // Work split: one work-group of four waves per (split s, kv head, sequence).  The
-// context rows of a sequence are cut into S splits of whole 64-key tiles; the last
-// split also takes the 16 block keys.  Each wave owns one query head of the GQA
+// context rows of a sequence are cut into SC splits of whole 64-key tiles; the last of
+// the S splits takes the 16 block keys (alone when SC = S - 1).  Each wave owns one query head of the GQA
 // group (16 query rows); with G < 4 heads per kv head, the 4/G waves of a head
 // share its 32-key slabs round-robin and are merged through LDS at the end.
 //
@@ -52,6 +52,7 @@ struct AttnArgs {
   int B;             // sequences (the split length follows the longest context)
   int bs;            // block rows that are keys (dynamic block size); rows >= bs are padding
   float scale_log2;  // log2(e) / sqrt(hd)
+  int SC;            // context splits: S, or S - 1 when the last split holds only the block keys
 };
 
 // LDS tile geometry (elements of T)
@@ -82,12 +83,15 @@ __device__ __forceinline__ u32x4_t keep_first(u32x4_t v, int n) {
   return v;
 }
 
-// Keys per split: the longest context of the batch (clamped to cap) over S, rounded up to
-// whole tiles.  Computed alike by the attention and the combine kernels.
-__device__ __forceinline__ int split_chunk(const int32_t* ctx_len, int B, int cap, int S, int tk) {
+// Keys per split: the longest context of the batch (clamped to cap) over the SC context
+// splits, rounded up to whole tiles.  With SC = S - 1 the last split gets no context and
+// holds only the block's 16 keys, so no work-group has a second memory round trip (the
+// block keys) after its context tiles; with SC = S the last split takes both.  Computed
+// alike by the attention and the combine kernels.
+__device__ __forceinline__ int split_chunk(const int32_t* ctx_len, int B, int cap, int SC, int tk) {
   int lmax = 0;
   for (int i = 0; i < B; ++i) lmax = max(lmax, min(max(ctx_len[i], 0), cap));
-  return max(tk, ((lmax + S - 1) / S + tk - 1) / tk * tk);
+  return max(tk, ((lmax + SC - 1) / SC + tk - 1) / tk * tk);
 }
 
 template <typename T, int HD, int G>
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
   // every sequence of the batch is cut into chunks of the same length (the longest context
   // over S), so a ragged batch spreads its long contexts over more work-groups; a split
   // with no context keys has no work unless it is the last (the block's own keys)
-  const int chunk = split_chunk(a.ctx_len, a.B, cap, S, TL::TK);
+  const int chunk = split_chunk(a.ctx_len, a.B, cap, a.SC, TL::TK);
   const int kbeg = min(L, s * chunk);
   const int kend = min(L, kbeg + chunk);
   if (kbeg == kend && s != S - 1) return;
@@ -347,7 +351,7 @@ template <typename T, int HD, int SG, int NS>
 __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restrict__ part_o,
                                                            const float* __restrict__ part_ml, T* __restrict__ out,
                                                            int H, int Hkv, int S, const int32_t* __restrict__ ctx_len,
-                                                           int B, int cap, int tk) {
+                                                           int B, int cap, int tk, int SC) {
   constexpr int LPR = HD / 8;     // lanes per row
   constexpr int RPW = 64 / LPR;   // rows per wave
   constexpr int RG = 4 / SG;      // row groups per work-group
@@ -362,7 +366,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(const float* __restri
   const size_t row0 = (static_cast<size_t>(b * Hkv + kvh) * S * G + hl) * 16 + q;        // split 0
   // splits that wrote partials: those holding context keys, and the last
   const int L = min(max(ctx_len[b], 0), cap);
-  const int chunk = split_chunk(ctx_len, B, cap, S, tk);
+  const int chunk = split_chunk(ctx_len, B, cap, SC, tk);
   const int nctx = (L + chunk - 1) / chunk;
   auto live = [&](int s) { return s < S && (s < nctx || s == S - 1); };
   float m[NS], l[NS];

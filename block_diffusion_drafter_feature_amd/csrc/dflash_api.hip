@@ -130,7 +130,16 @@ int attn_splits(const dflash_config* c, int batch, int cap) {
   if (pairs >= 256) want = std::max(want, std::min(cap / 1024, 16));
   const int maxs = cap / 256;
   int s = want < maxs ? want : maxs;
-  return s < 1 ? 1 : (s > kCombineMaxSplits ? kCombineMaxSplits : s);
+  s = s < 1 ? 1 : (s > kCombineMaxSplits ? kCombineMaxSplits : s);
+  // a small grid (latency-bound: batch 1) gives the block's own keys a split of their own
+  if (s > 1 && s < kCombineMaxSplits && pairs * (s + 1) <= 256) ++s;
+  return s;
+}
+
+// Context splits of a launch with S splits (see attn_splits): S - 1 when the last split
+// holds only the block keys.
+int attn_ctx_splits(const dflash_config* c, int batch, int cap, int S) {
+  return S > 1 && batch * c->n_kv_heads * S <= 256 ? S - 1 : S;
 }
 
 template <typename T>
@@ -151,7 +160,7 @@ struct DraftWs {
   int32_t* tk_i;
   float* scratch;
   size_t scratch_bytes;
-  int S;
+  int S, SC;
 };
 template <typename T>
 DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
@@ -159,6 +168,7 @@ DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
   const size_t M = 16 * static_cast<size_t>(B), d = c->d_model, hq = static_cast<size_t>(c->n_heads) * c->head_dim;
   const int G = c->n_heads / c->n_kv_heads;
   w.S = attn_splits(c, B, cap);
+  w.SC = attn_ctx_splits(c, B, cap, w.S);
   const int nch = (c->vocab + kTopkChunk - 1) / kTopkChunk;
   w.x = cv.take<float>(M * d);
   w.uf = cv.take<float>(M * d);
@@ -365,7 +375,7 @@ template <typename T, int HD, int SG, int NS>
 hipError_t combine_grid(const AttnArgs<T>& a, int H, int Hkv, int B, hipStream_t s) {
   constexpr int rows_per_block = (64 / (HD / 8)) * (4 / SG);
   attn_combine_kernel<T, HD, SG, NS><<<dim3(16 / rows_per_block, H, B), 256, 0, s>>>(
-      a.part_o, a.part_ml, a.out, H, Hkv, a.S, a.ctx_len, B, a.cap, AttnTile<T, HD>::TK);
+      a.part_o, a.part_ml, a.out, H, Hkv, a.S, a.ctx_len, B, a.cap, AttnTile<T, HD>::TK, a.SC);
   return hipGetLastError();
 }
 template <typename T, int HD>
@@ -467,6 +477,7 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
     AttnArgs<T> aa{W.q, W.kb, W.vbt, static_cast<const T*>(kv->k[l]), static_cast<const T*>(kv->vt[l]), ctx_len,
                    W.part_o, W.part_ml, W.o, H, Hkv, kv->cap, W.S, B, c->block_size,
                    1.4426950408889634f / sqrtf(static_cast<float>(hd))};
+    aa.SC = W.SC;
     pr.begin(DFLASH_PROBE_ATTN);
     GEMM_CHECK(run_attention<T>(c, aa, B, s));
     pr.end(DFLASH_PROBE_ATTN);
