@@ -68,9 +68,12 @@ def parse():
 
 # ------------------------------------------------------------------ algorithmic work per probed kernel
 
-def kernel_work(dims, batch, ctx_lens, fp8=False):
+def kernel_work(dims, batch, ctx_lens, fp8=False, lists=0):
     """(bytes, flops) each probed kernel must move / compute at minimum, per launch.  With
-    fp8, the streamed projections are read in FP8 storage (cols + 16 bytes per row)."""
+    fp8, the streamed projections are read in FP8 storage (cols + 16 bytes per row).  With
+    lists > 0 the LM head keeps per-work-group top-16 lists instead of writing the logits
+    (one drafted block, bf16 weights): it writes lists x 16 (value, id) pairs per row, which
+    the top-16 merge reads back."""
     e = 2 if dims.dtype == "bf16" else 4
     d, H, Hkv, hd, F, V = dims.d, dims.n_heads, dims.n_kv_heads, dims.head_dim, dims.d_ffn, dims.vocab
     M = 16 * batch
@@ -80,7 +83,7 @@ def kernel_work(dims, batch, ctx_lens, fp8=False):
     def wb(rows, cols):
         return rows * (cols + 16) if fp8 else rows * cols * e
     w = {
-        "lm_head": (wb(V, d) + M * d * e + M * V * 4, 2 * M * V * d),
+        "lm_head": (wb(V, d) + M * d * e + (M * lists * 16 * 8 if lists else M * V * 4), 2 * M * V * d),
         "qkv": (wb(hq + 2 * hk, d) + M * d * e + M * (hq + 2 * hk) * e, 2 * M * (hq + 2 * hk) * d),
         "o": (wb(d, hq) + M * hq * e + 2 * M * d * 4, 2 * M * d * hq),
         "gate_up": (wb(2 * F, d) + M * d * e + M * F * e, 2 * M * 2 * F * d),
@@ -88,7 +91,7 @@ def kernel_work(dims, batch, ctx_lens, fp8=False):
         # block attention of one layer: every context K and V row once, plus q, block k/v, o
         "attn": (2 * kv_rows * hk * e + M * hq * e * 2 + 2 * M * hk * e,
                  2 * 2 * batch * 16 * H * hd * (sum(ctx_lens) / max(batch, 1) + 16)),
-        "topk": (M * V * 4, 0),
+        "topk": (M * lists * 16 * 8 if lists else M * V * 4, 0),
         "inject_fc": (wb(d, dims.d_cat) + M * dims.d_cat * e + M * d * 4, 2 * M * d * dims.d_cat),
         "inject_kv": (dims.n_layers * wb(2 * hk, d) + M * d * e + M * dims.n_layers * 2 * hk * e,
                       2 * M * dims.n_layers * 2 * hk * d),
@@ -334,7 +337,12 @@ def main():
                              ws_p, nb_p)
         D.dflash_verify(pids, T, tdt, B, 15, dims.vocab, acc, bon, ws_v, nb_v)
 
-    work = kernel_work(dims, B, wl.ctx_lens)
+    # the library's streaming LM head (one drafted block, bf16) runs one work-group per
+    # compute unit, each keeping its own top-16 lists (at most 256 of them)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    lists = min(cus, dims.vocab // 16) if (dims.dtype == "bf16" and B == 1 and dims.d == 4096
+                                           and dims.vocab // 16 >= 384 and cus <= 256) else 0
+    work = kernel_work(dims, B, wl.ctx_lens, lists=lists)
     dominant = "lm_head"
     # live kernel probes on every PROBE_EVERY-th timed step (each probe adds event records
     # to the stream, ~5 us apiece); the average is over the probed steps of the timed region
@@ -385,7 +393,8 @@ def main():
     roofline = {k: dom[k] for k in ("bound", "achieved", "peak", "unit", "frac")}
     kname = ("gemm_skinny_kernel" if dims.dtype != "bf16" else
              "gemm_stream_kernel" if wl.batch == 1 else "gemm_pipe_kernel")
-    roofline.update({"traffic": traffic, "kernel": f"{dominant} GEMM ({kname}<..., EpiLogits>)",
+    epi = "EpiLogitsTop16" if lists else "EpiLogits"
+    roofline.update({"traffic": traffic, "kernel": f"{dominant} GEMM ({kname}<..., {epi}>)",
                      "algorithmic_bytes_per_launch": dom.get("algorithmic_bytes"), "ms_per_launch": dom["ms"]})
 
     breakdown = {}

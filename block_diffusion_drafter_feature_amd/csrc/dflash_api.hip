@@ -20,6 +20,7 @@ namespace {
 constexpr size_t kAlign = 256;
 constexpr int kTopkChunk = kTopkWaveChunk;   // vocabulary columns per top-k wave
 constexpr int kArgmaxChunk = 8192;   // vocabulary columns per argmax work-group
+constexpr int kTopkFinalLists = 256;  // lists topk_final_kernel merges per row (64 lanes x 4)
 
 size_t align_up(size_t n) { return (n + kAlign - 1) / kAlign * kAlign; }
 
@@ -182,8 +183,11 @@ DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
   w.delta = cv.take<float>(M * 2 * (d / 16));
   w.h = cv.take<T>(M * c->d_ffn);
   w.logits = cv.take<float>(M * c->vocab);
-  w.tk_v = cv.take<float>(M * nch * 16);
-  w.tk_i = cv.take<int32_t>(M * nch * 16);
+  // top-16 partial lists: one per vocabulary chunk, or one per LM-head work-group when
+  // the first stage runs in the streaming LM head (at most kTopkFinalLists)
+  const size_t ntk = std::max<size_t>(nch, kTopkFinalLists);
+  w.tk_v = cv.take<float>(M * ntk * 16);
+  w.tk_i = cv.take<int32_t>(M * ntk * 16);
   const int Mi = static_cast<int>(M), di = c->d_model, hqi = c->n_heads * c->head_dim;
   const int hki = c->n_kv_heads * c->head_dim, F = c->d_ffn;
   size_t sc = 0;
@@ -494,15 +498,28 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
   rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(w->g_final), d, c->rms_eps, W.ut, final_hidden);
   LAUNCH_CHECK();
   float* lg = logits ? logits : W.logits;
-  EpiLogits<T> el{{seg1<T>(w->lm_head, V, wstride(c, d)), lg, V, STORE}};
+  // one drafted block with bf16 weights: the streaming LM head keeps each work-group's top 16
+  // per row (the logits are written only when the caller asks for them); otherwise the
+  // logits go to memory and a chunked first stage reads them back
+  int groups = 0;
   P0.begin(DFLASH_PROBE_LM_HEAD);
-  GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, V / 16, el, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
+  if (!fp8w(c)) {
+    EpiLogitsTop16<T> et{{seg1<T>(w->lm_head, V, wstride(c, d)), logits, V, STORE}, W.tk_v, W.tk_i};
+    groups = run_lm_head_top16<T>(W.ut, d, M, d, V / 16, et, kTopkFinalLists, s);
+    if (groups < 0) return DFLASH_E_HIP;
+  }
+  if (groups == 0) {
+    EpiLogits<T> el{{seg1<T>(w->lm_head, V, wstride(c, d)), lg, V, STORE}};
+    GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, V / 16, el, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
+  }
   P0.end(DFLASH_PROBE_LM_HEAD);
-  const int nch = (V + kTopkChunk - 1) / kTopkChunk;
   P0.begin(DFLASH_PROBE_TOPK);
-  topk_partial_kernel<<<dim3(nch, M), 64, 0, s>>>(lg, V, V, W.tk_v, W.tk_i);
-  LAUNCH_CHECK();
-  topk_final_kernel<<<M, 64, 0, s>>>(W.tk_v, W.tk_i, nch, cand_ids, cand_logits);
+  if (groups == 0) {
+    groups = (V + kTopkChunk - 1) / kTopkChunk;
+    topk_partial_kernel<<<dim3(groups, M), 64, 0, s>>>(lg, V, V, W.tk_v, W.tk_i);
+    LAUNCH_CHECK();
+  }
+  topk_final_kernel<<<M, 64, 0, s>>>(W.tk_v, W.tk_i, groups, cand_ids, cand_logits);
   LAUNCH_CHECK();
   P0.end(DFLASH_PROBE_TOPK);
   return DFLASH_OK;

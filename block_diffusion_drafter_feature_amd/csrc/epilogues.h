@@ -10,6 +10,7 @@
 //                     stores): the kernels then hand consecutive rows to consecutive threads
 //   kDirect           true when Row is empty and no tile is colmajor (plain per-element
 //                     epilogues need no staging tile)
+//   kTop16            the streaming LM head keeps per-work-group top-16 lists (EpiLogitsTop16)
 //   apply(vt, m, row, c, v, partner)
 #pragma once
 
@@ -49,6 +50,7 @@ struct EpiStore {
   int mode;
   static constexpr int PX = 0, PC = 0;
   static constexpr bool kDirect = true;
+  static constexpr bool kTop16 = false;
   __device__ __forceinline__ const T* wrow(int vt, int c) const {
     const int n = vt * 16 + c;
     if (n >= w.off[w.n_seg]) return nullptr;
@@ -85,6 +87,17 @@ struct EpiStore {
 template <typename T>
 struct EpiLogits : EpiStore<T> {};
 
+// LM head of one drafted block with the first top-16 stage folded in (streaming kernel
+// only): every work-group keeps the running top 16 of its columns for each row (value
+// descending, then column ascending) and writes them to tk_v / tk_i [M][groups][16]; the
+// logits themselves are stored only when `out` is non-null.
+template <typename T>
+struct EpiLogitsTop16 : EpiStore<T> {
+  float* tk_v;
+  int32_t* tk_i;
+  static constexpr bool kTop16 = true;
+};
+
 // ------------------------------------------------------------------ block Q/K/V with RoPE
 
 template <typename T>
@@ -100,6 +113,7 @@ struct EpiQKV {
   T* vbt;                  // [B][Hkv][hd][16]
   static constexpr int PX = 0, PC = 8;
   static constexpr bool kDirect = false;
+  static constexpr bool kTop16 = false;
   // virtual tiles: H*hd/16 query tiles, Hkv*hd/16 key tiles (both RoPE-paired), Hkv*hd/16 value tiles
   __device__ __forceinline__ const T* wrow(int vt, int c) const {
     const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
@@ -160,6 +174,7 @@ struct EpiInject {
   const int32_t* n_new;    // [B]
   static constexpr int PX = 0, PC = 8;
   static constexpr bool kDirect = false;
+  static constexpr bool kTop16 = false;
   // virtual tiles per layer: Hkv*hd/16 key tiles (RoPE-paired) then Hkv*hd/16 value tiles
   __device__ __forceinline__ const T* wrow(int vt, int c) const {
     const int tk = Hkv * hd / 16, tph = hd / 16;
@@ -225,6 +240,7 @@ struct EpiSwiGLU {
   T* h;  // [M][Fd]
   static constexpr int PX = 1, PC = 0;
   static constexpr bool kDirect = true;
+  static constexpr bool kTop16 = false;
   __device__ __forceinline__ const T* wrow(int vt, int c) const {
     const int n = (vt >> 1) * 16 + c;
     if (n >= Fd) return nullptr;

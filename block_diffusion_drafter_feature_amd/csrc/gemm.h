@@ -26,6 +26,7 @@
 #pragma once
 
 #include "common.h"
+#include <limits.h>
 #include <type_traits>
 
 namespace dflash {
@@ -217,6 +218,29 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
   const int units = Epi::PX ? n_vtiles / 2 : n_vtiles;
   const int t_beg = static_cast<int>(static_cast<long>(units) * blockIdx.x / gridDim.x) << Epi::PX;
   const int t_end = static_cast<int>(static_cast<long>(units) * (blockIdx.x + 1) / gridDim.x) << Epi::PX;
+
+  // running top 16 of this work-group's columns per row (kTop16): list[p] is written by the
+  // tiles of parity p; entries start as distinct empties (-inf, ids above every column)
+  __shared__ float tl_v[Epi::kTop16 ? 2 : 1][16][16];
+  __shared__ int tl_i[Epi::kTop16 ? 2 : 1][16][16];
+  __shared__ float tc_v[Epi::kTop16 ? 2 : 1][16][16];
+  if constexpr (Epi::kTop16) {
+    if (threadIdx.x < 256) {
+      tl_v[1][threadIdx.x >> 4][threadIdx.x & 15] = -INFINITY;
+      tl_i[1][threadIdx.x >> 4][threadIdx.x & 15] = INT_MAX - 16 - (threadIdx.x & 15);
+    }
+    if (t_beg >= t_end) {   // no columns: an empty list
+      if (threadIdx.x < 256) {
+        const int r = threadIdx.x >> 4, j = threadIdx.x & 15;
+        if (r < M) {
+          const size_t o = (static_cast<size_t>(r) * gridDim.x + blockIdx.x) * 16 + j;
+          epi.tk_v[o] = -INFINITY;
+          epi.tk_i[o] = INT_MAX - 16 - j;
+        }
+      }
+      return;
+    }
+  }
   if (t_beg >= t_end) return;
 
   // this wave's K slice of A, kept for every tile (rows past M read row 0; never stored)
@@ -268,7 +292,39 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
 #pragma unroll
       for (int w2 = 0; w2 < NW; ++w2) sum += red[par][w2][e];
     }
-    if constexpr (kPlain) {
+    if constexpr (Epi::kTop16) {
+      // store the logits if asked, then merge this tile's 16 candidates of each row into the
+      // running list: every entry's rank in the union (16 old + 16 new, all distinct keys)
+      // is counted exactly, and the 16 best land in their places of the other list
+      const int m = 4 * (l >> 4) + i, c = l & 15;
+      if (e < 256) {
+        if (epi.out && m < M) epi.apply(vt, m, typename Epi::Row{}, c, sum, 0.f);
+        tc_v[par][m][c] = vt * 16 + c < epi.w.off[1] ? sum : -INFINITY;
+      }
+      pipe_barrier<63>();
+      if (e < 256) {
+        const int r = e >> 4, j = e & 15;
+        auto nid = [&](int k) { return vt * 16 + k < epi.w.off[1] ? vt * 16 + k : INT_MAX - k; };
+        const float ov = tl_v[par ^ 1][r][j], nv = tc_v[par][r][j];
+        const int oi = tl_i[par ^ 1][r][j], ni = nid(j);
+        int ro = j, rn = 0;
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const float ck = tc_v[par][r][k], lk = tl_v[par ^ 1][r][k];
+          const int cik = nid(k), lik = tl_i[par ^ 1][r][k];
+          ro += better(ck, cik, ov, oi) ? 1 : 0;
+          rn += (better(ck, cik, nv, ni) ? 1 : 0) + (better(lk, lik, nv, ni) ? 1 : 0);
+        }
+        if (ro < 16) {
+          tl_v[par][r][ro] = ov;
+          tl_i[par][r][ro] = oi;
+        }
+        if (rn < 16) {
+          tl_v[par][r][rn] = nv;
+          tl_i[par][r][rn] = ni;
+        }
+      }
+    } else if constexpr (kPlain) {
       const int m = 4 * (l >> 4) + i;
       if (e < 256 && m < M) epi.apply(vt, m, typename Epi::Row{}, l & 15, sum, 0.f);
     } else {
@@ -297,7 +353,19 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
     load(w1, vt + 3);
   }
   finish(w0, vt, 0);
+  const int last_par = vt + 1 < t_end ? 1 : 0;
   if (vt + 1 < t_end) finish(w1, vt + 1, 1);
+  if constexpr (Epi::kTop16) {
+    pipe_barrier<63>();
+    if (threadIdx.x < 256) {
+      const int r = threadIdx.x >> 4, j = threadIdx.x & 15;
+      if (r < M) {
+        const size_t o = (static_cast<size_t>(r) * gridDim.x + blockIdx.x) * 16 + j;
+        epi.tk_v[o] = tl_v[last_par][r][j];
+        epi.tk_i[o] = tl_i[last_par][r][j];
+      }
+    }
+  }
 }
 
 // FP8-weight variant (one drafted block: M <= 16, A in bf16).  W rows hold E4M3 codes
@@ -968,6 +1036,35 @@ inline int stream_grid(int n_vtiles) {
   return n_vtiles < cus[dev] ? n_vtiles : cus[dev];
 }
 
+// One drafted block against a wide weight stream (QKV, K/V injection, gate/up, LM head):
+// run_gemm takes the persistent streaming kernel, A resident in registers (bf16 weights).
+template <typename T, class Epi>
+inline bool stream_ok(int M, int K, int n_vtiles, const int32_t* arows, const Epi& epi) {
+  if (!std::is_same<T, bf16_t>::value) return false;
+  bool ok = M >= 1 && M <= 16 && !arows && K == 8 * 32 * 16 && n_vtiles >= 384 && n_vtiles % (Epi::PX + 1) == 0;
+  if constexpr (StreamPlain<Epi>::value)
+    ok = ok && epi.w.n_seg == 1 && static_cast<size_t>(epi.w.off[1]) * epi.w.K * sizeof(T) < (size_t{1} << 32) - 4096;
+  return ok;
+}
+
+// The LM head of one drafted block with the first top-16 stage in its epilogue: returns
+// the number of per-work-group lists written to epi.tk_v / tk_i ([M][groups][16]), or 0
+// when the streaming kernel does not apply or would use more than max_groups work-groups
+// (nothing is launched then).
+template <typename T>
+static int run_lm_head_top16(const T* A, int lda, int M, int K, int n_vtiles, const EpiLogitsTop16<T>& epi,
+                             int max_groups, hipStream_t s) {
+  if constexpr (std::is_same<T, bf16_t>::value) {
+    if (!stream_ok<T>(M, K, n_vtiles, nullptr, epi)) return 0;
+    const int groups = stream_grid(n_vtiles);
+    if (groups > max_groups) return 0;
+    gemm_stream_kernel<T, 8, 16, EpiLogitsTop16<T>><<<groups, 512, 0, s>>>(A, lda, M, n_vtiles, epi);
+    return hipGetLastError() == hipSuccess ? groups : -1;
+  } else {
+    return 0;
+  }
+}
+
 // n_vtiles: number of virtual 16-column tiles (multiple of 2 when Epi::PX == 1).
 // K: multiple of 64.  scratch: split-K partials (>= splitk_scratch_bytes, or nullptr: no split).
 // w8: W in FP8 storage (E4M3 rows with a float32 scale; the epilogue's row stride covers
@@ -995,13 +1092,7 @@ static hipError_t run_gemm(const AS* A, int lda, const int32_t* arows, int M, in
   }
   if (w8) return hipErrorNotSupported;
   if constexpr (std::is_same<T, bf16_t>::value && std::is_same<AS, T>::value) {
-    // one drafted block against a wide weight stream (QKV, K/V injection, gate/up, LM head):
-    // persistent streaming with A resident in registers
-    bool ok = M <= 16 && !arows && K == 8 * 32 * 16 && n_vtiles >= 384 && n_vtiles % (Epi::PX + 1) == 0;
-    if constexpr (StreamPlain<Epi>::value)
-      ok = ok && epi.w.n_seg == 1 &&
-           static_cast<size_t>(epi.w.off[1]) * epi.w.K * sizeof(T) < (size_t{1} << 32) - 4096;
-    if (ok) {
+    if (stream_ok<T>(M, K, n_vtiles, arows, epi)) {
       gemm_stream_kernel<T, 8, 16, Epi><<<stream_grid(n_vtiles >> Epi::PX), 512, 0, s>>>(A, lda, M, n_vtiles, epi);
       return hipGetLastError();
     }
