@@ -132,6 +132,14 @@ def test_fullsize_step(name, sample, conv_scale, fp8):
     D.dflash_draft_block(dr.cfg, dr.w, cache.kv, i32(ctx), i32(ids), B, ci, cl, fh, lg, ws(nb), nb)
     torch.cuda.synchronize()
     ci_h, cl_h, fh_h = ci.cpu().numpy(), cl.cpu().numpy(), fh.cpu().numpy()
+    # the timed launch passes no logits buffer (at one drafted block the LM head then keeps
+    # its top-16 lists without writing the logits): same candidates and hidden rows, bit for bit
+    ci2, cl2, fh2 = torch.zeros_like(ci), torch.zeros_like(cl), torch.zeros_like(fh)
+    D.dflash_draft_block(dr.cfg, dr.w, cache.kv, i32(ctx), i32(ids), B, ci2, cl2, fh2, None, ws(nb), nb)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(ci2.cpu().numpy(), ci_h)
+    np.testing.assert_array_equal(cl2.cpu().numpy(), cl_h)
+    np.testing.assert_array_equal(fh2.cpu().numpy(), fh_h)
     for b in sample:
         kc, vc = ocache[b]
         o = oracle.draft_block(m, kc, vc, int(ctx[b]), ids[b])
