@@ -498,14 +498,14 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
   rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(w->g_final), d, c->rms_eps, W.ut, final_hidden);
   LAUNCH_CHECK();
   float* lg = logits ? logits : W.logits;
-  // one drafted block with bf16 weights: the streaming LM head keeps each work-group's top 16
-  // per row (the logits are written only when the caller asks for them); otherwise the
-  // logits go to memory and a chunked first stage reads them back
+  // one drafted block (bf16 or FP8 weights): the streaming LM head keeps each work-group's
+  // top 16 per row (the logits are written only when the caller asks for them); otherwise
+  // the logits go to memory and a chunked first stage reads them back
   int groups = 0;
   P0.begin(DFLASH_PROBE_LM_HEAD);
-  if (!fp8w(c)) {
+  {
     EpiLogitsTop16<T> et{{seg1<T>(w->lm_head, V, wstride(c, d)), logits, V, STORE}, W.tk_v, W.tk_i};
-    groups = run_lm_head_top16<T>(W.ut, d, M, d, V / 16, et, kTopkFinalLists, s);
+    groups = run_lm_head_top16<T>(W.ut, d, M, d, V / 16, et, kTopkFinalLists, s, fp8w(c));
     if (groups < 0) return DFLASH_E_HIP;
   }
   if (groups == 0) {

@@ -200,12 +200,21 @@ struct StreamPlain {
   static constexpr bool value = Epi::kDirect && Epi::PX == 0 && Epi::PC == 0;
 };
 
-template <typename T, int NW, int KS, class Epi>
+// W8: the weights are E4M3 codes with a float32 scale after each row (plain epilogues only):
+// each lane loads 16 codes per 64-wide k group and widens them to two bf16 fragments when
+// the tile is consumed; A follows the same k order (see gemm_skinny_w8_kernel) and the row
+// scale multiplies the tile's sums before the reduction.
+template <typename T, int NW, int KS, class Epi, bool W8 = false>
 __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restrict__ A, int lda, int M, int n_vtiles,
                                                               Epi epi) {
   typedef Frag<T> F;
   typedef typename F::type frag_t;
   constexpr bool kPlain = StreamPlain<Epi>::value;
+  static_assert(!W8 || (kPlain && KS % 2 == 0), "FP8 weights: plain epilogues, whole 64-wide k groups");
+  struct WBuf {
+    typename std::conditional<W8, u32x4_t, frag_t>::type v[W8 ? KS / 2 : KS];
+    float sc;
+  };
   static_assert(Epi::PX == 0 || Epi::PX == 1, "partner tile: none or the pair");
   static_assert(NW * 64 >= 256, "one thread per output of a tile");
   __shared__ float red[2][NW][256];
@@ -246,9 +255,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
   // this wave's K slice of A, kept for every tile (rows past M read row 0; never stored)
   frag_t a[KS];
   {
-    const T* ap = A + static_cast<size_t>(r16 < M ? r16 : 0) * lda + g * 8 + k0;
+    const T* ap = A + static_cast<size_t>(r16 < M ? r16 : 0) * lda + k0;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) a[ks] = F::load(ap + 32 * ks);
+    for (int ks = 0; ks < KS; ++ks)
+      a[ks] = W8 ? F::load(ap + 64 * (ks >> 1) + 16 * g + 8 * (ks & 1)) : F::load(ap + g * 8 + 32 * ks);
   }
   if constexpr (!kPlain) {
     if (threadIdx.x < 16) rinfo[threadIdx.x] = epi.row(threadIdx.x < M ? threadIdx.x : M - 1);
@@ -257,10 +267,23 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
 
   // W of tile vt through a buffer descriptor over its matrix; tiles past this range and
   // rows past the matrix read nothing (offset past the descriptor's end)
-  auto load = [&](frag_t (&w)[KS], int vt) {
+  auto load = [&](WBuf& w, int vt) {
     __amdgpu_buffer_rsrc_t rw;
     uint32_t vo;
-    if constexpr (kPlain) {
+    if constexpr (W8) {
+      // row n: 4096 codes then its scale; lane group g takes codes 16g..16g+15 of each group
+      const int wrows = epi.w.off[1];
+      const uint32_t rowb = static_cast<uint32_t>(epi.w.K * sizeof(T));
+      const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(wrows) * rowb);
+      rw = make_rsrc(epi.w.p[0], wbytes);
+      const int n = vt * 16 + r16;
+      const uint32_t rb = (vt < t_end && n < wrows) ? static_cast<uint32_t>(n) * rowb : wbytes;
+#pragma unroll
+      for (int u = 0; u < KS / 2; ++u)
+        w.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, rb + k0 + 64 * u + 16 * g, 0, 0);
+      w.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, rb + NW * 32 * KS, 0, 0));
+      return;
+    } else if constexpr (kPlain) {
       const int wrows = epi.w.off[1], ldw = epi.w.K;
       const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(wrows) * ldw * sizeof(T));
       rw = make_rsrc(epi.w.p[0], wbytes);
@@ -276,13 +299,26 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
       const T* p = epi.wrow(v, r16);
       vo = (p && vt < t_end) ? static_cast<uint32_t>((p - base + g * 8 + k0) * sizeof(T)) : bytes;
     }
+    if constexpr (!W8) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) w[ks] = F::load_buf(rw, vo + 32 * ks * sizeof(T), 0);
+      for (int ks = 0; ks < KS; ++ks) w.v[ks] = F::load_buf(rw, vo + 32 * ks * sizeof(T), 0);
+    }
   };
-  auto finish = [&](frag_t (&w)[KS], int vt, int par) {
+  auto finish = [&](WBuf& w, int vt, int par) {
     f32x4_t acc{0.f, 0.f, 0.f, 0.f};
+    if constexpr (W8) {
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks) acc = F::mma(acc, a[ks], w[ks]);
+      for (int u = 0; u < KS / 2; ++u) {
+        frag_t lo, hi;
+        fp8x16_to_bf16(w.v[u], lo, hi);
+        acc = F::mma(acc, a[2 * u], lo);
+        acc = F::mma(acc, a[2 * u + 1], hi);
+      }
+      acc *= w.sc;
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = F::mma(acc, a[ks], w.v[ks]);
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[par][wave][lane * 4 + i] = acc[i];
     pipe_barrier<63>();
@@ -342,7 +378,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
       }
     }
   };
-  frag_t w0[KS], w1[KS];
+  WBuf w0, w1;
   load(w0, t_beg);
   load(w1, t_beg + 1);
   int vt = t_beg;
@@ -1053,12 +1089,15 @@ inline bool stream_ok(int M, int K, int n_vtiles, const int32_t* arows, const Ep
 // (nothing is launched then).
 template <typename T>
 static int run_lm_head_top16(const T* A, int lda, int M, int K, int n_vtiles, const EpiLogitsTop16<T>& epi,
-                             int max_groups, hipStream_t s) {
+                             int max_groups, hipStream_t s, bool w8 = false) {
   if constexpr (std::is_same<T, bf16_t>::value) {
     if (!stream_ok<T>(M, K, n_vtiles, nullptr, epi)) return 0;
     const int groups = stream_grid(n_vtiles);
     if (groups > max_groups) return 0;
-    gemm_stream_kernel<T, 8, 16, EpiLogitsTop16<T>><<<groups, 512, 0, s>>>(A, lda, M, n_vtiles, epi);
+    if (w8)
+      gemm_stream_kernel<T, 8, 16, EpiLogitsTop16<T>, true><<<groups, 512, 0, s>>>(A, lda, M, n_vtiles, epi);
+    else
+      gemm_stream_kernel<T, 8, 16, EpiLogitsTop16<T>><<<groups, 512, 0, s>>>(A, lda, M, n_vtiles, epi);
     return hipGetLastError() == hipSuccess ? groups : -1;
   } else {
     return 0;
