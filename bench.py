@@ -464,7 +464,7 @@ def main():
         stop.record()
         torch.cuda.synchronize()
         ms8 = start.elapsed_time(stop) / args.fp8_steps
-        w8 = kernel_work(dims, B, wl.ctx_lens, fp8=True)
+        w8 = kernel_work(dims, B, wl.ctx_lens, fp8=True, lists=lists)
         lm_ms = float(np.mean([p.ms("lm_head") for p in live8.values()]))
         lm_bytes = w8["lm_head"][0]
         sb8 = step_bytes(dims, B, wl.ctx_lens, fp8=True)

@@ -211,8 +211,8 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
   typedef typename F::type frag_t;
   constexpr bool kPlain = StreamPlain<Epi>::value;
   static_assert(!W8 || (kPlain && KS % 2 == 0), "FP8 weights: plain epilogues, whole 64-wide k groups");
-  struct WBuf {
-    typename std::conditional<W8, u32x4_t, frag_t>::type v[W8 ? KS / 2 : KS];
+  struct W8Buf {
+    u32x4_t v[KS / 2];
     float sc;
   };
   static_assert(Epi::PX == 0 || Epi::PX == 1, "partner tile: none or the pair");
@@ -254,11 +254,14 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
 
   // this wave's K slice of A, kept for every tile (rows past M read row 0; never stored)
   frag_t a[KS];
-  {
-    const T* ap = A + static_cast<size_t>(r16 < M ? r16 : 0) * lda + k0;
+  if constexpr (W8) {
+    const T* ap = A + static_cast<size_t>(r16 < M ? r16 : 0) * lda + k0 + 16 * g;
 #pragma unroll
-    for (int ks = 0; ks < KS; ++ks)
-      a[ks] = W8 ? F::load(ap + 64 * (ks >> 1) + 16 * g + 8 * (ks & 1)) : F::load(ap + g * 8 + 32 * ks);
+    for (int ks = 0; ks < KS; ++ks) a[ks] = F::load(ap + 64 * (ks >> 1) + 8 * (ks & 1));
+  } else {
+    const T* ap = A + static_cast<size_t>(r16 < M ? r16 : 0) * lda + g * 8 + k0;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) a[ks] = F::load(ap + 32 * ks);
   }
   if constexpr (!kPlain) {
     if (threadIdx.x < 16) rinfo[threadIdx.x] = epi.row(threadIdx.x < M ? threadIdx.x : M - 1);
@@ -267,23 +270,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
 
   // W of tile vt through a buffer descriptor over its matrix; tiles past this range and
   // rows past the matrix read nothing (offset past the descriptor's end)
-  auto load = [&](WBuf& w, int vt) {
+  auto load = [&](frag_t (&w)[KS], int vt) {
     __amdgpu_buffer_rsrc_t rw;
     uint32_t vo;
-    if constexpr (W8) {
-      // row n: 4096 codes then its scale; lane group g takes codes 16g..16g+15 of each group
-      const int wrows = epi.w.off[1];
-      const uint32_t rowb = static_cast<uint32_t>(epi.w.K * sizeof(T));
-      const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(wrows) * rowb);
-      rw = make_rsrc(epi.w.p[0], wbytes);
-      const int n = vt * 16 + r16;
-      const uint32_t rb = (vt < t_end && n < wrows) ? static_cast<uint32_t>(n) * rowb : wbytes;
-#pragma unroll
-      for (int u = 0; u < KS / 2; ++u)
-        w.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, rb + k0 + 64 * u + 16 * g, 0, 0);
-      w.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, rb + NW * 32 * KS, 0, 0));
-      return;
-    } else if constexpr (kPlain) {
+    if constexpr (kPlain) {
       const int wrows = epi.w.off[1], ldw = epi.w.K;
       const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(wrows) * ldw * sizeof(T));
       rw = make_rsrc(epi.w.p[0], wbytes);
@@ -299,12 +289,26 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
       const T* p = epi.wrow(v, r16);
       vo = (p && vt < t_end) ? static_cast<uint32_t>((p - base + g * 8 + k0) * sizeof(T)) : bytes;
     }
-    if constexpr (!W8) {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) w.v[ks] = F::load_buf(rw, vo + 32 * ks * sizeof(T), 0);
+    for (int ks = 0; ks < KS; ++ks) w[ks] = F::load_buf(rw, vo + 32 * ks * sizeof(T), 0);
+  };
+  // FP8 rows: 4096 codes then the row's scale; lane group g takes codes 16g..16g+15 of each
+  // 64-wide group (tiles past the range and rows past the matrix read nothing)
+  auto load8 = [&](auto& w, int vt) {
+    if constexpr (W8) {
+      const int wrows = epi.w.off[1];
+      const uint32_t rowb = static_cast<uint32_t>(epi.w.K * sizeof(T));
+      const uint32_t wbytes = static_cast<uint32_t>(static_cast<size_t>(wrows) * rowb);
+      const __amdgpu_buffer_rsrc_t rw = make_rsrc(epi.w.p[0], wbytes);
+      const int n = vt * 16 + r16;
+      const uint32_t rb = (vt < t_end && n < wrows) ? static_cast<uint32_t>(n) * rowb : wbytes;
+#pragma unroll
+      for (int u = 0; u < KS / 2; ++u)
+        w.v[u] = __builtin_amdgcn_raw_buffer_load_b128(rw, rb + k0 + 64 * u + 16 * g, 0, 0);
+      w.sc = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rw, rb + NW * 32 * KS, 0, 0));
     }
   };
-  auto finish = [&](WBuf& w, int vt, int par) {
+  auto finish = [&](auto& w, int vt, int par) {
     f32x4_t acc{0.f, 0.f, 0.f, 0.f};
     if constexpr (W8) {
 #pragma unroll
@@ -317,7 +321,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
       acc *= w.sc;
     } else {
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = F::mma(acc, a[ks], w.v[ks]);
+      for (int ks = 0; ks < KS; ++ks) acc = F::mma(acc, a[ks], w[ks]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) red[par][wave][lane * 4 + i] = acc[i];
@@ -378,19 +382,33 @@ __global__ __launch_bounds__(64 * NW) void gemm_stream_kernel(const T* __restric
       }
     }
   };
-  WBuf w0, w1;
-  load(w0, t_beg);
-  load(w1, t_beg + 1);
   int vt = t_beg;
-  for (; vt + 2 < t_end; vt += 2) {
+  if constexpr (W8) {
+    W8Buf w0, w1;
+    load8(w0, t_beg);
+    load8(w1, t_beg + 1);
+    for (; vt + 2 < t_end; vt += 2) {
+      finish(w0, vt, 0);
+      load8(w0, vt + 2);
+      finish(w1, vt + 1, 1);
+      load8(w1, vt + 3);
+    }
     finish(w0, vt, 0);
-    load(w0, vt + 2);
-    finish(w1, vt + 1, 1);
-    load(w1, vt + 3);
+    if (vt + 1 < t_end) finish(w1, vt + 1, 1);
+  } else {
+    frag_t w0[KS], w1[KS];
+    load(w0, t_beg);
+    load(w1, t_beg + 1);
+    for (; vt + 2 < t_end; vt += 2) {
+      finish(w0, vt, 0);
+      load(w0, vt + 2);
+      finish(w1, vt + 1, 1);
+      load(w1, vt + 3);
+    }
+    finish(w0, vt, 0);
+    if (vt + 1 < t_end) finish(w1, vt + 1, 1);
   }
-  finish(w0, vt, 0);
   const int last_par = vt + 1 < t_end ? 1 : 0;
-  if (vt + 1 < t_end) finish(w1, vt + 1, 1);
   if constexpr (Epi::kTop16) {
     pipe_barrier<63>();
     if (threadIdx.x < 256) {
