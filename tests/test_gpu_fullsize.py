@@ -62,14 +62,17 @@ def drafter_for(name, conv_scale, fp8=False):
     return wl, (st["W"], st["m"], st["dr"])
 
 
-# (workload, sampled sequences, conv scale).  c5 runs at the workload's own random-init
-# scale and at a milder one; at its own scale the conv corrections are O(1.3) per channel
-# and the computation is ill-conditioned (the tolerance follows the measured conditioning).
-# FP8 storage cases: c2 (one block: weight-streaming kernels) and c4 (4 blocks: the
-# pipelined kernel at 64 rows).
+# (workload, sampled sequences, conv scale, fp8).  Every case is held to the stated 2e-2
+# except c5 at its own random-init conv scale, where the conv corrections are O(1.3) per
+# channel and the computation is ill-conditioned: the oracle itself moves by 6-7e-2 under
+# fp32-level noise there, so that one case (CONDITIONED) is bounded by three times that
+# spread, and its top-16 is checked stage-wise only (exactly the top 16 of the device's own
+# logits).  c5 also runs at a milder conv scale, held to 2e-2.  FP8 storage cases: c2 (one
+# block: weight-streaming kernels) and c4 (4 blocks: the pipelined kernel at 64 rows).
 CASES = [("c2", (0,), "config", False), ("c3", (0, 31), "config", False), ("c4", (3,), "config", False),
          ("c5", (0, 15), "config", False), ("c5", (15,), "mild", False), ("c2", (0,), "config", True),
          ("c4", (1,), "config", True)]
+CONDITIONED = {("c5", "config", False)}
 
 
 @pytest.mark.parametrize("name,sample,conv_scale,fp8", CASES)
@@ -143,15 +146,25 @@ def test_fullsize_step(name, sample, conv_scale, fp8):
     for b in sample:
         kc, vc = ocache[b]
         o = oracle.draft_block(m, kc, vc, int(ctx[b]), ids[b])
-        kappa = H.conditioning(m, kc, vc, int(ctx[b]), ids[b], o)
-        td = H.tol_conditioned(dims, kappa)
-        say(f"  b{b}: oracle fp32-level spread {kappa:.2e} -> tolerance {td:.2e}")
+        conditioned = (name, conv_scale, fp8) in CONDITIONED
+        if conditioned:
+            kappa = H.conditioning(m, kc, vc, int(ctx[b]), ids[b], o)
+            td = H.tol_conditioned(dims, kappa)
+            say(f"  b{b}: oracle fp32-level spread {kappa:.2e} -> tolerance {td:.2e}")
+        else:
+            td = t
         lgb = lg[b].cpu().numpy()
         H.assert_close_rows(f"{name} logits b{b}", lgb, o["logits"], td)
         H.assert_close_rows(f"{name} final hidden b{b}", fh_h[b], o["xhat"], td)
+        # stage-wise exact: the candidates are exactly the top 16 of the device's own logits
         np.testing.assert_array_equal(ci_h[b], H.exact_topk_of(lgb))
-        near = H.topk_with_margin(ci_h[b], o["logits"], lgb)
-        say(f"  b{b}: logits rel err {H.rowwise_relerr(lgb, o['logits']):.2e}, near-tie top-16 swaps {near}")
+        if conditioned:
+            oi, _ = oracle.topk(o["logits"], 16)
+            say(f"  b{b}: logits rel err {H.rowwise_relerr(lgb, o['logits']):.2e}, top-16 ranks differing from "
+                f"the oracle's (not asserted in this ill-conditioned case) {int((oi != ci_h[b]).sum())}")
+        else:
+            near = H.topk_with_margin(ci_h[b], o["logits"], lgb)
+            say(f"  b{b}: logits rel err {H.rowwise_relerr(lgb, o['logits']):.2e}, near-tie top-16 swaps {near}")
 
     # ---- the step's own chain (device candidates -> path -> verify): properties only
     pidx = torch.zeros((B, 15), dtype=torch.int32, device="cuda")
