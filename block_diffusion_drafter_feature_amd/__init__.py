@@ -45,7 +45,7 @@ EXPORTED = (
     "dflash_calibrate_workspace_bytes", "dflash_path_table_bytes", "dflash_build_path_table",
     "dflash_inject_workspace_bytes", "dflash_draft_workspace_bytes", "dflash_path_workspace_bytes",
     "dflash_verify_workspace_bytes", "dflash_verify_sampled_workspace_bytes", "dflash_check_config",
-    "dflash_status_string",
+    "dflash_status_string", "dflash_verify_noalloc",
 )
 
 
@@ -129,6 +129,7 @@ def lib() -> ctypes.CDLL:
             "dflash_path_workspace_bytes": ([cfgp, _i32], PC),
             "dflash_verify_workspace_bytes": ([_i32, _i32, _i32], PC),
             "dflash_check_config": ([cfgp], ctypes.c_int),
+            "dflash_verify_noalloc": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
             "dflash_status_string": ([ctypes.c_int], ctypes.c_char_p),
         }
         for name, (args, res) in sig.items():
@@ -248,6 +249,16 @@ def dflash_verify(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_le
     _check("dflash_verify", lib().dflash_verify(
         _ptr(draft), _ptr(tgt_logits), tgt_dtype, batch, n_draft, vocab, _ptr(accept_len), _ptr(bonus),
         _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+DFLASH_VERIFY_NOALLOC_SCRATCH = 1 << 20
+
+
+def dflash_verify_noalloc(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_len, bonus,
+                          stream=None) -> None:
+    _check("dflash_verify_noalloc", lib().dflash_verify_noalloc(
+        _ptr(draft), _ptr(tgt_logits), tgt_dtype, batch, n_draft, vocab, _ptr(accept_len), _ptr(bonus),
+        _stream(stream)))
 
 
 _hip = None

@@ -12,6 +12,7 @@
 #include "select.h"
 
 #include <algorithm>
+#include <atomic>
 
 using namespace dflash;
 
@@ -599,6 +600,62 @@ int calibrate_impl(const dflash_config* c, const dflash_weights* w, const float*
 
 }  // namespace
 
+// ------------------------------------------------------------------ fixed scratch of dflash_verify_noalloc
+
+// Device scratch of the entry point that allocates nothing: one copy per GPU, held by the
+// loaded module until the process ends.  In host code `scratch` names a host-side shadow,
+// not device memory: the kernels only ever see the address hipGetSymbolAddress returns
+// for the current device (noalloc_scratch).
+static __device__ __align__(256) unsigned char scratch[DFLASH_VERIFY_NOALLOC_SCRATCH];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up on the first call per
+// device with that device current and kept; nullptr when the lookup fails.
+void* noalloc_scratch() {
+  static std::atomic<void*> addr[kMaxDevices];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = addr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    addr[dev].store(p, std::memory_order_release);
+  }
+  return p;
+}
+
+// Greedy verification over a workspace already carved (shared by both verify entry points).
+int verify_launch(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch, int32_t n_draft,
+                  int32_t vocab, int32_t* accept_len, int32_t* bonus, void* workspace, hipStream_t stream) {
+  Carver cv(workspace);
+  VerifyWs W = carve_verify(cv, batch, n_draft, vocab);
+  const int nch = (vocab + kArgmaxChunk - 1) / kArgmaxChunk;
+  dim3 grid(nch, batch * (n_draft + 1));
+  if (tgt_dtype == DFLASH_BF16)
+    argmax_partial_kernel<bf16_t><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(tgt_logits), vocab,
+                                                            kArgmaxChunk, W.pv, W.pi);
+  else
+    argmax_partial_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(tgt_logits), vocab,
+                                                           kArgmaxChunk, W.pv, W.pi);
+  LAUNCH_CHECK();
+  accept_kernel<<<batch, 64, 0, stream>>>(W.pv, W.pi, nch, draft, n_draft, accept_len, bonus);
+  LAUNCH_CHECK();
+  return DFLASH_OK;
+}
+
+int verify_args(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch, int32_t n_draft,
+                int32_t vocab, int32_t* accept_len, int32_t* bonus) {
+  if (batch <= 0 || n_draft < 0 || vocab <= 0) return DFLASH_E_INVAL;
+  if (n_draft > 64) return DFLASH_E_UNSUPPORTED;
+  if (tgt_dtype != DFLASH_BF16 && tgt_dtype != DFLASH_F32) return DFLASH_E_INVAL;
+  if ((n_draft > 0 && !draft) || !tgt_logits || !accept_len || !bonus) return DFLASH_E_INVAL;
+  return DFLASH_OK;
+}
+
+}  // namespace
+
 // =====================================================================================
 // exported C ABI
 // =====================================================================================
@@ -715,25 +772,21 @@ int dflash_select_path(const dflash_config* cfg, const dflash_weights* w, const 
 int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch, int32_t n_draft,
                   int32_t vocab, int32_t* accept_len, int32_t* bonus, void* workspace, size_t workspace_bytes,
                   hipStream_t stream) {
-  if (batch <= 0 || n_draft < 0 || vocab <= 0) return DFLASH_E_INVAL;
-  if (n_draft > 64) return DFLASH_E_UNSUPPORTED;
-  if (tgt_dtype != DFLASH_BF16 && tgt_dtype != DFLASH_F32) return DFLASH_E_INVAL;
-  if ((n_draft > 0 && !draft) || !tgt_logits || !accept_len || !bonus || !workspace) return DFLASH_E_INVAL;
+  int rc;
+  if ((rc = verify_args(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_len, bonus))) return rc;
+  if (!workspace) return DFLASH_E_INVAL;
   if (workspace_bytes < dflash_verify_workspace_bytes(batch, n_draft, vocab)) return DFLASH_E_WORKSPACE;
-  Carver cv(workspace);
-  VerifyWs W = carve_verify(cv, batch, n_draft, vocab);
-  const int nch = (vocab + kArgmaxChunk - 1) / kArgmaxChunk;
-  dim3 grid(nch, batch * (n_draft + 1));
-  if (tgt_dtype == DFLASH_BF16)
-    argmax_partial_kernel<bf16_t><<<grid, 256, 0, stream>>>(static_cast<const bf16_t*>(tgt_logits), vocab,
-                                                            kArgmaxChunk, W.pv, W.pi);
-  else
-    argmax_partial_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(tgt_logits), vocab,
-                                                           kArgmaxChunk, W.pv, W.pi);
-  LAUNCH_CHECK();
-  accept_kernel<<<batch, 64, 0, stream>>>(W.pv, W.pi, nch, draft, n_draft, accept_len, bonus);
-  LAUNCH_CHECK();
-  return DFLASH_OK;
+  return verify_launch(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_len, bonus, workspace, stream);
+}
+
+int dflash_verify_noalloc(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch,
+                          int32_t n_draft, int32_t vocab, int32_t* accept_len, int32_t* bonus, hipStream_t stream) {
+  int rc;
+  if ((rc = verify_args(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_len, bonus))) return rc;
+  if (dflash_verify_workspace_bytes(batch, n_draft, vocab) > DFLASH_VERIFY_NOALLOC_SCRATCH) return DFLASH_E_WORKSPACE;
+  void* ws = noalloc_scratch();
+  if (!ws) return DFLASH_E_HIP;
+  return verify_launch(draft, tgt_logits, tgt_dtype, batch, n_draft, vocab, accept_len, bonus, ws, stream);
 }
 
 int dflash_sample_path(const dflash_config* cfg, const dflash_weights* w, const int32_t* cand_ids,

@@ -23,9 +23,11 @@
  *
  * Conventions (all calls):
  *   - Every pointer argument named as device memory must point to memory of the
- *     current HIP device; the caller owns it.  The library keeps no pointer after
- *     a call returns and holds no global state; calls on different streams may run
- *     concurrently if they do not share output or workspace memory.
+ *     current HIP device; the caller owns it.  The library keeps no pointer to caller
+ *     memory after a call returns, and calls on different streams may run concurrently
+ *     if they do not share output or workspace memory.  Its only state of its own is
+ *     the fixed per-GPU scratch of dflash_verify_noalloc (and that scratch's device
+ *     address, looked up once per device).
  *   - Struct arguments (dflash_config, dflash_weights, dflash_kv) are host memory,
  *     read during the call only.
  *   - All device work is enqueued on `stream`; no call synchronises the host or
@@ -264,6 +266,22 @@ int dflash_select_path(const dflash_config* cfg, const dflash_weights* w,
 int dflash_verify(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch,
                   int32_t n_draft, int32_t vocab, int32_t* accept_len, int32_t* bonus,
                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Greedy verification that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same arguments, results and errors as dflash_verify
+ * without the workspace.  Its scratch is a fixed array of DFLASH_VERIFY_NOALLOC_SCRATCH
+ * bytes inside the library, one copy per GPU, held until the process ends; a call whose
+ * dflash_verify_workspace_bytes(batch, n_draft, vocab) exceeds it returns
+ * DFLASH_E_WORKSPACE with nothing enqueued (1 MiB covers batch 431 at 15 drafts over a
+ * 151,936-token vocabulary).  DFLASH_E_HIP if the scratch's device address cannot be
+ * looked up.  Every call on a GPU shares that GPU's array, whose content is whatever the
+ * last call left (each call overwrites all of the part it reads, so nothing needs
+ * clearing): calls that can overlap on one GPU -- different streams, or host threads
+ * without ordering -- race and give undefined results; keep them on one stream. */
+#define DFLASH_VERIFY_NOALLOC_SCRATCH (1u << 20)
+int dflash_verify_noalloc(const int32_t* draft, const void* tgt_logits, int32_t tgt_dtype, int32_t batch,
+                          int32_t n_draft, int32_t vocab, int32_t* accept_len, int32_t* bonus, hipStream_t stream);
 
 /* The Path Selector's per-token table (a cache of weights, not of activations): row t =
  * [ps_left E[t] ; ps_right E[t]] in float (fp32 accumulation), for every token of the

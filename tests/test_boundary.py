@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 19
+    assert len(names) == 20
     lib = ctypes.CDLL(D.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -119,6 +119,19 @@ def test_calls_validate_before_launch():
     assert _status(D.dflash_verify, FAKE, FAKE, 9, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_INVAL
     assert _status(D.dflash_verify, FAKE, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v - 1, S) == D.DFLASH_E_WORKSPACE
     assert _status(D.dflash_verify, None, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_INVAL
+
+
+def test_verify_noalloc_rejects_before_launch():
+    S = 1
+    assert _status(D.dflash_verify_noalloc, FAKE, FAKE, D.DFLASH_BF16, 0, 15, 1024, FAKE, FAKE, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_verify_noalloc, FAKE, FAKE, D.DFLASH_BF16, 2, 65, 1024, FAKE, FAKE, S) == D.DFLASH_E_UNSUPPORTED
+    assert _status(D.dflash_verify_noalloc, FAKE, FAKE, 9, 2, 15, 1024, FAKE, FAKE, S) == D.DFLASH_E_INVAL
+    assert _status(D.dflash_verify_noalloc, None, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, S) == D.DFLASH_E_INVAL
+    # sizes beyond the fixed scratch are refused (no launch, no allocation)
+    V = 151936
+    assert D.dflash_verify_workspace_bytes(431, 15, V) <= D.DFLASH_VERIFY_NOALLOC_SCRATCH
+    assert D.dflash_verify_workspace_bytes(432, 15, V) > D.DFLASH_VERIFY_NOALLOC_SCRATCH
+    assert _status(D.dflash_verify_noalloc, FAKE, FAKE, D.DFLASH_BF16, 432, 15, V, FAKE, FAKE, S) == D.DFLASH_E_WORKSPACE
 
 
 def test_advance_rejects_bad_arguments():
