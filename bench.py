@@ -7,8 +7,12 @@ resident in HBM:
   2. dflash_draft_block    : one parallel forward pass over the 16-row block
   3. dflash_select_path    : Path Selector pair scores + greedy path
   4. dflash_verify         : greedy acceptance against the target logits
-blocks/s = batch x steps/s.  The default workload is the Qwen3-8B-shaped drafter at
-batch 1, context 4096 (``--workload c2``); c1, c3, c4, c5 select the other shapes.
+blocks/s = batch x steps/s.  The default workload is the full DFlash 2 step (``--workload
+c5``: batch 16, context 16384, the Qwen3-8B-shaped drafter with the dynamic short conv around
+every sublayer and the gated Path Selector), the largest configuration that runs on one GPU
+and the only one with every part of the step; c1..c4 select the other shapes.  Before the
+timed steps the whole context of every sequence is injected (prefill), and that injection is
+timed on its own (rows/s and the matrix-core fraction of its GEMMs).
 
 Prints ONE JSON line (rank 0): the metric, a roofline object for the dominant kernel
 (algorithmic bytes or flops per launch over its event-timed duration inside the timed
@@ -39,7 +43,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3", "c4", "c5"])
+    ap.add_argument("--workload", default="c5", choices=["c1", "c2", "c3", "c4", "c5"])
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="CPU oracle sample budget (0 to skip)")
     ap.add_argument("--no-breakdown", action="store_true", help="skip the per-kernel breakdown pass")
     ap.add_argument("--cycles", type=int, default=32,
@@ -60,9 +64,9 @@ def parse():
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="after the step, run a plain fp32 elementwise copy (torch.neg) of this many MiB "
                          "three times: a kernel of known traffic that calibrates HBM byte counters")
-    ap.add_argument("--prefill", choices=["inject", "synthetic"], default=None,
-                    help="fill the KV cache by injecting every context row (default for c1, c2) or with "
-                         "device-generated values at the scale injection produces (default for c3..c5)")
+    ap.add_argument("--prefill", choices=["inject", "synthetic"], default="inject",
+                    help="fill the KV cache by injecting every context row (default; timed apart) or with "
+                         "device-generated values at the scale injection produces")
     return ap.parse_args()
 
 
@@ -96,6 +100,13 @@ def kernel_work(dims, batch, ctx_lens, fp8=False, lists=0):
         "inject_kv": (dims.n_layers * wb(2 * hk, d) + M * d * e + M * dims.n_layers * 2 * hk * e,
                       2 * M * dims.n_layers * 2 * hk * d),
     }
+    if dims.use_conv:
+        ng = d // 16
+        gen = 2 * ng * d * e + 2 * d * e              # correction generator + two static taps
+        # FFN input site: the residual rows in, the norm gain, the conv'd rows out (GEMM operand)
+        w["conv_pre"] = (gen + M * d * 4 + d * e + M * d * e, 2 * M * 2 * ng * d)
+        # attention output site: the O projection's rows in, the residual read and written
+        w["conv_post"] = (gen + M * d * 4 + 2 * M * d * 4, 2 * M * 2 * ng * d)
     return w
 
 
@@ -117,15 +128,23 @@ def step_bytes(dims, batch, ctx_lens, fp8=False):
 # ------------------------------------------------------------------ CPU oracle baseline
 
 def cpu_baseline(wl, W, seconds):
+    """The oracle timed on this host's cores (BLAS on every core it may use), then again
+    with BLAS held to one thread (half the time budget)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    allc = _cpu_run(wl, W, seconds, threads)
+    with threadpool_limits(limits=1, user_api="blas"):
+        one = _cpu_run(wl, W, seconds / 2, 1, warm_model=allc.pop("_model"))
+    one.pop("_model", None)
+    allc["one_thread"] = {k: one[k] for k in ("value", "unit", "cores", "sample")}
+    return allc
+
+
+def _cpu_run(wl, W, seconds, threads, warm_model=None):
     import numpy as np
 
     import oracle
     import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
     dims = wl.dims
     L = int(wl.ctx_lens[0])
     cap = ((L + 16 + 31) // 32) * 32
@@ -136,7 +155,7 @@ def cpu_baseline(wl, W, seconds):
     ids = synth.make_block_ids(dims, 1, wl.seed, 1)[0]
     T = oracle.decode(synth.make_target_logits(dims, 1, 15, wl.seed, planted="random" if wl.planted else "none")[0],
                       dims.dtype)
-    m = oracle.Model(dims, W)
+    m = warm_model if warm_model is not None else oracle.Model(dims, W)
     pos = np.arange(L - 16, L) if L >= 16 else np.arange(0)
     t0 = time.perf_counter()
     oracle.drafting_step(m, kc, vc, L, hid[:len(pos)], pos, ids, T)        # warm-up: decodes the weights
@@ -149,10 +168,10 @@ def cpu_baseline(wl, W, seconds):
         if el >= seconds or (n >= 1 and el + el / n > 3 * seconds):
             break
     return {"value": n / el, "unit": "blocks/s", "cores": int(threads), "kind": "oracle",
-            "host_cpus": len(os.sched_getaffinity(0)),
+            "host_cpus": len(os.sched_getaffinity(0)), "_model": m,
             "sample": f"{n} full drafting step(s) of sequence 0 (inject 16 rows, draft, path, verify) at the "
-                      f"{wl.name} shapes, context {L}, float64 NumPy oracle; {el:.1f} s timed after a "
-                      f"{warm:.1f} s warm-up that decodes the weights"}
+                      f"{wl.name} shapes, context {L}, float64 NumPy oracle on {threads} BLAS thread(s); "
+                      f"{el:.1f} s timed after a {warm:.1f} s warm-up"}
 
 
 # ------------------------------------------------------------------ main
@@ -275,28 +294,63 @@ def main():
     i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()  # noqa: E731
     dt_t = D.torch_dtype(dims)
 
-    # ---- prefill: inject every context row (device-generated target hiddens, in chunks), or
-    # fill the cache directly (K after RoPE and V of an injected row are ~N(0, 0.02^2 * d)
-    # for unit-RMS context features).  The timed step reads the same bytes either way.
-    prefill = args.prefill or ("inject" if wl.name in ("c1", "c2") else "synthetic")
+    # ---- prefill: inject every context row (device-generated N(0,1) target hiddens, one
+    # chunk of at most 16384 rows per call), each call bracketed by events so that only the
+    # injection itself is timed; or fill the cache directly (K after RoPE and V of an injected
+    # row are ~N(0, 0.02^2 d) for unit-RMS context features).  The timed step reads the same
+    # bytes either way.
+    prefill = args.prefill
     cache = D.KVCache(dims, B, cap, fill=None if prefill == "synthetic" else 0.0)
     gen = torch.Generator(device="cuda")
     gen.manual_seed(wl.seed)
     t0 = time.time()
+    prefill_info = None
     if prefill == "inject":
         chunk = 16384
         ws_inj = D.Workspace()
-        for b in range(B):
-            for r0 in range(0, int(ctx[b]), chunk):
-                n = min(chunk, int(ctx[b]) - r0)
-                hid = torch.randn((n, dims.d_cat), generator=gen, device="cuda", dtype=torch.float32).to(dt_t)
-                nb = D.dflash_inject_workspace_bytes(dr.cfg, n)
-                sub = D.dflash_kv(batch=1, cap=cap)
-                for l in range(dims.n_layers):
-                    sub.k[l] = cache.k[l][b].data_ptr()
-                    sub.vt[l] = cache.vt[l][b].data_ptr()
-                D.dflash_inject_context(dr.cfg, dr.w, sub, hid, n, i32([0, n]), i32([r0]), i32([n]), 1,
-                                        ws_inj.get(nb), nb)
+        marks, rows_done = [], 0
+        pf_probe = D.Probes(("inject_fc", "inject_kv"))
+        pieces = [(b, r0, min(chunk, int(ctx[b]) - r0)) for b in range(B) for r0 in range(0, int(ctx[b]), chunk)]
+        for i, (b, r0, n) in enumerate(pieces):
+            hid = torch.randn((n, dims.d_cat), generator=gen, device="cuda", dtype=torch.float32).to(dt_t)
+            nb = D.dflash_inject_workspace_bytes(dr.cfg, n)
+            sub = D.dflash_kv(batch=1, cap=cap)
+            for l in range(dims.n_layers):
+                sub.k[l] = cache.k[l][b].data_ptr()
+                sub.vt[l] = cache.vt[l][b].data_ptr()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            ws_buf = ws_inj.get(nb)
+            e0.record()
+            D.dflash_inject_context(dr.cfg, dr.w, sub, hid, n, i32([0, n]), i32([r0]), i32([n]), 1, ws_buf, nb,
+                                    probes=pf_probe.struct if i == len(pieces) - 1 else None)
+            e1.record()
+            marks.append((e0, e1, n))
+            rows_done += n
+            del hid
+        torch.cuda.synchronize()
+        if marks:
+            pf_ms = sum(a.elapsed_time(b_) for a, b_, _ in marks)
+            kv_cols = dims.n_layers * 2 * dims.n_kv_heads * dims.head_dim
+            flop_row = 2 * dims.d_cat * dims.d + 2 * dims.d * kv_cols
+            tf = rows_done * flop_row / (pf_ms * 1e-3)
+            n_last = marks[-1][2]
+            fc_ms, kv_ms = pf_probe.ms("inject_fc"), pf_probe.ms("inject_kv")
+            peak = MFMA_PEAK[dims.dtype]
+            prefill_info = {
+                "rows": rows_done, "calls": len(marks), "rows_per_call": chunk, "ms": round(pf_ms, 3),
+                "rows_per_s": round(rows_done / (pf_ms * 1e-3), 1),
+                "achieved": round(tf / 1e12, 1), "peak": peak / 1e12, "unit": "TFLOP/s", "frac": round(tf / peak, 4),
+                "flop_per_row": int(flop_row),
+                "last_call": {"rows": n_last,
+                              "fusion_gemm": {"ms": round(fc_ms, 4), "frac": round(
+                                  2 * n_last * dims.d_cat * dims.d / (fc_ms * 1e-3) / peak, 4)},
+                              "kv_gemm": {"ms": round(kv_ms, 4), "frac": round(
+                                  2 * n_last * dims.d * kv_cols / (kv_ms * 1e-3) / peak, 4)}},
+                "includes": "per call: fusion GEMM, RMSNorm, K/V GEMM with RoPE and the cache scatter; the "
+                            "target hiddens are generated outside the timed calls"}
+            log(f"[bench] prefill injection: {rows_done} rows in {pf_ms:.1f} ms ({rows_done / pf_ms * 1e3:.0f} "
+                f"rows/s, {tf / 1e12:.0f} TFLOP/s = {tf / peak:.3f} of peak)")
+        del ws_inj
     else:
         scale = 0.02 * dims.d ** 0.5
         for l in range(dims.n_layers):
@@ -343,7 +397,6 @@ def main():
     lists = min(cus, dims.vocab // 16) if (dims.dtype == "bf16" and B == 1 and dims.d == 4096
                                            and dims.vocab // 16 >= 384 and cus <= 256) else 0
     work = kernel_work(dims, B, wl.ctx_lens, lists=lists)
-    dominant = "lm_head"
     # live kernel probes on every PROBE_EVERY-th timed step (each probe adds event records
     # to the stream, ~5 us apiece); the average is over the probed steps of the timed region
     probed = list(range(0, args.steps, PROBE_EVERY))
@@ -376,8 +429,13 @@ def main():
         return {"bound": "mfma", "achieved": round(a / 1e12, 1), "peak": peak_mf / 1e12, "unit": "TFLOP/s",
                 "frac": round(a / peak_mf, 4), "algorithmic_flops": int(fl), "ms": round(t_ms, 4)}
 
-    dom = roof(dominant, avg_ms(live.values(), dominant))
-    attn = roof("attn", avg_ms(live.values(), "attn"))
+    # the dominant kernel: the larger share of the step's time, the LM head (one launch per
+    # step) or the block attention (one launch per layer)
+    lm_ms, at_ms = avg_ms(live.values(), "lm_head"), avg_ms(live.values(), "attn")
+    dominant = "attn" if at_ms * dims.n_layers > lm_ms else "lm_head"
+    dom = roof(dominant, lm_ms if dominant == "lm_head" else at_ms)
+    attn = roof("attn", at_ms)
+    lmh = roof("lm_head", lm_ms)
     traffic = None
     tpath = os.path.join(ROOT, "profiles", f"traffic_{wl.name}.json")
     if os.path.exists(tpath):
@@ -394,16 +452,22 @@ def main():
     kname = ("gemm_skinny_kernel" if dims.dtype != "bf16" else
              "gemm_stream_kernel" if wl.batch == 1 else "gemm_pipe_kernel")
     epi = "EpiLogitsTop16" if lists else "EpiLogits"
-    roofline.update({"traffic": traffic, "kernel": f"{dominant} GEMM ({kname}<..., {epi}>)",
+    kdesc = (f"lm_head GEMM ({kname}<..., {epi}>)" if dominant == "lm_head" else
+             "block attention, one layer (block_attn_kernel + attn_combine_kernel)")
+    roofline.update({"traffic": traffic, "kernel": kdesc, "share_of_step": round(
+                         (lm_ms if dominant == "lm_head" else at_ms * dims.n_layers) / ms, 4),
                      "algorithmic_bytes_per_launch": dom.get("algorithmic_bytes"), "ms_per_launch": dom["ms"]})
 
     breakdown = {}
     if not args.no_breakdown:
-        pr = [D.Probes() for _ in range(5)]
+        names = ["lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv"]
+        if dims.use_conv:
+            names += ["conv_pre", "conv_post"]
+        pr = [D.Probes(tuple(names)) for _ in range(5)]
         for p in pr:
             step(p)
         torch.cuda.synchronize()
-        for n in ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv"):
+        for n in names:
             breakdown[n] = roof(n, avg_ms(pr, n)) if n != "topk" else {"ms": round(avg_ms(pr, n), 4)}
 
     sampled = None
@@ -565,7 +629,8 @@ def main():
     if W is not None:
         log(f"[bench] CPU oracle sample ({args.cpu_seconds:.0f} s budget) ...")
         cpu = cpu_baseline(wl, W, args.cpu_seconds)
-        log(f"[bench] CPU oracle: {cpu['value']:.4f} blocks/s on {cpu['cores']} BLAS threads")
+        log(f"[bench] CPU oracle: {cpu['value']:.4f} blocks/s on {cpu['cores']} BLAS threads, "
+            f"{cpu['one_thread']['value']:.4f} on one")
 
     sb = step_bytes(dims, B, wl.ctx_lens)
     out = {
@@ -581,6 +646,8 @@ def main():
                    "path": "greedy", "prefill": prefill, "parallelism": "single GPU"},
         "roofline": roofline,
         "attention": {k: attn[k] for k in ("bound", "achieved", "peak", "unit", "frac", "ms")},
+        "lm_head": {k: lmh[k] for k in ("bound", "achieved", "peak", "unit", "frac", "ms")},
+        "prefill": prefill_info,
         "step_roofline": {"algorithmic_bytes": int(sb), "hbm_bound_ms": round(sb / HBM_PEAK * 1e3, 4),
                           "frac": round(sb / HBM_PEAK * 1e3 / ms, 4)},
         "breakdown": breakdown,

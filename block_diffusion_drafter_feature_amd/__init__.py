@@ -36,7 +36,8 @@ DFLASH_PATH_EXACT = 1
 MAX_LAYERS = 16
 CONV_SITES = 4
 BLOCK = 16
-PROBES = ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv")
+PROBES = ("lm_head", "topk", "attn", "qkv", "o", "gate_up", "down", "inject_fc", "inject_kv", "conv_pre",
+          "conv_post")
 N_PROBES = len(PROBES)
 
 EXPORTED = (
@@ -45,7 +46,7 @@ EXPORTED = (
     "dflash_calibrate_workspace_bytes", "dflash_path_table_bytes", "dflash_build_path_table",
     "dflash_inject_workspace_bytes", "dflash_draft_workspace_bytes", "dflash_path_workspace_bytes",
     "dflash_verify_workspace_bytes", "dflash_verify_sampled_workspace_bytes", "dflash_check_config",
-    "dflash_status_string", "dflash_verify_noalloc",
+    "dflash_status_string", "dflash_kv_bytes", "dflash_verify_noalloc",
 )
 
 
@@ -129,6 +130,7 @@ def lib() -> ctypes.CDLL:
             "dflash_path_workspace_bytes": ([cfgp, _i32], PC),
             "dflash_verify_workspace_bytes": ([_i32, _i32, _i32], PC),
             "dflash_check_config": ([cfgp], ctypes.c_int),
+            "dflash_kv_bytes": ([cfgp, _i32, _i32], PC),
             "dflash_verify_noalloc": ([_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp], ctypes.c_int),
             "dflash_status_string": ([ctypes.c_int], ctypes.c_char_p),
         }
@@ -179,6 +181,10 @@ def dflash_inject_workspace_bytes(cfg: dflash_config, n_rows: int) -> int:
 
 def dflash_draft_workspace_bytes(cfg: dflash_config, batch: int, cap: int) -> int:
     return lib().dflash_draft_workspace_bytes(ctypes.byref(cfg), batch, cap)
+
+
+def dflash_kv_bytes(cfg: dflash_config, batch: int, cap: int) -> int:
+    return lib().dflash_kv_bytes(ctypes.byref(cfg), batch, cap)
 
 
 def dflash_path_workspace_bytes(cfg: dflash_config, batch: int) -> int:

@@ -6,6 +6,7 @@
 #include "attention.h"
 #include <cmath>
 #include "common.h"
+#include "conv.h"
 #include "elementwise.h"
 #include "epilogues.h"
 #include "gemm.h"
@@ -87,9 +88,16 @@ int check_weights(const dflash_config* c, const dflash_weights* w, bool draft, b
   return DFLASH_OK;
 }
 
+// The attention kernel addresses one (sequence, kv head) slice of the cache through a
+// buffer descriptor with 32-bit offsets and takes 2^31 as its "past the end" offset, so a
+// slice (cap rows of head_dim elements) must stay below 2 GiB.
+bool kv_slice_ok(const dflash_config* c, int cap) {
+  return static_cast<int64_t>(cap) * c->head_dim * static_cast<int64_t>(esize(c)) < (int64_t{1} << 31);
+}
+
 int check_kv(const dflash_config* c, const dflash_kv* kv, int batch) {
   if (!kv || kv->cap <= 0 || kv->batch <= 0) return DFLASH_E_INVAL;
-  if (kv->cap % 32) return DFLASH_E_UNSUPPORTED;
+  if (kv->cap % 32 || !kv_slice_ok(c, kv->cap)) return DFLASH_E_UNSUPPORTED;
   if (batch > kv->batch) return DFLASH_E_CAPACITY;
   for (int l = 0; l < c->n_layers; ++l)
     if (!kv->k[l] || !kv->vt[l]) return DFLASH_E_INVAL;
@@ -147,7 +155,8 @@ int attn_ctx_splits(const dflash_config* c, int batch, int cap, int S) {
 template <typename T>
 struct DraftWs {
   float* x;       // [M][d] residual stream
-  float* uf;      // [M][max(d)] normed (or post-GEMM) rows before the conv, fp32
+  float* uf;      // [M][d] sublayer GEMM output before the conv, fp32
+  float* ss;      // [M][d/256 rounded up] partial sums of squares of x rows (conv kernels)
   T* ut;          // [M][d] GEMM operand
   T* q;           // [M][H*hd]
   T* kb;          // [B][Hkv][16][hd]
@@ -155,7 +164,6 @@ struct DraftWs {
   float* part_o;  // [B][Hkv][S][G][16][hd]
   float* part_ml;
   T* o;           // [M][H*hd]
-  float* delta;   // [M][2*d/16]
   T* h;           // [M][d_ffn]
   float* logits;  // [M][V] (when the caller passes none)
   float* tk_v;    // [M][n_chunks][16]
@@ -174,6 +182,7 @@ DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
   const int nch = (c->vocab + kTopkChunk - 1) / kTopkChunk;
   w.x = cv.take<float>(M * d);
   w.uf = cv.take<float>(M * d);
+  w.ss = cv.take<float>(M * ((d / 16 + 15) / 16));
   w.ut = cv.take<T>(M * d);
   w.q = cv.take<T>(M * hq);
   w.kb = cv.take<T>(static_cast<size_t>(B) * c->n_kv_heads * 16 * c->head_dim);
@@ -181,7 +190,6 @@ DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
   w.part_o = cv.take<float>(static_cast<size_t>(B) * c->n_kv_heads * w.S * G * 16 * c->head_dim);
   w.part_ml = cv.take<float>(static_cast<size_t>(B) * c->n_kv_heads * w.S * G * 16 * 2);
   w.o = cv.take<T>(M * hq);
-  w.delta = cv.take<float>(M * 2 * (d / 16));
   w.h = cv.take<T>(M * c->d_ffn);
   w.logits = cv.take<float>(M * c->vocab);
   // top-16 partial lists: one per vocabulary chunk, or one per LM-head work-group when
@@ -197,7 +205,6 @@ DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
   sc = std::max(sc, splitk_scratch_bytes<T>(Mi, di, 2 * (F / 16)));
   sc = std::max(sc, splitk_scratch_bytes<T>(Mi, F, di / 16));
   sc = std::max(sc, splitk_scratch_bytes<T>(Mi, di, c->vocab / 16));
-  if (c->use_conv) sc = std::max(sc, splitk_scratch_bytes<T>(Mi, di, (2 * (di / 16) + 15) / 16));
   w.scratch_bytes = sc;
   w.scratch = cv.take<float>(sc / sizeof(float) + 1);
   return w;
@@ -409,49 +416,48 @@ hipError_t run_attention(const dflash_config* c, const AttnArgs<T>& a, int B, hi
                            : launch_combine<T, 128>(a, c->n_heads, c->n_kv_heads, B, s);
 }
 
-// pre-sublayer input: u = RMSNorm(x; g), conv'd when enabled, rounded to T into W.ut
+// pre-sublayer input: u = RMSNorm(x; g), conv'd when enabled, rounded to T into W.ut (the
+// first layer gathers the block's embedding rows into x in the same launch)
 template <typename T>
 int pre_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site, const void* gain, int M,
-                 DraftWs<T>& W, hipStream_t s, const T* emb = nullptr, const int32_t* ids = nullptr) {
+                 DraftWs<T>& W, hipStream_t s, const T* emb = nullptr, const int32_t* ids = nullptr,
+                 const Probe* pr = nullptr) {
   const int d = c->d_model;
   if (!c->use_conv) {
     rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, W.ut, nullptr, emb, ids);
     LAUNCH_CHECK();
     return DFLASH_OK;
   }
-  rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, nullptr, W.uf, emb, ids);
+  if (pr) pr->begin(DFLASH_PROBE_CONV_PRE);
+  // row scales: the first layer's gathered rows are summed in the kernel; later inputs come
+  // from a post-sublayer conv, which leaves partial sums of squares of the rows it wrote
+  const int tiles = (d / 16 + 15) / 16;
+  conv_site_kernel<T, true><<<dim3(tiles, M / 16), 64 * kConvWaves, 0, s>>>(
+      W.x, emb, ids, emb ? nullptr : W.ss, tiles, static_cast<const T*>(gain), c->rms_eps,
+      static_cast<const T*>(L.conv_gen[site]), static_cast<const T*>(L.conv_w0[site]),
+      static_cast<const T*>(L.conv_w1[site]), d, W.x, nullptr, W.ut);
   LAUNCH_CHECK();
-  EpiStore<T> e{seg1<T>(L.conv_gen[site], 2 * (d / 16), d), W.delta, 2 * (d / 16), STORE};
-  GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, e, s, W.scratch,
-                                   W.scratch_bytes)));
-  conv_apply_kernel<T><<<M, 256, 0, s>>>(W.uf, W.delta, static_cast<const T*>(L.conv_w0[site]),
-                                         static_cast<const T*>(L.conv_w1[site]), d, 0, W.ut, nullptr);
-  LAUNCH_CHECK();
+  if (pr) pr->end(DFLASH_PROBE_CONV_PRE);
   return DFLASH_OK;
 }
 
-// post-sublayer: x += A W^T, through the conv when enabled
+// post-sublayer: x += A W^T, through the conv when enabled (the GEMM stores its rows, the
+// conv kernel adds the conv'd rows to x)
 template <typename T, typename AS>
 int post_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site, const void* wmat, const AS* A,
                   int K, int M, DraftWs<T>& W, const Probe& pr, int probe, hipStream_t s) {
   const int d = c->d_model;
-  if (!c->use_conv) {
-    EpiStore<T> e{seg1<T>(wmat, d, wstride(c, K)), W.x, d, ADD};
-    pr.begin(probe);
-    GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
-    pr.end(probe);
-    return DFLASH_OK;
-  }
-  EpiStore<T> e{seg1<T>(wmat, d, wstride(c, K)), W.uf, d, STORE};
+  EpiStore<T> e{seg1<T>(wmat, d, wstride(c, K)), c->use_conv ? W.uf : W.x, d, c->use_conv ? STORE : ADD};
   pr.begin(probe);
   GEMM_CHECK((run_gemm<T, AS>(A, K, nullptr, M, K, d / 16, e, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
   pr.end(probe);
-  EpiStore<T> g{seg1<T>(L.conv_gen[site], 2 * (d / 16), d), W.delta, 2 * (d / 16), STORE};
-  GEMM_CHECK((run_gemm<T, float>(W.uf, d, nullptr, M, d, (2 * (d / 16) + 15) / 16, g, s, W.scratch,
-                                   W.scratch_bytes)));
-  conv_apply_kernel<T><<<M, 256, 0, s>>>(W.uf, W.delta, static_cast<const T*>(L.conv_w0[site]),
-                                         static_cast<const T*>(L.conv_w1[site]), d, 1, nullptr, W.x);
+  if (!c->use_conv) return DFLASH_OK;
+  if (probe == DFLASH_PROBE_O) pr.begin(DFLASH_PROBE_CONV_POST);
+  conv_site_kernel<T, false><<<dim3((d / 16 + 15) / 16, M / 16), 64 * kConvWaves, 0, s>>>(
+      W.uf, nullptr, nullptr, nullptr, 0, nullptr, 0.f, static_cast<const T*>(L.conv_gen[site]),
+      static_cast<const T*>(L.conv_w0[site]), static_cast<const T*>(L.conv_w1[site]), d, W.x, W.ss, nullptr);
   LAUNCH_CHECK();
+  if (probe == DFLASH_PROBE_O) pr.end(DFLASH_PROBE_CONV_POST);
   return DFLASH_OK;
 }
 
@@ -488,7 +494,7 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
     pr.end(DFLASH_PROBE_ATTN);
     if ((rc = post_sublayer<T, T>(c, L, 1, L.w_o, W.o, hq, M, W, pr, DFLASH_PROBE_O, s))) return rc;
     // feed-forward sublayer
-    if ((rc = pre_sublayer<T>(c, L, 2, L.g_ffn, M, W, s))) return rc;
+    if ((rc = pre_sublayer<T>(c, L, 2, L.g_ffn, M, W, s, nullptr, nullptr, &pr))) return rc;
     EpiSwiGLU<T> ef{static_cast<const T*>(L.w_gate), static_cast<const T*>(L.w_up), wstride(c, d), F, W.h};
     pr.begin(DFLASH_PROBE_GATE_UP);
     GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, 2 * (F / 16), ef, s, W.scratch, W.scratch_bytes, 0,
@@ -674,6 +680,12 @@ const char* dflash_status_string(int status) {
     case DFLASH_E_HIP: return "HIP launch failed";
     default: return "unknown status";
   }
+}
+
+size_t dflash_kv_bytes(const dflash_config* cfg, int32_t batch, int32_t cap) {
+  if (check_config(cfg) != DFLASH_OK || batch <= 0 || cap <= 0 || cap % 32 || !kv_slice_ok(cfg, cap)) return 0;
+  return static_cast<size_t>(2) * cfg->n_layers * batch * cfg->n_kv_heads * static_cast<size_t>(cap) *
+         cfg->head_dim * esize(cfg);
 }
 
 size_t dflash_inject_workspace_bytes(const dflash_config* cfg, int32_t n_rows) {

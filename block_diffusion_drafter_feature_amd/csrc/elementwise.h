@@ -1,5 +1,5 @@
 // Row-wise kernels of the drafter: RMSNorm (optionally gathering the embedding rows
-// first), the dynamic short conv's apply step.  One work-group per row; fixed-order reductions.
+// first), the calibration MLP's input rows, FP8 weight quantization.  One work-group per row; fixed-order reductions.
 #pragma once
 
 #include "common.h"
@@ -83,27 +83,6 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, con
     if (c < nv) emit(c, v[i], gv[i]);
   }
   for (int c = threadIdx.x + 256 * MAXV; c < nv; c += 256) emit(c, xr[c], load4<T>(g + 4 * c));
-}
-
-// Dynamic short conv, apply step, for block rows m (row j = m % 16 of its block):
-//   a = w0 + delta[m][c/16],  b = w1 + delta[m][d/16 + c/16]
-//   y = u[m] + a * u[m] + b * u[m-1]     (u[m-1] = 0 on block row 0)
-// mode 0: out_t[m] = y rounded to T (a GEMM operand);  mode 1: x[m] += y (residual).
-template <typename T>
-__global__ __launch_bounds__(256) void conv_apply_kernel(const float* __restrict__ u, const float* __restrict__ delta,
-                                                         const T* __restrict__ w0, const T* __restrict__ w1, int d,
-                                                         int mode, T* __restrict__ out_t, float* __restrict__ x) {
-  const int m = blockIdx.x, j = m & 15, ng = d / 16;
-  const float* ur = u + static_cast<size_t>(m) * d;
-  const float* dr = delta + static_cast<size_t>(m) * 2 * ng;
-  for (int c = threadIdx.x; c < d; c += blockDim.x) {
-    const float a = to_f<T>(w0[c]) + dr[c >> 4];
-    const float bb = to_f<T>(w1[c]) + dr[ng + (c >> 4)];
-    const float prev = j > 0 ? ur[c - d] : 0.f;
-    const float y = ur[c] + a * ur[c] + bb * prev;
-    if (mode == 0) out_t[static_cast<size_t>(m) * d + c] = from_f<T>(y);
-    else x[static_cast<size_t>(m) * d + c] += y;
-  }
 }
 
 // ------------------------------------------------------------------ bonus calibration input

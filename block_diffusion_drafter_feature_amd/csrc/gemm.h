@@ -1078,16 +1078,14 @@ static hipError_t launch_skinny_w8(const T* A, int lda, const int32_t* arows, in
 }
 
 // Work-groups of the persistent streaming kernel: one per compute unit of the current
-// device (queried once per device), never more than there are work units.
+// device (asked of the runtime at each launch, so no state is kept between calls), never
+// more than there are work units.
 inline int stream_grid(int n_vtiles) {
-  static int cus[64] = {0};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cus[dev] <= 0) {
-    int n = 0;
-    cus[dev] = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0 ? n : 256;
-  }
-  return n_vtiles < cus[dev] ? n_vtiles : cus[dev];
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    n = 256;
+  return n_vtiles < n ? n_vtiles : n;
 }
 
 // One drafted block against a wide weight stream (QKV, K/V injection, gate/up, LM head):

@@ -150,8 +150,9 @@ typedef struct dflash_weights {
 /* The drafter's KV cache of injected context, one pair of arrays per layer.
  *   k[l]  : [batch][Hkv][cap][hd]   keys after RoPE, position-major
  *   vt[l] : [batch][Hkv][hd][cap]   values, transposed (position contiguous)
- * cap is a multiple of 32.  Row p of sequence b holds context position p.  Rows at
- * or beyond a sequence's context length are never read by dflash_draft_block. */
+ * cap is a multiple of 32, and one (sequence, kv head) slice, cap * hd elements, stays
+ * below 2 GiB (else DFLASH_E_UNSUPPORTED).  Row p of sequence b holds context position p.
+ * Rows at or beyond a sequence's context length are never read by dflash_draft_block. */
 typedef struct dflash_kv {
   void*   k[DFLASH_MAX_LAYERS];
   void*   vt[DFLASH_MAX_LAYERS];
@@ -172,7 +173,9 @@ typedef struct dflash_kv {
 #define DFLASH_PROBE_DOWN       6   /* draft: FFN down projection (+ residual)      */
 #define DFLASH_PROBE_INJECT_FC  7   /* inject: context-feature projection GEMM      */
 #define DFLASH_PROBE_INJECT_KV  8   /* inject: K/V projection + RoPE + cache scatter */
-#define DFLASH_N_PROBES         9
+#define DFLASH_PROBE_CONV_PRE   9   /* draft (use_conv): the FFN input's norm and short conv    */
+#define DFLASH_PROBE_CONV_POST 10   /* draft (use_conv): the short conv on the attention output */
+#define DFLASH_N_PROBES        11
 typedef struct dflash_probes {
   hipEvent_t begin[DFLASH_N_PROBES];
   hipEvent_t end[DFLASH_N_PROBES];
@@ -387,7 +390,6 @@ int dflash_verify_sampled(const int32_t* draft, const int32_t* q_ids, int64_t q_
 int dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batch, int32_t mask_id, int32_t cap,
                    int32_t* ctx_len, int32_t* pos0, int32_t* n_new, int32_t* block_ids, hipStream_t stream);
 
-/* Workspace sizes in bytes (0 when the arguments are invalid). */
 /* FP8 storage of one weight matrix (see dflash_weights).
  *
  * w   : device bf16 [rows, cols], row-major.
@@ -399,12 +401,21 @@ int dflash_advance(const int32_t* accept_len, const int32_t* bonus, int32_t batc
  */
 int dflash_quantize_fp8(const void* w, int32_t rows, int32_t cols, void* out, hipStream_t stream);
 
+/* Workspace sizes in bytes (0 when the arguments are invalid). */
 size_t dflash_inject_workspace_bytes(const dflash_config* cfg, int32_t n_rows);
 size_t dflash_draft_workspace_bytes(const dflash_config* cfg, int32_t batch, int32_t cap);
 size_t dflash_path_workspace_bytes(const dflash_config* cfg, int32_t batch);
 size_t dflash_verify_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab);
 size_t dflash_verify_sampled_workspace_bytes(int32_t batch, int32_t n_draft, int32_t vocab);
 size_t dflash_calibrate_workspace_bytes(const dflash_config* cfg, int32_t batch);
+
+/* Bytes of a whole KV cache ("DFlash ...", section 2.2: the context features injected
+ * into every drafter layer's keys and values) for `batch` sequences of `cap` rows: all
+ * 2 * n_layers arrays of dflash_kv, each of them batch * Hkv * cap * hd elements of the
+ * storage type (so one array is this size / (2 * n_layers)).  0 when the configuration
+ * is invalid, batch <= 0, cap <= 0, cap is not a multiple of 32 or a slice would reach
+ * 2 GiB.  The caller allocates the arrays. */
+size_t dflash_kv_bytes(const dflash_config* cfg, int32_t batch, int32_t cap);
 
 /* Check a configuration against what the kernels support: DFLASH_OK, DFLASH_E_INVAL
  * or DFLASH_E_UNSUPPORTED. */

@@ -22,7 +22,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 20
+    assert len(names) == 21
     lib = ctypes.CDLL(D.LIB_PATH)
     for n in names:
         assert hasattr(lib, n), n
@@ -119,6 +119,23 @@ def test_calls_validate_before_launch():
     assert _status(D.dflash_verify, FAKE, FAKE, 9, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_INVAL
     assert _status(D.dflash_verify, FAKE, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v - 1, S) == D.DFLASH_E_WORKSPACE
     assert _status(D.dflash_verify, None, FAKE, D.DFLASH_BF16, 2, 15, 1024, FAKE, FAKE, FAKE, ws_v, S) == D.DFLASH_E_INVAL
+
+
+def test_kv_bytes_and_slice_bound():
+    cfg = D.make_config(synth.workload("c2").dims)
+    assert D.dflash_kv_bytes(cfg, 1, 4096) == 2 * 5 * 8 * 4096 * 128 * 2
+    assert D.dflash_kv_bytes(cfg, 3, 64) == 3 * D.dflash_kv_bytes(cfg, 1, 64)
+    assert D.dflash_kv_bytes(cfg, 1, 48) == 0            # not a multiple of 32
+    assert D.dflash_kv_bytes(cfg, 0, 64) == 0
+    # one (sequence, kv head) slice must stay below 2 GiB: cap * 128 * 2 B
+    big = (1 << 31) // (128 * 2)
+    assert D.dflash_kv_bytes(cfg, 1, big - 32) > 0
+    assert D.dflash_kv_bytes(cfg, 1, big) == 0
+    dims = synth.workload("c2").dims
+    cfg, w, kv = _fake_structs(dims, batch=1, cap=big)
+    ws_d = D.dflash_draft_workspace_bytes(cfg, 1, 64)
+    assert _status(D.dflash_draft_block, cfg, w, kv, FAKE, FAKE, 1, FAKE, FAKE, FAKE, None, FAKE, ws_d, None, 1) == D.DFLASH_E_UNSUPPORTED
+    assert _status(D.dflash_inject_context, cfg, w, kv, FAKE, 8, FAKE, FAKE, FAKE, 1, FAKE, 1 << 40, None, 1) == D.DFLASH_E_UNSUPPORTED
 
 
 def test_verify_noalloc_rejects_before_launch():
