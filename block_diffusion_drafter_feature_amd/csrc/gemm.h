@@ -940,8 +940,12 @@ inline int splitk_plan(int M, int K, int n_vtiles) {
 // factor, from measurements on MI355X.
 //  * M <= 64 (weight streaming), or grids of fewer than 32 tiles of 128 x 128: 64 x 128
 //    tiles, 3 slots; K split until the grid has >= 128 work-groups (>= 256 at M <= 16).
-//  * M >= 384 with >= 256 tiles of 256 x 128: those tiles, 3 slots (each weight tile is
-//    read by fewer work-groups).
+//  * M >= 256: 256 x 128 tiles, 3 slots (each weight tile is read by fewer work-groups, and
+//    the grid moves fewer bytes per flop); when there are fewer than 192 of them, K split
+//    (at most 4 ways, >= 16 slabs per split) until the grid reaches 192 work-groups.  Cold
+//    sweeps at 256 rows (x 4096 K unless noted): gate/up 24576 wide 92 -> 75 us, QKV 6144
+//    wide 40 -> 30 us, O 4096 wide 36 -> 26 us, down (K 12288) 56 -> 55 us, against
+//    128 x 128 tiles.
 //  * otherwise 128 x 128 tiles, 2 slots (two work-groups per compute unit); when there are
 //    fewer than 256 tiles, K split until the grid has >= 512 work-groups with >= 16 slabs
 //    (1024 K values) per split.
@@ -951,9 +955,9 @@ struct BigPlan {
 };
 inline BigPlan big_plan(int M, int K, int n_vtiles) {
   const int N = n_vtiles * 16;
-  auto split = [&](long tiles, long want, int min_slabs) {
+  auto split = [&](long tiles, long want, int min_slabs, int max_ks = 8) {
     int ks = 1;
-    while (ks < 8 && tiles * ks < want && (K / 64) % (2 * ks) == 0 && K / 64 / (2 * ks) >= min_slabs) ks *= 2;
+    while (ks < max_ks && tiles * ks < want && (K / 64) % (2 * ks) == 0 && K / 64 / (2 * ks) >= min_slabs) ks *= 2;
     return ks;
   };
   const long t128 = static_cast<long>((M + 127) / 128) * ((N + 127) / 128);
@@ -962,7 +966,7 @@ inline BigPlan big_plan(int M, int K, int n_vtiles) {
     return {64, 128, 3, split(tiles, M <= 16 ? 256 : 128, 4)};
   }
   const long t256 = static_cast<long>((M + 255) / 256) * ((N + 127) / 128);
-  if (M >= 256 && t256 >= 256) return {256, 128, 3, 1};
+  if (M >= 256) return {256, 128, 3, split(t256, 192, 16, 4)};
   return {128, 128, 2, t128 >= 256 ? 1 : split(t128, 512, 16)};
 }
 
