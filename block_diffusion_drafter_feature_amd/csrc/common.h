@@ -16,6 +16,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <cmath>
+
 namespace dflash {
 
 typedef uint16_t bf16_t;
@@ -144,11 +146,23 @@ template <> struct Frag<float> {
 
 // ------------------------------------------------------------------ rotary encoding
 
-// cos/sin of the rotary angle pos * theta^(-2i/hd) (log_theta = ln theta).  The angle is formed and
-// reduced to [-pi, pi] in double precision (context positions reach 10^5 and a
-// float angle would be off by ~1e-2 rad there), then evaluated in float.
-__device__ __forceinline__ void rope_cs(int pos, int i, int hd, double log_theta, float* c, float* s) {
-  const double inv = exp(-(2.0 * i / hd) * log_theta);
+// Inverse rotary frequencies theta^(-2i/hd), i < hd/2, in double: filled once per call on the
+// host (rope_freq) and carried by value in the epilogues, so no element evaluates exp.
+struct RopeFreq {
+  double inv[64];
+};
+
+inline RopeFreq rope_freq(double theta, int hd) {
+  RopeFreq f{};
+  const double lt = std::log(theta);
+  for (int i = 0; i < hd / 2 && i < 64; ++i) f.inv[i] = std::exp(-(2.0 * i / hd) * lt);
+  return f;
+}
+
+// cos/sin of the rotary angle pos * inv.  The angle is formed and reduced to [-pi, pi] in
+// double precision (context positions reach 10^5 and a float angle would be off by ~1e-2
+// rad there), then evaluated in float.
+__device__ __forceinline__ void rope_cs(int pos, double inv, float* c, float* s) {
   double a = static_cast<double>(pos) * inv;
   const double two_pi = 6.283185307179586476925286766559;
   a -= two_pi * rint(a / two_pi);

@@ -362,7 +362,7 @@ int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv
   e.hd = c->head_dim;
   e.B = B;
   e.cap = kv->cap;
-  e.log_theta = std::log(static_cast<double>(c->rope_theta));
+  e.rf = rope_freq(c->rope_theta, c->head_dim);
   e.row_off = row_off;
   e.pos0 = pos0;
   e.n_new = n_new;
@@ -479,8 +479,7 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
                               l == 0 ? block_ids : nullptr)))
       return rc;
     EpiQKV<T> eq{static_cast<const T*>(L.w_q), static_cast<const T*>(L.w_k), static_cast<const T*>(L.w_v),
-                 wstride(c, d), H, Hkv, hd, std::log(static_cast<double>(c->rope_theta)), ctx_len, W.q, W.kb,
-                 W.vbt};
+                 wstride(c, d), H, Hkv, hd, rope_freq(c->rope_theta, hd), ctx_len, W.q, W.kb, W.vbt};
     pr.begin(DFLASH_PROBE_QKV);
     GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, (hq + 2 * Hkv * hd) / 16, eq, s, W.scratch,
                                W.scratch_bytes, 0, fp8w(c))));

@@ -106,7 +106,7 @@ struct EpiQKV {
   const T* wk;
   const T* wv;
   int K, H, Hkv, hd;
-  double log_theta;        // ln(rope theta)
+  RopeFreq rf;             // inverse rotary frequencies
   const int32_t* ctx_len;  // [B]
   T* q;                    // [M][H][hd]
   T* kb;                   // [B][Hkv][16][hd]
@@ -146,7 +146,7 @@ struct EpiQKV {
       const int head = t / tph, tt = t % tph;
       const int dim = rope_dim(tt, c, hd);
       float cs, sn;
-      rope_cs(rw.pos, 8 * tt + (c & 7), hd, log_theta, &cs, &sn);
+      rope_cs(rw.pos, rf.inv[8 * tt + (c & 7)], &cs, &sn);
       const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
       if (isq) q[(static_cast<size_t>(m) * H + head) * hd + dim] = from_f<T>(r);
       else kb[((static_cast<size_t>(b) * Hkv + head) * 16 + j) * hd + dim] = from_f<T>(r);
@@ -168,7 +168,7 @@ struct EpiInject {
   T* kc[16];
   T* vtc[16];
   int K, L, Hkv, hd, B, cap;
-  double log_theta;        // ln(rope theta)
+  RopeFreq rf;             // inverse rotary frequencies
   const int32_t* row_off;  // [B+1]
   const int32_t* pos0;     // [B]
   const int32_t* n_new;    // [B]
@@ -220,7 +220,7 @@ struct EpiInject {
     if (t < tk) {
       const int head = t / tph, tt = t % tph, dim = rope_dim(tt, c, hd);
       float cs, sn;
-      rope_cs(pos, 8 * tt + (c & 7), hd, log_theta, &cs, &sn);
+      rope_cs(pos, rf.inv[8 * tt + (c & 7)], &cs, &sn);
       const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
       kc[l][((static_cast<size_t>(b) * Hkv + head) * cap + pos) * hd + dim] = from_f<T>(r);
     } else {
