@@ -941,11 +941,12 @@ inline int splitk_plan(int M, int K, int n_vtiles) {
 //  * M <= 64 (weight streaming), or grids of fewer than 32 tiles of 128 x 128: 64 x 128
 //    tiles, 3 slots; K split until the grid has >= 128 work-groups (>= 256 at M <= 16).
 //  * M >= 256: 256 x 128 tiles, 3 slots (each weight tile is read by fewer work-groups, and
-//    the grid moves fewer bytes per flop); when there are fewer than 192 of them, K split
-//    (at most 4 ways, >= 16 slabs per split) until the grid reaches 192 work-groups.  Cold
-//    sweeps at 256 rows (x 4096 K unless noted): gate/up 24576 wide 92 -> 75 us, QKV 6144
-//    wide 40 -> 30 us, O 4096 wide 36 -> 26 us, down (K 12288) 56 -> 55 us, against
-//    128 x 128 tiles.
+//    the grid moves fewer bytes per flop); when there are fewer than 128 of them, K split
+//    (at most 8 ways, >= 16 slabs per split) until the grid reaches 256 work-groups.  Cold
+//    sweeps at 256 rows (x 4096 K unless noted), against 128 x 128 tiles without the long
+//    splits: gate/up 24576 wide 92 -> 75 us (unsplit; 2 splits 90 us), QKV 6144 wide 40 ->
+//    30 us (4 splits), O 4096 wide 36 -> 26 us (4), K/V injection 10240 wide 54 -> 44 us
+//    (2), down (K 12288) 56 -> 42 us (8), context fusion (K 20480) 83 -> 57 us (8).
 //  * otherwise 128 x 128 tiles, 2 slots (two work-groups per compute unit); when there are
 //    fewer than 256 tiles, K split until the grid has >= 512 work-groups with >= 16 slabs
 //    (1024 K values) per split.
@@ -966,7 +967,7 @@ inline BigPlan big_plan(int M, int K, int n_vtiles) {
     return {64, 128, 3, split(tiles, M <= 16 ? 256 : 128, 4)};
   }
   const long t256 = static_cast<long>((M + 255) / 256) * ((N + 127) / 128);
-  if (M >= 256) return {256, 128, 3, split(t256, 192, 16, 4)};
+  if (M >= 256) return {256, 128, 3, t256 < 128 ? split(t256, 256, 16, 8) : 1};
   return {128, 128, 2, t128 >= 256 ? 1 : split(t128, 512, 16)};
 }
 
