@@ -217,6 +217,7 @@ struct PathWs {
   float* z;         // [B][T][2*PD]
   float* gamma;     // [B*16][PD]
   float* S;         // [B][16][16][16] pair scores
+  void* xb;         // [B*16][d] final hidden rounded to the weights' type (bf16 only)
   float* scratch;
   size_t scratch_bytes;
 };
@@ -228,6 +229,7 @@ PathWs carve_path(Carver& cv, const dflash_config* c, int B) {
   w.z = cv.take<float>(B * T * 2 * c->ps_dim);
   w.gamma = cv.take<float>(static_cast<size_t>(B) * 16 * c->ps_dim);
   w.S = cv.take<float>(static_cast<size_t>(B) * 16 * 256);
+  w.xb = std::is_same<X, bf16_t>::value ? cv.take<X>(static_cast<size_t>(B) * 16 * c->d_model) : nullptr;
   size_t sc = 0;
   for (int nf = 0; nf < 2; ++nf)
     sc = std::max(sc, splitk_scratch_bytes<X>(B * (16 * (16 - nf) + nf), c->d_model, 2 * c->ps_dim / 16));
@@ -559,8 +561,21 @@ int path_impl(const dflash_config* c, const dflash_weights* w, const int32_t* ca
   }
   if (c->use_gate) {
     EpiStore<T> e{seg1<T>(w->ps_gate, PD, d), W.gamma, PD, SIGMOID};
-    GEMM_CHECK((run_gemm<T, float>(final_hidden, d, nullptr, 16 * B, d, PD / 16, e, s, W.scratch,
-                                   W.scratch_bytes)));
+    bool rounded = false;
+    if constexpr (std::is_same<T, bf16_t>::value) rounded = (reinterpret_cast<uintptr_t>(final_hidden) & 15) == 0;
+    if (rounded) {
+      // the gate reads bf16(x^): rounded once here so the pipelined bf16 kernel applies
+      // (256 x 256 x 4096: 31 us on the fp32-input tiled kernel)
+      T* xb = static_cast<T*>(W.xb);
+      const size_t n4 = static_cast<size_t>(16) * B * d / 4;
+      round_to_kernel<T><<<static_cast<unsigned>(std::min<size_t>((n4 + 255) / 256, 2048)), 256, 0, s>>>(
+          final_hidden, n4, xb);
+      LAUNCH_CHECK();
+      GEMM_CHECK((run_gemm<T, T>(xb, d, nullptr, 16 * B, d, PD / 16, e, s, W.scratch, W.scratch_bytes)));
+    } else {   // fp32 storage, or rows not 16-byte aligned: A widened/rounded as it is loaded
+      GEMM_CHECK((run_gemm<T, float>(final_hidden, d, nullptr, 16 * B, d, PD / 16, e, s, W.scratch,
+                                     W.scratch_bytes)));
+    }
   }
   const size_t smem = 2 * 16 * (c->ps_rank + 1) * sizeof(float);
   path_scores_kernel<T><<<dim3(P, B), 512, smem, s>>>(W.z, c->use_gate ? W.gamma : nullptr,

@@ -1,5 +1,6 @@
 // Row-wise kernels of the drafter: RMSNorm (optionally gathering the embedding rows
-// first), the calibration MLP's input rows, FP8 weight quantization.  One work-group per row; fixed-order reductions.
+// first), the calibration MLP's input rows, rounding fp32 rows to the weights' type, FP8
+// weight quantization.  One work-group per row; fixed-order reductions.
 #pragma once
 
 #include "common.h"
@@ -99,6 +100,19 @@ __global__ __launch_bounds__(256) void cal_input_kernel(const T* __restrict__ em
   for (int j = threadIdx.x; j < d; j += 256) {
     o[j] = e[j];
     o[d + j] = from_f<T>(x[j]);
+  }
+}
+
+// ------------------------------------------------------------------ rounding to T
+
+// y = x rounded to T, 4 elements per thread (n a multiple of 4, both 4-element aligned):
+// hands fp32 rows to the bf16 GEMM kernels, which read A only in the weights' type.
+template <typename T>
+__global__ __launch_bounds__(256) void round_to_kernel(const float* __restrict__ x, size_t n4, T* __restrict__ y) {
+  for (size_t i = blockIdx.x * static_cast<size_t>(256) + threadIdx.x; i < n4; i += static_cast<size_t>(gridDim.x) * 256) {
+    const f32x4_t v = *reinterpret_cast<const f32x4_t*>(x + 4 * i);
+    const float u[4] = {v[0], v[1], v[2], v[3]};
+    store4<T>(y + 4 * i, u);
   }
 }
 

@@ -234,6 +234,7 @@ int dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const 
  * rows are mask tokens) or 1 (row 0 is the anchor block_ids[b][0]).  With
  *   z_l(t) = ps_left * E[t],  z_r(t) = ps_right * E[t]                (256-d)
  *   gamma_i = sigmoid(ps_gate * xhat_i)  (use_gate; else 1), xhat_i = final_hidden row i
+ *             rounded to the storage type
  *   phi_i(a, t) = (ps_u * z_l(a)) . (ps_v * (gamma_i (.) z_r(t)))
  * the score of candidate j at drafted position p given left token a is
  *   cand_logits[p][j] + phi_{row p}(a, cand_ids[p][j])
