@@ -53,6 +53,32 @@ __device__ __forceinline__ void load8f(const T* p, float (&v)[8]) {
   }
 }
 
+// Per-wave LDS staging of the corrections' operands (bf16 weights, rows not gathered, d <=
+// 4096): slot I of wave w holds one 64-k slab -- the 16 fp32 rows (4 KB, chunk c of row r at
+// position c ^ (r & 15)) and the tile's 32 generator rows (4 KB, chunk c of row r at
+// c ^ ((r >> 1) & 7)) -- and (PRE) one 1 KB block holds the RMSNorm gains of all of the wave's
+// slabs; all are filled by direct loads.  Fragment-shaped loads straight into
+// registers (16 rows x 64 B per instruction) stream these operands at well under half the
+// rate (~33 against ~74 GB/s per work-group).
+constexpr int kConvSlabBytes = 8192;
+constexpr int kConvMaxStagedD = 4096;   // at most 8 slabs per wave (one 1 KB block of gains)
+template <int I>
+__device__ __forceinline__ char* conv_ring() {
+  __shared__ __attribute__((aligned(16))) char s[kConvWaves * kConvSlabBytes];
+  return s;
+}
+
+template <typename T>
+__device__ __forceinline__ T* conv_gains() {   // [wave][slab][64]
+  __shared__ __attribute__((aligned(16))) T s[kConvWaves * 512];
+  return s;
+}
+
+__device__ __forceinline__ void conv_dma(const void* g, void* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+
 template <typename T, bool PRE>
 __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
     const float* __restrict__ src,      // PRE: residual x (unless gathering); POST: sublayer output
@@ -136,38 +162,122 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
 
   f32x4_t acc_a{0.f, 0.f, 0.f, 0.f}, acc_b{0.f, 0.f, 0.f, 0.f};
   const int nks = d / 32;
-  // wave w takes k-steps w, w + NW, w + 2 NW, ...: U of them per stage, all of a stage's
-  // loads issued together (A as raw fp32 rows, scaled and rounded once the row scales are in)
-  for (int s0 = wave; s0 < nks; s0 += NW * U) {
-    float av[U][8], gv[U][8];
-    frag_t wa[U], wb[U];
+  bool staged = false;
+  if constexpr (sizeof(T) == 2) staged = !gather && d <= kConvMaxStagedD;
+  if (staged) {
+    if constexpr (sizeof(T) == 2) {
+      // wave w takes the 64-k slabs w, w + NW, ...; two slots per wave, the next slab's loads
+      // in flight while one is consumed (each wave reads only its own slots: no barrier)
+      constexpr int LPS = 8;   // 4 row loads + 4 generator loads per slab
+      float inv = 1.f;         // (PRE) this lane's row scale
+      T* const gsh = conv_gains<T>();
+      const int nsl = d / 64, ntw = wave < nsl ? (nsl - 1 - wave) / NW + 1 : 0;
+      char* const sl0 = conv_ring<0>() + wave * kConvSlabBytes;
+      char* const sl1 = conv_ring<1>() + wave * kConvSlabBytes;
+      const uint32_t gbytes = static_cast<uint32_t>(static_cast<size_t>(2 * ng) * d * sizeof(T));
+      const __amdgpu_buffer_rsrc_t rgen = make_rsrc(gen, gbytes);
+      auto issue = [&](int v, int t) {
+        const int k0 = 64 * (wave + NW * (t < ntw ? t : ntw - 1));
+        char* b = v ? sl1 : sl0;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int ks = s0 + u * NW;
-      const bool ok = ks < nks;
-      const int k = ok ? 32 * ks + 8 * g : 0;
-      const uint32_t koff = static_cast<uint32_t>(ks * 32 * sizeof(T));
-      if (gather) load8f<T>(erow + k, av[u]);
-      else load8f<float>(arow + k, av[u]);
-      if constexpr (PRE) load8f<T>(gain + k, gv[u]);
-      wa[u] = F::load_buf(rg, ok ? oa + koff : past, 0);
-      wb[u] = F::load_buf(rg, ok ? ob + koff : past, 0);
-    }
-    if (PRE && s0 == wave) __syncthreads();   // the row scales are in LDS
+        for (int j = 0; j < 4; ++j) {
+          const int row = 4 * j + (lane >> 4), c = (lane & 15) ^ row;
+          conv_dma(row_ptr_f(row) + k0 + 4 * c, b + j * 1024);
+        }
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const bool ok = s0 + u * NW < nks;
-      if constexpr (PRE) {
-        const float inv = inv_s[r16];
+        for (int j = 0; j < 4; ++j) {
+          const int row = 8 * j + (lane >> 3), c = (lane & 7) ^ ((row >> 1) & 7);
+          const int grow = row < 16 ? g0 + row : ng + g0 + row - 16;
+          const uint32_t off = grow < 2 * ng ? static_cast<uint32_t>((static_cast<size_t>(grow) * d + k0 + 8 * c) * sizeof(T))
+                                             : gbytes;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(rgen, (__attribute__((address_space(3))) void*)(b + 4096 + j * 1024),
+                                                   16, off, 0, 0, 0);
+        }
+
+      };
+      auto step = [&](int v, int t) {
+        __builtin_amdgcn_s_waitcnt((LPS & 15) | ((LPS >> 4) << 14) | (7 << 4));   // slab t is in
+        const char* b = v ? sl1 : sl0;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) av[u][e] = av[u][e] * inv * gv[u][e];
+        for (int q = 0; q < 2; ++q) {
+          const int c0 = 8 * q + 2 * g;
+          const f32x4_t x0 = *reinterpret_cast<const f32x4_t*>(b + r16 * 256 + ((c0 ^ r16) << 4));
+          const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(b + r16 * 256 + (((c0 + 1) ^ r16) << 4));
+          float av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+          if constexpr (PRE) {
+            const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(gsh + 512 * wave + 64 * t + 32 * q + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              av[2 * e] = av[2 * e] * inv * __uint_as_float(gw[e] << 16);
+              av[2 * e + 1] = av[2 * e + 1] * inv * __uint_as_float(gw[e] & 0xffff0000u);
+            }
+          }
+          const frag_t a = F::from_floats(av);
+          const int pw = ((4 * q + g) ^ ((r16 >> 1) & 7)) << 4;
+          const frag_t wa = *reinterpret_cast<const frag_t*>(b + 4096 + r16 * 128 + pw);
+          const frag_t wb = *reinterpret_cast<const frag_t*>(b + 4096 + (16 + r16) * 128 + pw);
+          acc_a = F::mma(acc_a, a, wa);
+          acc_b = F::mma(acc_b, a, wb);
+        }
+        // this slot's reads must have completed before its next slab's direct loads can land
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        issue(v, t + 2);
+      };
+      if constexpr (PRE) {   // lane l: the gains of the wave's slab l / 8 (clamped), chunk l % 8
+        const int t = (lane >> 3) < ntw ? lane >> 3 : (ntw > 0 ? ntw - 1 : 0);
+        conv_dma(gain + (64 * (wave + NW * t)) % d + 8 * (lane & 7), gsh + 512 * wave);
       }
-      const frag_t a = ok ? F::from_floats(av[u]) : F::zero();
-      acc_a = F::mma(acc_a, a, wa[u]);
-      acc_b = F::mma(acc_b, a, wb[u]);
+      if (ntw > 0) {
+        issue(0, 0);
+        issue(1, 1);
+      }
+      if constexpr (PRE) {   // the row scales are in LDS (a barrier without a memory fence)
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_barrier();
+        inv = inv_s[r16];
+      }
+      int t = 0;
+      for (; t + 2 <= ntw; t += 2) {
+        step(0, t);
+        step(1, t + 1);
+      }
+      if (t < ntw) step(0, t);
+      __builtin_amdgcn_s_waitcnt(0);   // the re-reads past the wave's last slab
     }
+  } else {
+    // wave w takes k-steps w, w + NW, w + 2 NW, ...: U of them per stage, all of a stage's
+    // loads issued together (A as raw fp32 rows, scaled and rounded once the row scales are in)
+    for (int s0 = wave; s0 < nks; s0 += NW * U) {
+      float av[U][8], gv[U][8];
+      frag_t wa[U], wb[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int ks = s0 + u * NW;
+        const bool ok = ks < nks;
+        const int k = ok ? 32 * ks + 8 * g : 0;
+        const uint32_t koff = static_cast<uint32_t>(ks * 32 * sizeof(T));
+        if (gather) load8f<T>(erow + k, av[u]);
+        else load8f<float>(arow + k, av[u]);
+        if constexpr (PRE) load8f<T>(gain + k, gv[u]);
+        wa[u] = F::load_buf(rg, ok ? oa + koff : past, 0);
+        wb[u] = F::load_buf(rg, ok ? ob + koff : past, 0);
+      }
+      if (PRE && s0 == wave) __syncthreads();   // the row scales are in LDS
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const bool ok = s0 + u * NW < nks;
+        if constexpr (PRE) {
+          const float inv = inv_s[r16];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) av[u][e] = av[u][e] * inv * gv[u][e];
+        }
+        const frag_t a = ok ? F::from_floats(av[u]) : F::zero();
+        acc_a = F::mma(acc_a, a, wa[u]);
+        acc_b = F::mma(acc_b, a, wb[u]);
+      }
+    }
+    if (PRE && wave >= nks) __syncthreads();    // waves without k-steps meet the row-scale barrier too
   }
-  if (PRE && wave >= nks) __syncthreads();    // waves without k-steps meet the row-scale barrier too
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     red[wave][0][lane * 4 + i] = acc_a[i];
