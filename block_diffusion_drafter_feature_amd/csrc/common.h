@@ -25,6 +25,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x16_t __attribute__((ext_vector_type(16)));
 
 // ------------------------------------------------------------------ conversions
 
@@ -57,6 +58,19 @@ template <typename T> __device__ __forceinline__ float round_to(float v) { retur
 // Word 3 = 0x00020000 is the gfx9-family raw (untyped, unswizzled) buffer format.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, static_cast<int>(bytes), 0x00020000);
+}
+
+// ------------------------------------------------------------------ direct global -> LDS loads
+
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// 16 bytes per lane from global address g into LDS at (wave-uniform) byte address lds + 16 * lane.
+// Issued as an instruction the compiler does not track: it adds no waits of its own for these
+// loads, so the caller waits (vmcnt) before reading what they wrote.
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
 }
 
 // ------------------------------------------------------------------ fragments

@@ -53,31 +53,21 @@ __device__ __forceinline__ void load8f(const T* p, float (&v)[8]) {
   }
 }
 
-// Per-wave LDS staging of the corrections' operands (bf16 weights, rows not gathered, d <=
-// 4096): slot I of wave w holds one 64-k slab -- the 16 fp32 rows (4 KB, chunk c of row r at
-// position c ^ (r & 15)) and the tile's 32 generator rows (4 KB, chunk c of row r at
-// c ^ ((r >> 1) & 7)) -- and (PRE) one 1 KB block holds the RMSNorm gains of all of the wave's
-// slabs; all are filled by direct loads.  Fragment-shaped loads straight into
+// Per-wave LDS staging of the corrections' operands (bf16 weights, rows not gathered): slot I
+// of wave w holds one 64-k slab -- the 16 fp32 rows (4 KB, chunk c of row r at position
+// c ^ (r & 15)) and the tile's 32 generator rows (4 KB, chunk c of row r at c ^ ((r >> 1) & 7)),
+// both filled by direct loads (dma16) that the wave waits for itself.  (PRE: the slab's
+// RMSNorm gains, the same for every lane group's rows, come through scalar loads.)  Fragment-shaped loads straight into
 // registers (16 rows x 64 B per instruction) stream these operands at well under half the
 // rate (~33 against ~74 GB/s per work-group).
 constexpr int kConvSlabBytes = 8192;
-constexpr int kConvMaxStagedD = 4096;   // at most 8 slabs per wave (one 1 KB block of gains)
 template <int I>
 __device__ __forceinline__ char* conv_ring() {
   __shared__ __attribute__((aligned(16))) char s[kConvWaves * kConvSlabBytes];
   return s;
 }
 
-template <typename T>
-__device__ __forceinline__ T* conv_gains() {   // [wave][slab][64]
-  __shared__ __attribute__((aligned(16))) T s[kConvWaves * 512];
-  return s;
-}
 
-__device__ __forceinline__ void conv_dma(const void* g, void* lds) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
-}
 
 template <typename T, bool PRE>
 __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
@@ -97,7 +87,8 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
   __shared__ float inv_s[16];
   __shared__ float ssp[2][4][8];        // POST: [row half][wave][row] partial sums of squares
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
   const int ng = d >> 4, g0 = blockIdx.x * 16;
   const size_t m0 = static_cast<size_t>(blockIdx.y) * 16;
@@ -163,41 +154,44 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
   f32x4_t acc_a{0.f, 0.f, 0.f, 0.f}, acc_b{0.f, 0.f, 0.f, 0.f};
   const int nks = d / 32;
   bool staged = false;
-  if constexpr (sizeof(T) == 2) staged = !gather && d <= kConvMaxStagedD;
+  if constexpr (sizeof(T) == 2) staged = !gather;
   if (staged) {
     if constexpr (sizeof(T) == 2) {
       // wave w takes the 64-k slabs w, w + NW, ...; two slots per wave, the next slab's loads
       // in flight while one is consumed (each wave reads only its own slots: no barrier)
       constexpr int LPS = 8;   // 4 row loads + 4 generator loads per slab
       float inv = 1.f;         // (PRE) this lane's row scale
-      T* const gsh = conv_gains<T>();
       const int nsl = d / 64, ntw = wave < nsl ? (nsl - 1 - wave) / NW + 1 : 0;
       char* const sl0 = conv_ring<0>() + wave * kConvSlabBytes;
       char* const sl1 = conv_ring<1>() + wave * kConvSlabBytes;
-      const uint32_t gbytes = static_cast<uint32_t>(static_cast<size_t>(2 * ng) * d * sizeof(T));
-      const __amdgpu_buffer_rsrc_t rgen = make_rsrc(gen, gbytes);
       auto issue = [&](int v, int t) {
         const int k0 = 64 * (wave + NW * (t < ntw ? t : ntw - 1));
-        char* b = v ? sl1 : sl0;
+        const uint32_t b = lds_addr(v ? sl1 : sl0);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int row = 4 * j + (lane >> 4), c = (lane & 15) ^ row;
-          conv_dma(row_ptr_f(row) + k0 + 4 * c, b + j * 1024);
+          dma16(row_ptr_f(row) + k0 + 4 * c, b + j * 1024);
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
+        for (int j = 0; j < 4; ++j) {   // rows past the 2 ng generator rows (unused groups) read row 0
           const int row = 8 * j + (lane >> 3), c = (lane & 7) ^ ((row >> 1) & 7);
           const int grow = row < 16 ? g0 + row : ng + g0 + row - 16;
-          const uint32_t off = grow < 2 * ng ? static_cast<uint32_t>((static_cast<size_t>(grow) * d + k0 + 8 * c) * sizeof(T))
-                                             : gbytes;
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(rgen, (__attribute__((address_space(3))) void*)(b + 4096 + j * 1024),
-                                                   16, off, 0, 0, 0);
+          dma16(gen + static_cast<size_t>(grow < 2 * ng ? grow : 0) * d + k0 + 8 * c, b + 4096 + j * 1024);
         }
 
       };
       auto step = [&](int v, int t) {
         __builtin_amdgcn_s_waitcnt((LPS & 15) | ((LPS >> 4) << 14) | (7 << 4));   // slab t is in
+        asm volatile("" ::: "memory");
         const char* b = v ? sl1 : sl0;
+        u32x16_t gs[2];   // (PRE) the slab's 64 gains: k-step q's 32 in gs[q], wave-uniform
+        if constexpr (PRE) {
+          // (read-only weights, wave-uniform address: the constant address space gives scalar loads)
+          typedef const __attribute__((address_space(4))) u32x16_t cu32x16;
+          const cu32x16* gp = (const cu32x16*)(gain + 64 * (wave + NW * t));
+          gs[0] = gp[0];
+          gs[1] = gp[1];
+        }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int c0 = 8 * q + 2 * g;
@@ -205,11 +199,12 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
           const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(b + r16 * 256 + (((c0 + 1) ^ r16) << 4));
           float av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           if constexpr (PRE) {
-            const u32x4_t gw = *reinterpret_cast<const u32x4_t*>(gsh + 512 * wave + 64 * t + 32 * q + 8 * g);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              av[2 * e] = av[2 * e] * inv * __uint_as_float(gw[e] << 16);
-              av[2 * e + 1] = av[2 * e + 1] * inv * __uint_as_float(gw[e] & 0xffff0000u);
+              const uint32_t ge = gs[q][e], g1 = gs[q][4 + e], g2 = gs[q][8 + e], g3 = gs[q][12 + e];
+              const uint32_t gw = g == 0 ? ge : g == 1 ? g1 : g == 2 ? g2 : g3;
+              av[2 * e] = av[2 * e] * inv * __uint_as_float(gw << 16);
+              av[2 * e + 1] = av[2 * e + 1] * inv * __uint_as_float(gw & 0xffff0000u);
             }
           }
           const frag_t a = F::from_floats(av);
@@ -223,10 +218,6 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
         __builtin_amdgcn_s_waitcnt(0xc07f);
         issue(v, t + 2);
       };
-      if constexpr (PRE) {   // lane l: the gains of the wave's slab l / 8 (clamped), chunk l % 8
-        const int t = (lane >> 3) < ntw ? lane >> 3 : (ntw > 0 ? ntw - 1 : 0);
-        conv_dma(gain + (64 * (wave + NW * t)) % d + 8 * (lane & 7), gsh + 512 * wave);
-      }
       if (ntw > 0) {
         issue(0, 0);
         issue(1, 1);
@@ -236,13 +227,22 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
         __builtin_amdgcn_s_barrier();
         inv = inv_s[r16];
       }
-      int t = 0;
-      for (; t + 2 <= ntw; t += 2) {
-        step(0, t);
-        step(1, t + 1);
+      if (ntw == 8) {   // d = 4096: straight-line code keeps the compiler's wait counting exact
+#pragma unroll
+        for (int t = 0; t < 8; t += 2) {
+          step(0, t);
+          step(1, t + 1);
+        }
+      } else {
+        int t = 0;
+        for (; t + 2 <= ntw; t += 2) {
+          step(0, t);
+          step(1, t + 1);
+        }
+        if (t < ntw) step(0, t);
       }
-      if (t < ntw) step(0, t);
       __builtin_amdgcn_s_waitcnt(0);   // the re-reads past the wave's last slab
+      asm volatile("" ::: "memory");
     }
   } else {
     // wave w takes k-steps w, w + NW, w + 2 NW, ...: U of them per stage, all of a stage's

@@ -681,14 +681,6 @@ __device__ __forceinline__ T* pipe_slot() {
   return s;
 }
 
-__device__ __forceinline__ uint32_t lds_addr(const void* p) {
-  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
-}
-
-// 16 bytes per lane from global address g into LDS at (wave-uniform) byte address lds + 16 * lane
-__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
-}
 
 template <typename T, int BM, int BN, int NS, class Epi, bool W8, int NWV>
 __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict__ A, int lda,
