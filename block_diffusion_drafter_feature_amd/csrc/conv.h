@@ -56,11 +56,17 @@ __device__ __forceinline__ void load8f(const T* p, float (&v)[8]) {
 // Per-wave LDS staging of the corrections' operands (bf16 weights, rows not gathered): slot I
 // of wave w holds one 64-k slab -- the 16 fp32 rows (4 KB, chunk c of row r at position
 // c ^ (r & 15)) and the tile's 32 generator rows (4 KB, chunk c of row r at c ^ ((r >> 1) & 7)),
-// both filled by direct loads (dma16) that the wave waits for itself.  (PRE: the slab's
-// RMSNorm gains, the same for every lane group's rows, come through scalar loads.)  Fragment-shaped loads straight into
+// both filled by direct loads (dma16) that the wave waits for itself, and (PRE) the slab's 64
+// RMSNorm gains (128 B, loaded twice by a 4-byte-per-lane direct load).  Fragment-shaped loads straight into
 // registers (16 rows x 64 B per instruction) stream these operands at well under half the
 // rate (~33 against ~74 GB/s per work-group).
-constexpr int kConvSlabBytes = 8192;
+constexpr int kConvSlabBytes = 8192 + 256;
+
+// 4 bytes per lane from global address g into LDS at (wave-uniform) byte address lds + 4 * lane
+// (untracked by the compiler, as dma16)
+__device__ __forceinline__ void dma4(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(g), "s"(lds) : "memory", "m0");
+}
 template <int I>
 __device__ __forceinline__ char* conv_ring() {
   __shared__ __attribute__((aligned(16))) char s[kConvWaves * kConvSlabBytes];
@@ -159,9 +165,10 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
     if constexpr (sizeof(T) == 2) {
       // wave w takes the 64-k slabs w, w + NW, ...; two slots per wave, the next slab's loads
       // in flight while one is consumed (each wave reads only its own slots: no barrier)
-      constexpr int LPS = 8;   // 4 row loads + 4 generator loads per slab
-      float inv = 1.f;         // (PRE) this lane's row scale
+      constexpr int LPS = PRE ? 9 : 8;   // 4 row loads + 4 generator loads (+ the gains) per slab
       const int nsl = d / 64, ntw = wave < nsl ? (nsl - 1 - wave) / NW + 1 : 0;
+      float inv = 1.f;         // (PRE) this lane's row scale
+
       char* const sl0 = conv_ring<0>() + wave * kConvSlabBytes;
       char* const sl1 = conv_ring<1>() + wave * kConvSlabBytes;
       auto issue = [&](int v, int t) {
@@ -178,20 +185,14 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
           const int grow = row < 16 ? g0 + row : ng + g0 + row - 16;
           dma16(gen + static_cast<size_t>(grow < 2 * ng ? grow : 0) * d + k0 + 8 * c, b + 4096 + j * 1024);
         }
+        if constexpr (PRE) dma4(gain + k0 + 2 * (lane & 31), b + 8192);
+
 
       };
       auto step = [&](int v, int t) {
         __builtin_amdgcn_s_waitcnt((LPS & 15) | ((LPS >> 4) << 14) | (7 << 4));   // slab t is in
         asm volatile("" ::: "memory");
         const char* b = v ? sl1 : sl0;
-        u32x16_t gs[2];   // (PRE) the slab's 64 gains: k-step q's 32 in gs[q], wave-uniform
-        if constexpr (PRE) {
-          // (read-only weights, wave-uniform address: the constant address space gives scalar loads)
-          typedef const __attribute__((address_space(4))) u32x16_t cu32x16;
-          const cu32x16* gp = (const cu32x16*)(gain + 64 * (wave + NW * t));
-          gs[0] = gp[0];
-          gs[1] = gp[1];
-        }
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
           const int c0 = 8 * q + 2 * g;
@@ -199,10 +200,10 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
           const f32x4_t x1 = *reinterpret_cast<const f32x4_t*>(b + r16 * 256 + (((c0 + 1) ^ r16) << 4));
           float av[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
           if constexpr (PRE) {
+            const u32x4_t gv4 = *reinterpret_cast<const u32x4_t*>(b + 8192 + (32 * q + 8 * g) * sizeof(T));
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              const uint32_t ge = gs[q][e], g1 = gs[q][4 + e], g2 = gs[q][8 + e], g3 = gs[q][12 + e];
-              const uint32_t gw = g == 0 ? ge : g == 1 ? g1 : g == 2 ? g2 : g3;
+              const uint32_t gw = gv4[e];
               av[2 * e] = av[2 * e] * inv * __uint_as_float(gw << 16);
               av[2 * e + 1] = av[2 * e + 1] * inv * __uint_as_float(gw & 0xffff0000u);
             }
