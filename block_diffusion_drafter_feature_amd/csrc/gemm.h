@@ -879,7 +879,8 @@ static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks,
                                    hipStream_t s);
 
 // Split-K reduction: sum the partial tiles in z order into an LDS block of 16 rows x 64
-// columns (each wave reads one 256-byte row segment of every partial), then the epilogue.
+// columns (each thread four consecutive columns of one row: a wave reads four 256-byte row
+// segments of every partial with 16-byte loads), then the epilogue.
 // grid (ldp / 64, ceil(M / 16)), 256 threads.
 template <class Epi>
 __global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* __restrict__ partial, int M,
@@ -887,22 +888,22 @@ __global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* 
   __shared__ float Ct[16 * 65];
   __shared__ typename Epi::Row rinfo[16];
   const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 16;
-  const int r = threadIdx.x >> 6, cc = threadIdx.x & 63;
+  const int r = threadIdx.x >> 4, cc = (threadIdx.x & 15) * 4;
   const size_t zs = static_cast<size_t>(M) * ldp;
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int m = m0 + 4 * k + r;
-    float v = 0.f;
+  {
+    const int m = m0 + r;
+    f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
     if (m < M) {
       const float* p = partial + static_cast<size_t>(m) * ldp + c0 + cc;
-      float part[8];
+      f32x4_t part[8];
 #pragma unroll
-      for (int z = 0; z < 8; ++z) part[z] = z < ks ? p[z * zs] : 0.f;
+      for (int z = 0; z < 8; ++z) part[z] = z < ks ? *reinterpret_cast<const f32x4_t*>(p + z * zs) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int z = 0; z < 8; ++z) v += part[z];
-      for (int z = 8; z < ks; ++z) v += p[z * zs];
+      for (int z = 8; z < ks; ++z) v += *reinterpret_cast<const f32x4_t*>(p + z * zs);
     }
-    Ct[(4 * k + r) * 65 + cc] = v;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Ct[r * 65 + cc + e] = v[e];
   }
   __syncthreads();
   const int vt0 = c0 / 16, nvt = min(4, n_vtiles - vt0);
