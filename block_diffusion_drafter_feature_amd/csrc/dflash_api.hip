@@ -21,6 +21,7 @@ namespace {
 
 constexpr size_t kAlign = 256;
 constexpr int kTopkChunk = kTopkWaveChunk;   // vocabulary columns per top-k wave
+constexpr int kTopkTilesNG = 20;              // 128-column groups per lane in topk_tiles_kernel
 constexpr int kArgmaxChunk = 8192;   // vocabulary columns per argmax work-group
 constexpr int kTopkFinalLists = 256;  // lists topk_final_kernel merges per row (64 lanes x 4)
 
@@ -166,6 +167,7 @@ struct DraftWs {
   T* o;           // [M][H*hd]
   T* h;           // [M][d_ffn]
   float* logits;  // [M][V] (when the caller passes none)
+  float* tmax;    // [M][V/128 rounded up] row maxima of the logits per 128-column group
   float* tk_v;    // [M][n_chunks][16]
   int32_t* tk_i;
   float* scratch;
@@ -192,6 +194,7 @@ DraftWs<T> carve_draft(Carver& cv, const dflash_config* c, int B, int cap) {
   w.o = cv.take<T>(M * hq);
   w.h = cv.take<T>(M * c->d_ffn);
   w.logits = cv.take<float>(M * c->vocab);
+  w.tmax = cv.take<float>(M * ((c->vocab + 127) / 128));
   // top-16 partial lists: one per vocabulary chunk, or one per LM-head work-group when
   // the first stage runs in the streaming LM head (at most kTopkFinalLists)
   const size_t ntk = std::max<size_t>(nch, kTopkFinalLists);
@@ -516,19 +519,29 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
     groups = run_lm_head_top16<T>(W.ut, d, M, d, V / 16, et, kTopkFinalLists, s, fp8w(c));
     if (groups < 0) return DFLASH_E_HIP;
   }
+  // several drafted blocks through the unsplit pipelined LM head: it also leaves each row's
+  // maximum per 128-column group, and the top-16 stage reads only the groups that can hold an
+  // entry
+  const bool by_tiles = groups == 0 && std::is_same<T, bf16_t>::value && (V + 127) / 128 <= 64 * kTopkTilesNG &&
+                        pipe_unsplit(M, d, V / 16);
   if (groups == 0) {
-    EpiLogits<T> el{{seg1<T>(w->lm_head, V, wstride(c, d)), lg, V, STORE}};
+    EpiLogits<T> el{{seg1<T>(w->lm_head, V, wstride(c, d)), lg, V, STORE}, by_tiles ? W.tmax : nullptr};
     GEMM_CHECK((run_gemm<T, T>(W.ut, d, nullptr, M, d, V / 16, el, s, W.scratch, W.scratch_bytes, 0, fp8w(c))));
   }
   P0.end(DFLASH_PROBE_LM_HEAD);
   P0.begin(DFLASH_PROBE_TOPK);
-  if (groups == 0) {
-    groups = (V + kTopkChunk - 1) / kTopkChunk;
-    topk_partial_kernel<<<dim3(groups, M), 64, 0, s>>>(lg, V, V, W.tk_v, W.tk_i);
+  if (by_tiles) {
+    topk_tiles_kernel<kTopkTilesNG><<<M, 64, 0, s>>>(lg, V, W.tmax, cand_ids, cand_logits);
+    LAUNCH_CHECK();
+  } else {
+    if (groups == 0) {
+      groups = (V + kTopkChunk - 1) / kTopkChunk;
+      topk_partial_kernel<<<dim3(groups, M), 64, 0, s>>>(lg, V, V, W.tk_v, W.tk_i);
+      LAUNCH_CHECK();
+    }
+    topk_final_kernel<<<M, 64, 0, s>>>(W.tk_v, W.tk_i, groups, cand_ids, cand_logits);
     LAUNCH_CHECK();
   }
-  topk_final_kernel<<<M, 64, 0, s>>>(W.tk_v, W.tk_i, groups, cand_ids, cand_logits);
-  LAUNCH_CHECK();
   P0.end(DFLASH_PROBE_TOPK);
   return DFLASH_OK;
 }

@@ -83,9 +83,21 @@ struct EpiStore {
 };
 
 // LM-head logits: a plain fp32 store, kept as its own type so that the LM-head GEMM is a
-// kernel of its own in profiles.
+// kernel of its own in profiles.  With tmax != nullptr the pipelined kernel (unsplit, 128-
+// column tiles) also writes each row's maximum over every 128-column group of the logits,
+// tmax[m][n / 128] (columns past the vocabulary excluded).
 template <typename T>
-struct EpiLogits : EpiStore<T> {};
+struct EpiLogits : EpiStore<T> {
+  float* tmax;
+};
+template <class Epi>
+struct HasTileMax {
+  static constexpr bool value = false;
+};
+template <typename T>
+struct HasTileMax<EpiLogits<T>> {
+  static constexpr bool value = true;
+};
 
 // LM head of one drafted block with the first top-16 stage folded in (streaming kernel
 // only): every work-group keeps the running top 16 of its columns for each row (value

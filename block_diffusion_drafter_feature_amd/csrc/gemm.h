@@ -849,6 +849,25 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
     __syncthreads();
     __shared__ typename Epi::Row rinfo[EPR];
     epilogue_tile(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rinfo);
+    if constexpr (HasTileMax<Epi>::value && BN == 128) {
+      // each row's maximum over the tile's 128 columns (past the vocabulary: excluded);
+      // 64 * NWV / EPR threads per row, fixed shuffle tree
+      constexpr int TPR = 64 * NWV / EPR, CPT = BN / TPR;
+      static_assert(TPR <= 64 && (TPR & (TPR - 1)) == 0 && CPT * TPR == BN, "row max layout");
+      if (epi.tmax) {
+        const int r = tid / TPR, q = tid % TPR, ncol = epi.w.off[epi.w.n_seg];
+        float mx = -INFINITY;
+#pragma unroll
+        for (int k = 0; k < CPT; ++k) {
+          const int col = q * CPT + k;
+          if (vt0 * 16 + col < ncol) mx = fmaxf(mx, Ct[r * (BN + 1) + col]);
+        }
+#pragma unroll
+        for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        const int m = m0 + h * EPR + r;
+        if (q == 0 && m < M) epi.tmax[static_cast<size_t>(m) * ((ncol + 127) / 128) + vt0 / 8] = mx;
+      }
+    }
     __syncthreads();
   }
 }
@@ -962,6 +981,12 @@ inline BigPlan big_plan(int M, int K, int n_vtiles) {
   const long t256 = static_cast<long>((M + 255) / 256) * ((N + 127) / 128);
   if (M >= 256) return {256, 128, 3, t256 < 128 ? split(t256, 256, 16, 8) : 1};
   return {128, 128, 2, t128 >= 256 ? 1 : split(t128, 512, 16)};
+}
+
+// True when run_gemm takes the pipelined kernel without split-K at this shape (bf16 weights):
+// its epilogue then sees whole 128-column tiles (EpiLogits row maxima).
+inline bool pipe_unsplit(int M, int K, int n_vtiles) {
+  return M > 16 && K % 64 == 0 && big_plan(M, K, n_vtiles).ks == 1;
 }
 
 template <typename T>

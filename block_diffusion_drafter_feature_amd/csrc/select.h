@@ -215,6 +215,95 @@ __global__ __launch_bounds__(64) void topk_partial_kernel(const float* __restric
 // Stage 2: merge the per-chunk lists of each row.  grid (rows), one wave; lane l takes
 // lists l, l + 64, ... (at most 4 per lane), each read as four 16-byte loads.  Whole lists
 // per lane keep the lane maxima high, so few candidates survive the threshold.
+// Top 16 of each row of the logits (value descending, then column ascending) from the row's
+// maxima over 128-column groups (tmax, written by the LM head): the 16th largest group
+// maximum tau bounds the 16th largest logit from below (16 distinct columns reach it), so a
+// column of a group whose maximum is below tau cannot be among the top 16.  The groups whose
+// maximum is >= tau (typically 16) are scanned 16 at a time, each round's 2048 columns ranked
+// together with the best 16 so far by the same comparator as the two-pass route, so the
+// result is the same.  One wave per row; at most 64 * NG groups.
+template <int NG>
+__global__ __launch_bounds__(64) void topk_tiles_kernel(const float* __restrict__ logits, int V,
+                                                        const float* __restrict__ tmax,
+                                                        int32_t* __restrict__ out_ids,
+                                                        float* __restrict__ out_vals) {
+  __shared__ float sv[256];
+  __shared__ int si[256];
+  __shared__ float ov[16];
+  __shared__ int oi[16];
+  __shared__ int gl[64 * NG];
+  const int m = blockIdx.x, lane = threadIdx.x;
+  const int ng = (V + 127) / 128;
+  const float* tm = tmax + static_cast<size_t>(m) * ng;
+  const float* row = logits + static_cast<size_t>(m) * V;
+  float v[NG];
+  int id[NG];
+#pragma unroll
+  for (int j = 0; j < NG; ++j) {
+    const int g = lane + 64 * j;
+    v[j] = g < ng ? tm[g] : -INFINITY;
+    id[j] = g;
+  }
+  wave_select16<NG, 256>(v, id, sv, si, ov, oi);
+  const float tau = ov[15];
+  // the candidate groups, in increasing group order
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < NG; ++j) cnt += (lane + 64 * j < ng && v[j] >= tau) ? 1 : 0;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += t;
+  }
+  const int total = __shfl(incl, 63, 64);
+  {
+    int pos = incl - cnt;
+#pragma unroll
+    for (int j = 0; j < NG; ++j)
+      if (lane + 64 * j < ng && v[j] >= tau) gl[pos++] = lane + 64 * j;
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  float bv = -INFINITY;   // lanes 0..15: the best 16 so far
+  int bi = INT_MAX;
+  const bool vec = (V & 3) == 0 && (reinterpret_cast<uintptr_t>(logits) & 15) == 0;
+  for (int r0 = 0; r0 < total; r0 += 16) {
+    // lane l: 32 consecutive columns of group gl[r0 + l / 4]
+    float x[33];
+    int xi[33];
+    const int gi = r0 + (lane >> 2);
+    const int col0 = (gi < total ? gl[gi] : 0) * 128 + (lane & 3) * 32;
+#pragma unroll
+    for (int k4 = 0; k4 < 8; ++k4) {
+      const int col = col0 + 4 * k4;
+      f32x4_t q = f32x4_t{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (gi < total) {
+        if (vec && col + 3 < V) {
+          q = *reinterpret_cast<const f32x4_t*>(row + col);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) q[e] = col + e < V ? row[col + e] : -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[4 * k4 + e] = q[e];
+        xi[4 * k4 + e] = gi < total && col + e < V ? col + e : INT_MAX;
+      }
+    }
+    x[32] = bv;
+    xi[32] = bi;
+    wave_select16<33, 256>(x, xi, sv, si, ov, oi);
+    bv = lane < 16 ? ov[lane] : -INFINITY;
+    bi = lane < 16 ? oi[lane] : INT_MAX;
+  }
+  if (lane < 16) {
+    out_ids[static_cast<size_t>(m) * 16 + lane] = bi;
+    out_vals[static_cast<size_t>(m) * 16 + lane] = bv;
+  }
+}
+
 __global__ __launch_bounds__(64) void topk_final_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
                                                         int n_chunks, int32_t* __restrict__ out_ids,
                                                         float* __restrict__ out_vals) {
