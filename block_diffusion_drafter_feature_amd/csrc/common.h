@@ -178,8 +178,8 @@ inline RopeFreq rope_freq(double theta, int hd) {
 // rad there), then evaluated in float.
 __device__ __forceinline__ void rope_cs(int pos, double inv, float* c, float* s) {
   double a = static_cast<double>(pos) * inv;
-  const double two_pi = 6.283185307179586476925286766559;
-  a -= two_pi * rint(a / two_pi);
+  const double two_pi = 6.283185307179586476925286766559, inv_two_pi = 0.15915494309189533576888376337251;
+  a -= two_pi * rint(a * inv_two_pi);
   sincosf(static_cast<float>(a), s, c);
 }
 

@@ -12,9 +12,13 @@
 //                     epilogues need no staging tile)
 //   kTop16            the streaming LM head keeps per-work-group top-16 lists (EpiLogitsTop16)
 //   apply(vt, m, row, c, v, partner)
+//   Col, col(vt)      optional: per-tile facts (destination, kind) worked out once per virtual
+//                     tile; the staged epilogues then call apply(col, m, row, c, v, partner)
 #pragma once
 
 #include "common.h"
+
+#include <type_traits>
 
 namespace dflash {
 
@@ -90,6 +94,20 @@ template <typename T>
 struct EpiLogits : EpiStore<T> {
   float* tmax;
 };
+template <class Epi, class = void>
+struct HasCol : std::false_type {};
+template <class Epi>
+struct HasCol<Epi, std::void_t<typename Epi::Col>> : std::true_type {};
+// Epi::Col, or an empty stand-in for epilogues without per-tile facts
+template <class Epi, bool = HasCol<Epi>::value>
+struct ColOf {
+  struct type {};
+};
+template <class Epi>
+struct ColOf<Epi, true> {
+  typedef typename Epi::Col type;
+};
+
 template <class Epi>
 struct HasTileMax {
   static constexpr bool value = false;
@@ -149,25 +167,55 @@ struct EpiQKV {
   };
   __device__ __forceinline__ Row row(int m) const { return Row{ctx_len[m >> 4] + (m & 15)}; }
   __device__ __forceinline__ bool colmajor(int vt) const { return vt >= (H + Hkv) * hd / 16; }
-  __device__ __forceinline__ void apply(int vt, int m, const Row& rw, int c, float v, float pv) const {
+  // destination of tile vt: kind 0 query, 1 key (both rotated, base at the head; inv = the
+  // inverse frequencies of its 8 dimension pairs), 2 value (base at the tile's first
+  // dimension), -1 none
+  struct Col {
+    double inv[8];
+    T* p;
+    int kind, tt;
+  };
+  __device__ __forceinline__ Col col(int vt) const {
     const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
+    Col cf{};
+    cf.kind = -1;
+    if (vt < tq) {
+      cf = Col{{}, q + (vt / tph) * hd, 0, vt % tph};
+    } else if (vt - tq < tk) {
+      cf = Col{{}, kb + ((vt - tq) / tph) * 16 * hd, 1, (vt - tq) % tph};
+    } else if (vt - tq - tk < tk) {
+      cf = Col{{}, vbt + (vt - tq - tk) * 16 * 16, 2, 0};   // value dims from (vt-tq-tk)*16 (no head straddles a tile)
+    }
+    if (cf.kind == 0 || cf.kind == 1)
+      for (int j = 0; j < 8; ++j) cf.inv[j] = rf.inv[8 * cf.tt + j];
+    return cf;
+  }
+  __device__ __forceinline__ void put(T* p, int kind, int tt, double inv, int m, const Row& rw, int c, float v,
+                                      float pv) const {
     const int b = m >> 4, j = m & 15;
-    if (vt < tq + tk) {
-      const bool isq = vt < tq;
-      const int t = isq ? vt : vt - tq;
-      const int head = t / tph, tt = t % tph;
+    if (kind < 0) return;
+    if (kind < 2) {
       const int dim = rope_dim(tt, c, hd);
       float cs, sn;
-      rope_cs(rw.pos, rf.inv[8 * tt + (c & 7)], &cs, &sn);
+      rope_cs(rw.pos, inv, &cs, &sn);
       const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
-      if (isq) q[(static_cast<size_t>(m) * H + head) * hd + dim] = from_f<T>(r);
-      else kb[((static_cast<size_t>(b) * Hkv + head) * 16 + j) * hd + dim] = from_f<T>(r);
+      if (kind == 0) p[static_cast<size_t>(m) * H * hd + dim] = from_f<T>(r);
+      else p[(static_cast<size_t>(b) * Hkv * 16 + j) * hd + dim] = from_f<T>(r);
     } else {
-      const int t = vt - tq - tk;
-      if (t >= tk) return;
-      const int n = t * 16 + c, head = n / hd, dim = n % hd;
-      vbt[((static_cast<size_t>(b) * Hkv + head) * hd + dim) * 16 + j] = from_f<T>(v);
+      p[static_cast<size_t>(b) * Hkv * hd * 16 + c * 16 + j] = from_f<T>(v);
     }
+  }
+  // cf: facts of the tile held in shared memory (read in place)
+  __device__ __forceinline__ void apply(const Col& cf, int m, const Row& rw, int c, float v, float pv) const {
+    const int kind = cf.kind;
+    put(cf.p, kind, cf.tt, kind == 0 || kind == 1 ? cf.inv[c & 7] : 0.0, m, rw, c, v, pv);
+  }
+  __device__ __forceinline__ void apply(int vt, int m, const Row& rw, int c, float v, float pv) const {
+    const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
+    if (vt < tq) put(q + (vt / tph) * hd, 0, vt % tph, rf.inv[8 * (vt % tph) + (c & 7)], m, rw, c, v, pv);
+    else if (vt - tq < tk)
+      put(kb + ((vt - tq) / tph) * 16 * hd, 1, (vt - tq) % tph, rf.inv[8 * ((vt - tq) % tph) + (c & 7)], m, rw, c, v, pv);
+    else if (vt - tq - tk < tk) put(vbt + (vt - tq - tk) * 16 * 16, 2, 0, 0.0, m, rw, c, v, pv);
   }
 };
 
@@ -224,21 +272,51 @@ struct EpiInject {
     return Row{lo, pos};
   }
   __device__ __forceinline__ bool colmajor(int vt) const { return vt % (2 * (Hkv * hd / 16)) >= Hkv * hd / 16; }
-  __device__ __forceinline__ void apply(int vt, int m, const Row& rw, int c, float v, float pv) const {
+  // destination of tile vt: kind 0 key (rotated; base at the head; inv = the inverse
+  // frequencies of its 8 dimension pairs), 1 value (base at the tile's first dimension), -1 none
+  struct Col {
+    double inv[8];
+    T* p;
+    int kind, tt;
+  };
+  __device__ __forceinline__ Col col(int vt) const {
     const int tk = Hkv * hd / 16, tph = hd / 16;
     const int l = vt / (2 * tk), t = vt % (2 * tk);
-    if (l >= L || rw.b < 0) return;
-    const int b = rw.b, pos = rw.pos;
+    Col cf{};
+    cf.kind = -1;
+    if (l >= L) return cf;
     if (t < tk) {
-      const int head = t / tph, tt = t % tph, dim = rope_dim(tt, c, hd);
-      float cs, sn;
-      rope_cs(pos, rf.inv[8 * tt + (c & 7)], &cs, &sn);
-      const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
-      kc[l][((static_cast<size_t>(b) * Hkv + head) * cap + pos) * hd + dim] = from_f<T>(r);
+      cf = Col{{}, kc[l] + static_cast<size_t>(t / tph) * cap * hd, 0, t % tph};
+      for (int j = 0; j < 8; ++j) cf.inv[j] = rf.inv[8 * cf.tt + j];
     } else {
-      const int n = (t - tk) * 16 + c, head = n / hd, dim = n % hd;
-      vtc[l][((static_cast<size_t>(b) * Hkv + head) * hd + dim) * cap + pos] = from_f<T>(v);
+      cf = Col{{}, vtc[l] + static_cast<size_t>(t - tk) * 16 * cap, 1, 0};   // value dims (t-tk)*16.. of the layer
     }
+    return cf;
+  }
+  __device__ __forceinline__ void put(T* p, int kind, int tt, double inv, const Row& rw, int c, float v,
+                                      float pv) const {
+    if (kind < 0 || rw.b < 0) return;
+    const size_t bo = static_cast<size_t>(rw.b) * Hkv * cap * hd;
+    if (kind == 0) {
+      float cs, sn;
+      rope_cs(rw.pos, inv, &cs, &sn);
+      const float r = (c < 8) ? v * cs - pv * sn : v * cs + pv * sn;
+      p[bo + static_cast<size_t>(rw.pos) * hd + rope_dim(tt, c, hd)] = from_f<T>(r);
+    } else {
+      p[bo + static_cast<size_t>(c) * cap + rw.pos] = from_f<T>(v);
+    }
+  }
+  // cf: facts of the tile held in shared memory (read in place)
+  __device__ __forceinline__ void apply(const Col& cf, int, const Row& rw, int c, float v, float pv) const {
+    const int kind = cf.kind;
+    put(cf.p, kind, cf.tt, kind == 0 ? cf.inv[c & 7] : 0.0, rw, c, v, pv);
+  }
+  __device__ __forceinline__ void apply(int vt, int, const Row& rw, int c, float v, float pv) const {
+    const int tk = Hkv * hd / 16, tph = hd / 16;
+    const int l = vt / (2 * tk), t = vt % (2 * tk);
+    if (l >= L) return;
+    if (t < tk) put(kc[l] + static_cast<size_t>(t / tph) * cap * hd, 0, t % tph, rf.inv[8 * (t % tph) + (c & 7)], rw, c, v, pv);
+    else put(vtc[l] + static_cast<size_t>(t - tk) * 16 * cap, 1, 0, 0.0, rw, c, v, pv);
   }
 };
 

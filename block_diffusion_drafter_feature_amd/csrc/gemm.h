@@ -41,23 +41,43 @@ __device__ __forceinline__ typename Frag<T>::type load_a(const AS* p) {
 // (r < rows) and the 16 columns of virtual tiles vt0 .. vt0 + nvt - 1.  The per-row facts
 // are worked out once per row; a tile whose stores run along m (Epi::colmajor) gives
 // consecutive rows to consecutive threads.  Called by every thread of the work-group;
-// rinfo holds >= rows entries.  Ends without a barrier (the caller syncs before reusing Ct).
-template <class Epi>
+// rinfo holds >= rows entries (ROWS_READY: already filled by the caller, and visible to every
+// thread); cols, when given, the per-tile facts of tiles vt0.. (Epi::Col).  Ends without a
+// barrier (the caller syncs before reusing Ct).
+template <class Epi, bool ROWS_READY = false>
 __device__ __forceinline__ void epilogue_tile(const Epi& epi, const float* Ct, int ldc, int m_base, int rows,
-                                              int vt0, int nvt, int M, typename Epi::Row* rinfo) {
+                                              int vt0, int nvt, int M, const typename Epi::Row* rinfo_in,
+                                              const typename ColOf<Epi>::type* cols = nullptr) {
   const int nth = blockDim.x, tid = threadIdx.x;
-  for (int r = tid; r < rows; r += nth) rinfo[r] = epi.row(m_base + r < M ? m_base + r : M - 1);
-  __syncthreads();
+  typename Epi::Row* rinfo = const_cast<typename Epi::Row*>(rinfo_in);
+  if constexpr (!ROWS_READY) {
+    for (int r = tid; r < rows; r += nth) rinfo[r] = epi.row(m_base + r < M ? m_base + r : M - 1);
+    __syncthreads();
+  }
   const int per = rows * 16;
   for (int v = 0; v < nvt; ++v) {
     const int vt = vt0 + v;
     const bool cm = epi.colmajor(vt);
-    for (int e = tid; e < per; e += nth) {
-      const int r = cm ? e % rows : e >> 4, c = cm ? e / rows : e & 15;
-      const int m = m_base + r;
-      if (m >= M) continue;
-      const float* row = Ct + r * ldc;
-      epi.apply(vt, m, rinfo[r], c, row[v * 16 + c], row[((v ^ Epi::PX) << 4) | (c ^ Epi::PC)]);
+    if constexpr (HasCol<Epi>::value) {
+      if (cols) {   // (passed by reference: read in place from shared memory)
+        for (int e = tid; e < per; e += nth) {
+          const int r = cm ? e % rows : e >> 4, c = cm ? e / rows : e & 15;
+          const int m = m_base + r;
+          if (m >= M) continue;
+          const float* row = Ct + r * ldc;
+          epi.apply(cols[v], m, rinfo[r], c, row[v * 16 + c], row[((v ^ Epi::PX) << 4) | (c ^ Epi::PC)]);
+        }
+        continue;
+      }
+    }
+    {
+      for (int e = tid; e < per; e += nth) {
+        const int r = cm ? e % rows : e >> 4, c = cm ? e / rows : e & 15;
+        const int m = m_base + r;
+        if (m >= M) continue;
+        const float* row = Ct + r * ldc;
+        epi.apply(vt, m, rinfo[r], c, row[v * 16 + c], row[((v ^ Epi::PX) << 4) | (c ^ Epi::PC)]);
+      }
     }
   }
 }
@@ -799,6 +819,19 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
   auto slot = [&](int i) { return i == 0 ? s0 : i == 1 ? s1 : i == 2 ? s2 : s3; };
 #pragma unroll
   for (int i = 0; i < NS - 1; ++i) issue(slot(i), kslab(i));
+  // the per-row facts of the epilogue, worked out once per tile while the first slabs load
+  // (their loads are dependent global reads for some epilogues)
+  // (and the per-tile facts: kernel-argument arrays indexed at run time are memory reads)
+  constexpr bool kRows = !std::is_empty<typename Epi::Row>::value;
+  __shared__ typename Epi::Row rows_all[kRows ? BM : 1];
+  __shared__ typename ColOf<Epi>::type cols_all[HasCol<Epi>::value ? BN / 16 : 1];
+  if constexpr (kRows) {
+    if (!partial)
+      for (int r = tid; r < BM; r += 64 * NWV) rows_all[r] = epi.row(m0 + r < M ? m0 + r : M - 1);
+  }
+  if constexpr (HasCol<Epi>::value) {
+    if (!partial && tid >= 64 * NWV - BN / 16) cols_all[tid - (64 * NWV - BN / 16)] = epi.col(vt0 + tid - (64 * NWV - BN / 16));
+  }
   for (int kt = 0; kt < KT; kt += NS) {
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
@@ -847,15 +880,22 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
       }
     }
     __syncthreads();
-    __shared__ typename Epi::Row rinfo[EPR];
-    epilogue_tile(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rinfo);
-    if constexpr (HasTileMax<Epi>::value && BN == 128) {
-      // each row's maximum over the tile's 128 columns (past the vocabulary: excluded);
-      // 64 * NWV / EPR threads per row, fixed shuffle tree
-      constexpr int TPR = 64 * NWV / EPR, CPT = BN / TPR;
-      static_assert(TPR <= 64 && (TPR & (TPR - 1)) == 0 && CPT * TPR == BN, "row max layout");
+    const typename ColOf<Epi>::type* cols = HasCol<Epi>::value ? cols_all : nullptr;
+    if constexpr (kRows) {
+      epilogue_tile<Epi, true>(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rows_all + h * EPR, cols);
+    } else {
+      __shared__ typename Epi::Row rinfo[EPR];
+      epilogue_tile(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rinfo, cols);
+    }
+    if constexpr (HasTileMax<Epi>::value) {
+      // each row's maximum over every 128-column group of the tile (past the vocabulary:
+      // excluded; groups wholly past it are not written); 64 * NWV / EPR threads per row,
+      // TPG of them per group, fixed shuffle tree
+      constexpr int TPR = 64 * NWV / EPR, CPT = BN / TPR, NGR = BN / 128, TPG = TPR / NGR;
+      static_assert(BN % 128 == 0 && TPR <= 64 && (TPR & (TPR - 1)) == 0 && CPT * TPR == BN && TPG * NGR == TPR,
+                    "row max layout");
       if (epi.tmax) {
-        const int r = tid / TPR, q = tid % TPR, ncol = epi.w.off[epi.w.n_seg];
+        const int r = tid / TPR, q = tid % TPR, ncol = epi.w.off[epi.w.n_seg], ngr = (ncol + 127) / 128;
         float mx = -INFINITY;
 #pragma unroll
         for (int k = 0; k < CPT; ++k) {
@@ -863,9 +903,9 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
           if (vt0 * 16 + col < ncol) mx = fmaxf(mx, Ct[r * (BN + 1) + col]);
         }
 #pragma unroll
-        for (int o = 1; o < TPR; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-        const int m = m0 + h * EPR + r;
-        if (q == 0 && m < M) epi.tmax[static_cast<size_t>(m) * ((ncol + 127) / 128) + vt0 / 8] = mx;
+        for (int o = 1; o < TPG; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        const int m = m0 + h * EPR + r, grp = vt0 / 8 + q / TPG;
+        if (q % TPG == 0 && m < M && grp < ngr) epi.tmax[static_cast<size_t>(m) * ngr + grp] = mx;
       }
     }
     __syncthreads();
@@ -908,6 +948,13 @@ __global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* 
   __shared__ typename Epi::Row rinfo[16];
   const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 16;
   const int r = threadIdx.x >> 4, cc = (threadIdx.x & 15) * 4;
+  // the rows' and tiles' facts first: their loads overlap the partial loads below
+  __shared__ typename ColOf<Epi>::type cols[HasCol<Epi>::value ? 4 : 1];
+  const int vt0 = c0 / 16, nvt = min(4, n_vtiles - vt0);
+  if (threadIdx.x < 16) rinfo[threadIdx.x] = epi.row(m0 + threadIdx.x < M ? m0 + threadIdx.x : M - 1);
+  if constexpr (HasCol<Epi>::value) {
+    if (threadIdx.x >= 64 && threadIdx.x < 64 + nvt) cols[threadIdx.x - 64] = epi.col(vt0 + threadIdx.x - 64);
+  }
   const size_t zs = static_cast<size_t>(M) * ldp;
   {
     const int m = m0 + r;
@@ -925,8 +972,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* 
     for (int e = 0; e < 4; ++e) Ct[r * 65 + cc + e] = v[e];
   }
   __syncthreads();
-  const int vt0 = c0 / 16, nvt = min(4, n_vtiles - vt0);
-  epilogue_tile(epi, Ct, 65, m0, 16, vt0, nvt, M, rinfo);
+  epilogue_tile<Epi, true>(epi, Ct, 65, m0, 16, vt0, nvt, M, rinfo, HasCol<Epi>::value ? cols : nullptr);
 }
 
 // ---------------------------------------------------------------------------------
@@ -959,6 +1005,9 @@ inline int splitk_plan(int M, int K, int n_vtiles) {
 //    splits: gate/up 24576 wide 92 -> 75 us (unsplit; 2 splits 90 us), QKV 6144 wide 40 ->
 //    30 us (4 splits), O 4096 wide 36 -> 26 us (4), K/V injection 10240 wide 54 -> 44 us
 //    (2), down (K 12288) 56 -> 42 us (8), context fusion (K 20480) 83 -> 57 us (8).
+//  * M >= 512 with at least 256 tiles of 256 x 256: 256 x 256 tiles, 2 slots (half the
+//    bytes per flop of 256 x 128; warm, 16384 x 4096 x 20480: 0.41 -> 0.50 of the bf16
+//    peak, 16384 x 10240 x 4096: 0.39 -> 0.45, 512 x 151936 x 4096: 0.34 -> 0.37).
 //  * otherwise 128 x 128 tiles, 2 slots (two work-groups per compute unit); when there are
 //    fewer than 256 tiles, K split until the grid has >= 512 work-groups with >= 16 slabs
 //    (1024 K values) per split.
@@ -979,6 +1028,7 @@ inline BigPlan big_plan(int M, int K, int n_vtiles) {
     return {64, 128, 3, split(tiles, M <= 16 ? 256 : 128, 4)};
   }
   const long t256 = static_cast<long>((M + 255) / 256) * ((N + 127) / 128);
+  if (M >= 512 && static_cast<long>((M + 255) / 256) * ((N + 255) / 256) >= 256) return {256, 256, 2, 1};
   if (M >= 256) return {256, 128, 3, t256 < 128 ? split(t256, 256, 16, 8) : 1};
   return {128, 128, 2, t128 >= 256 ? 1 : split(t128, 512, 16)};
 }
@@ -1073,7 +1123,9 @@ static hipError_t launch_big(const T* A, int lda, const int32_t* arows, int M, i
   // 64 x 24576 x 4096: 41.6 -> 35.6 us
   if (p.bm == 64)
     return launch_pipe_shape<T, 64, 128, 3, W8, Epi, 8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
-  if (p.bm == 256)
+  if (p.bm == 256 && p.bn == 256 && !W8)
+    return launch_pipe_shape<T, 256, 256, 2, W8, Epi, 8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
+  if (p.bm == 256)   // (FP8 weights keep 256 x 128 tiles)
     return launch_pipe_shape<T, 256, 128, 3, W8, Epi, 8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
   return launch_pipe_shape<T, 128, 128, 2, W8>(A, lda, arows, M, K, n_vtiles, epi, p.ks, scratch, s);
 }
