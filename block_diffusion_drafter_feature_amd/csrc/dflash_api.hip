@@ -352,7 +352,7 @@ int inject_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv
                                W.scratch, W.scratch_bytes, 0, fp8w(c))));
     pr.end(DFLASH_PROBE_INJECT_FC);
   }
-  rmsnorm_kernel<T><<<rows, 256, 0, s>>>(W.hf, static_cast<const T*>(w->g_fc), d, c->rms_eps, W.f, nullptr);
+  launch_rmsnorm<T>(rows, s, W.hf, static_cast<const T*>(w->g_fc), d, c->rms_eps, W.f, nullptr);
   LAUNCH_CHECK();
   EpiInject<T> e{};
   for (int l = 0; l < c->n_layers; ++l) {
@@ -429,7 +429,7 @@ int pre_sublayer(const dflash_config* c, const dflash_layer_weights& L, int site
                  const Probe* pr = nullptr) {
   const int d = c->d_model;
   if (!c->use_conv) {
-    rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(gain), d, c->rms_eps, W.ut, nullptr, emb, ids);
+    launch_rmsnorm<T>(M, s, W.x, static_cast<const T*>(gain), d, c->rms_eps, W.ut, nullptr, emb, ids);
     LAUNCH_CHECK();
     return DFLASH_OK;
   }
@@ -506,7 +506,7 @@ int draft_impl(const dflash_config* c, const dflash_weights* w, const dflash_kv*
     pr.end(DFLASH_PROBE_GATE_UP);
     if ((rc = post_sublayer<T, T>(c, L, 3, L.w_down, W.h, F, M, W, pr, DFLASH_PROBE_DOWN, s))) return rc;
   }
-  rmsnorm_kernel<T><<<M, 256, 0, s>>>(W.x, static_cast<const T*>(w->g_final), d, c->rms_eps, W.ut, final_hidden);
+  launch_rmsnorm<T>(M, s, W.x, static_cast<const T*>(w->g_final), d, c->rms_eps, W.ut, final_hidden);
   LAUNCH_CHECK();
   float* lg = logits ? logits : W.logits;
   // one drafted block (bf16 or FP8 weights): the streaming LM head keeps each work-group's

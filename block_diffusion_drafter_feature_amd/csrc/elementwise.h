@@ -33,16 +33,17 @@ __device__ __forceinline__ void store4(T* p, const float (&u)[4]) {
 
 // u = x / sqrt(mean(x^2) + eps) * g.  Writes u rounded to T (out_t) and/or in fp32 (out_f).
 // One work-group per row; each thread owns 4-float groups c = tid, tid + 256, ... and issues
-// all of its row loads, and the loads of its gains, before reducing (d <= 256 * 4 * 16 per
+// all of its row loads, and the loads of its gains, before reducing (d <= 256 * 4 * MAXV per
 // row in one pass of registers), so the row costs one memory round trip before the stores.
+// MAXV = 4 (d <= 4096) keeps the register count low enough for more rows in flight per
+// compute unit; the sums are the same for every MAXV (the extra groups add zeros).
 // With emb != nullptr the row is first gathered: x[m] = E[ids[m]] widened to fp32 (and
 // stored to x), then normalised -- the embedding step and the first norm in one pass.
-template <typename T>
+template <typename T, int MAXV = 16>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, const T* __restrict__ g, int d,
                                                       float eps, T* __restrict__ out_t, float* __restrict__ out_f,
                                                       const T* __restrict__ emb = nullptr,
                                                       const int32_t* __restrict__ ids = nullptr) {
-  constexpr int MAXV = 16;
   __shared__ float red[8];
   const int m = blockIdx.x;
   f32x4_t* const xw = reinterpret_cast<f32x4_t*>(x + static_cast<size_t>(m) * d);
@@ -84,6 +85,15 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* __restrict__ x, con
     if (c < nv) emit(c, v[i], gv[i]);
   }
   for (int c = threadIdx.x + 256 * MAXV; c < nv; c += 256) emit(c, xr[c], load4<T>(g + 4 * c));
+}
+
+template <typename T>
+inline void launch_rmsnorm(int rows, hipStream_t s, float* x, const T* g, int d, float eps, T* out_t, float* out_f,
+                           const T* emb = nullptr, const int32_t* ids = nullptr) {
+  if (d <= 256 * 4 * 4)
+    rmsnorm_kernel<T, 4><<<rows, 256, 0, s>>>(x, g, d, eps, out_t, out_f, emb, ids);
+  else
+    rmsnorm_kernel<T><<<rows, 256, 0, s>>>(x, g, d, eps, out_t, out_f, emb, ids);
 }
 
 // ------------------------------------------------------------------ bonus calibration input
