@@ -200,6 +200,39 @@ def test_draft_parity(name):
     say(f"  near-tie top-16 swaps: {near}")
 
 
+@pytest.mark.parametrize("batch,vocab,period", [(12, 2000, 0), (12, 2000, 37), (32, 32848, 37)])
+def test_draft_top16_over_group_maxima(batch, vocab, period):
+    """Several drafted blocks with an unsplit LM head: the top-16 stage reads only the
+    128-column groups whose maximum reaches the 16th-largest group maximum.  Vocabularies
+    that end in a partial group (and, at 512 rows with 256-column tiles, a tile whose second
+    half lies wholly past the vocabulary); with period > 0 the LM-head rows repeat, so every
+    logit value recurs across many groups and the ties must resolve to the lowest ids."""
+    import dataclasses
+    say(f"draft top-16 over group maxima: batch {batch}, vocab {vocab}, period {period}")
+    base = synth.workload("t_batch")
+    dims = dataclasses.replace(base.dims, vocab=vocab)
+    ctx = tuple((17 * i) % 150 for i in range(batch))
+    cap = ((max(ctx) + 16 + 31) // 32) * 32
+    W = synth.make_weights(dims, base.seed + period)
+    if period:
+        lm = W["lm_head"]
+        W["lm_head"] = lm[np.arange(lm.shape[0]) % period].copy()
+    K, V = synth.make_cache(dims, ctx, cap, base.seed + 2)
+    ids = synth.make_block_ids(dims, batch, base.seed, 1)
+    dr = D.Drafter(dims, W)
+    cache = D.KVCache(dims, batch, cap)
+    cache.load_logical(K, V)
+    ci, cl, fh, lg = run_draft(dims, dr, cache, ctx, ids)
+    for b in range(batch):
+        np.testing.assert_array_equal(ci[b], H.exact_topk_of(lg[b]))
+        np.testing.assert_array_equal(cl[b], np.take_along_axis(lg[b], ci[b].astype(np.int64), axis=1))
+    if period:   # the winners of a row all carry its largest value, at the lowest ids
+        assert (cl == cl[..., :1]).all()
+    outs = H.oracle_draft(oracle.Model(dims, W), K, V, ctx, ids)
+    for b in (0, batch - 1):
+        H.assert_close_rows(f"logits b{b}", lg[b], outs[b]["logits"], H.tol(dims))
+
+
 def test_draft_long_context():
     """Contexts long enough for many 32-key slabs per attention split (and ragged ends)."""
     say("draft long context t_hd128")
