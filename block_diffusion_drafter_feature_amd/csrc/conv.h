@@ -96,8 +96,23 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r16 = lane & 15, g = lane >> 4;
-  const int ng = d >> 4, g0 = blockIdx.x * 16;
-  const size_t m0 = static_cast<size_t>(blockIdx.y) * 16;
+  // Work-groups are dealt to the 8 XCDs round-robin in dispatch order (x fastest).  When the
+  // grid allows, consecutive work-groups of one XCD take a block of 4 sequences x 8 channel
+  // tiles, so that XCD's L2 holds those sequences' rows and those tiles' generator rows
+  // (otherwise every XCD would fetch every sequence's rows).  A bijection of the grid.
+  int tile = blockIdx.x, seq = blockIdx.y;
+  {
+    const int nt = gridDim.x, ns = gridDim.y, n = nt * ns;
+    if (nt % 8 == 0 && ns % 4 == 0) {
+      const int L = blockIdx.y * nt + blockIdx.x;
+      const int W = (L % 8) * (n / 8) + L / 8;
+      const int r = W % (4 * nt);
+      seq = (W / (4 * nt)) * 4 + r % 4;
+      tile = r / 4;
+    }
+  }
+  const int ng = d >> 4, g0 = tile * 16;
+  const size_t m0 = static_cast<size_t>(seq) * 16;
   const bool gather = PRE && emb != nullptr;
 
   // row r of this block as fp32: the residual / the sublayer output (unused when gathering)
@@ -139,7 +154,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
 #pragma unroll
           for (int i = 0; i < 8; ++i) {
             const int c = c0 + 128 * i;
-            if (gather && blockIdx.x == 0 && c < d) *reinterpret_cast<f32x4_t*>(x + (m0 + r) * d + c) = v[i];
+            if (gather && tile == 0 && c < d) *reinterpret_cast<f32x4_t*>(x + (m0 + r) * d + c) = v[i];
             ss += v[i][0] * v[i][0] + v[i][1] * v[i][1] + v[i][2] * v[i][2] + v[i][3] * v[i][3];
           }
         }
@@ -343,7 +358,7 @@ __global__ __launch_bounds__(64 * kConvWaves) void conv_site_kernel(
       if (tid < 16) {
         const int h = tid >> 3, r = tid & 7;
         const float s = ((ssp[h][0][r] + ssp[h][1][r]) + ssp[h][2][r]) + ssp[h][3][r];
-        ss_out[(m0 + tid) * gridDim.x + blockIdx.x] = s;
+        ss_out[(m0 + tid) * gridDim.x + tile] = s;
       }
     }
   }
