@@ -311,8 +311,16 @@ def main():
         marks, rows_done = [], 0
         pf_probe = D.Probes(("inject_fc", "inject_kv"))
         pieces = [(b, r0, min(chunk, int(ctx[b]) - r0)) for b in range(B) for r0 in range(0, int(ctx[b]), chunk)]
-        for i, (b, r0, n) in enumerate(pieces):
-            hid = torch.randn((n, dims.d_cat), generator=gen, device="cuda", dtype=torch.float32).to(dt_t)
+        # one untimed warm-up call (zero hiddens into the first piece's positions, which the
+        # timed calls overwrite; the generator is not drawn from): the timed calls then run at
+        # the steady clock
+        warm = [pieces[0]] if pieces else []
+        for i, (b, r0, n) in enumerate(warm + pieces):
+            timed = i >= len(warm)
+            if timed:
+                hid = torch.randn((n, dims.d_cat), generator=gen, device="cuda", dtype=torch.float32).to(dt_t)
+            else:
+                hid = torch.zeros((n, dims.d_cat), device="cuda", dtype=dt_t)
             nb = D.dflash_inject_workspace_bytes(dr.cfg, n)
             sub = D.dflash_kv(batch=1, cap=cap)
             for l in range(dims.n_layers):
@@ -322,10 +330,11 @@ def main():
             ws_buf = ws_inj.get(nb)
             e0.record()
             D.dflash_inject_context(dr.cfg, dr.w, sub, hid, n, i32([0, n]), i32([r0]), i32([n]), 1, ws_buf, nb,
-                                    probes=pf_probe.struct if i == len(pieces) - 1 else None)
+                                    probes=pf_probe.struct if i == len(warm) + len(pieces) - 1 else None)
             e1.record()
-            marks.append((e0, e1, n))
-            rows_done += n
+            if timed:
+                marks.append((e0, e1, n))
+                rows_done += n
             del hid
         torch.cuda.synchronize()
         if marks:
