@@ -44,11 +44,13 @@ __device__ __forceinline__ typename Frag<T>::type load_a(const AS* p) {
 // rinfo holds >= rows entries (ROWS_READY: already filled by the caller, and visible to every
 // thread); cols, when given, the per-tile facts of tiles vt0.. (Epi::Col).  Ends without a
 // barrier (the caller syncs before reusing Ct).
-template <class Epi, bool ROWS_READY = false>
+template <class Epi, bool ROWS_READY = false, int NTH = 0>
 __device__ __forceinline__ void epilogue_tile(const Epi& epi, const float* Ct, int ldc, int m_base, int rows,
                                               int vt0, int nvt, int M, const typename Epi::Row* rinfo_in,
                                               const typename ColOf<Epi>::type* cols = nullptr) {
-  const int nth = blockDim.x, tid = threadIdx.x;
+  // NTH: the work-group size when known at compile time (the element loops then have a known
+  // trip count, so their loads can be issued ahead of the stores)
+  const int nth = NTH > 0 ? NTH : static_cast<int>(blockDim.x), tid = threadIdx.x;
   typename Epi::Row* rinfo = const_cast<typename Epi::Row*>(rinfo_in);
   if constexpr (!ROWS_READY) {
     for (int r = tid; r < rows; r += nth) rinfo[r] = epi.row(m_base + r < M ? m_base + r : M - 1);
@@ -675,7 +677,7 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ 
     }
     __syncthreads();
     __shared__ typename Epi::Row rinfo[64];
-    epilogue_tile(epi, Ct, BN + 1, m0 + half * 64, 64, vt0, BN / 16, M, rinfo);
+    epilogue_tile<Epi, false, 256>(epi, Ct, BN + 1, m0 + half * 64, 64, vt0, BN / 16, M, rinfo);
     __syncthreads();
   }
 }
@@ -895,10 +897,10 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
     __syncthreads();
     const typename ColOf<Epi>::type* cols = HasCol<Epi>::value ? cols_all : nullptr;
     if constexpr (kRows) {
-      epilogue_tile<Epi, true>(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rows_all + h * EPR, cols);
+      epilogue_tile<Epi, true, 64 * NWV>(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rows_all + h * EPR, cols);
     } else {
       __shared__ typename Epi::Row rinfo[EPR];
-      epilogue_tile(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rinfo, cols);
+      epilogue_tile<Epi, false, 64 * NWV>(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rinfo, cols);
     }
     if constexpr (HasTileMax<Epi>::value) {
       // each row's maximum over every 128-column group of the tile (past the vocabulary:
@@ -985,7 +987,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* 
     for (int e = 0; e < 4; ++e) Ct[r * 65 + cc + e] = v[e];
   }
   __syncthreads();
-  epilogue_tile<Epi, true>(epi, Ct, 65, m0, 16, vt0, nvt, M, rinfo, HasCol<Epi>::value ? cols : nullptr);
+  epilogue_tile<Epi, true, 256>(epi, Ct, 65, m0, 16, vt0, nvt, M, rinfo, HasCol<Epi>::value ? cols : nullptr);
 }
 
 // ---------------------------------------------------------------------------------
