@@ -14,6 +14,9 @@
 //   apply(vt, m, row, c, v, partner)
 //   Col, col(vt)      optional: per-tile facts (destination, kind) worked out once per virtual
 //                     tile; the staged epilogues then call apply(col, m, row, c, v, partner)
+//   kRope             optional: rotary epilogue; rope_pairs(), rope_inv(j) give the frequencies
+//                     and apply(col, m, row, c, v, partner, cs_row) takes the row's (cos, sin)
+//                     table (Row has pos)
 #pragma once
 
 #include "common.h"
@@ -107,6 +110,13 @@ template <class Epi>
 struct ColOf<Epi, true> {
   typedef typename Epi::Col type;
 };
+
+// Epilogues with rotary pairs (Epi::kRope): the staged epilogues may hand apply() a table of
+// (cos, sin) per row and frequency, worked out once per row and pair instead of per element.
+template <class Epi, class = void>
+struct HasRope : std::false_type {};
+template <class Epi>
+struct HasRope<Epi, std::void_t<decltype(Epi::kRope)>> : std::integral_constant<bool, Epi::kRope> {};
 
 template <class Epi>
 struct HasTileMax {
@@ -210,6 +220,23 @@ struct EpiQKV {
     const int kind = cf.kind;
     put(cf.p, kind, cf.tt, kind == 0 || kind == 1 ? cf.inv[c & 7] : 0.0, m, rw, c, v, pv);
   }
+  static constexpr bool kRope = true;
+  __device__ __forceinline__ int rope_pairs() const { return hd / 2; }
+  __device__ __forceinline__ double rope_inv(int j) const { return rf.inv[j]; }
+  __device__ __forceinline__ void apply(const Col& cf, int m, const Row&, int c, float v, float pv,
+                                        const float2* cs_row) const {
+    const int kind = cf.kind, b = m >> 4, j = m & 15;
+    if (kind < 0) return;
+    if (kind < 2) {
+      const float2 t = cs_row[8 * cf.tt + (c & 7)];
+      const float r = (c < 8) ? v * t.x - pv * t.y : v * t.x + pv * t.y;
+      const int dim = rope_dim(cf.tt, c, hd);
+      if (kind == 0) cf.p[static_cast<size_t>(m) * H * hd + dim] = from_f<T>(r);
+      else cf.p[(static_cast<size_t>(b) * Hkv * 16 + j) * hd + dim] = from_f<T>(r);
+    } else {
+      cf.p[static_cast<size_t>(b) * Hkv * hd * 16 + c * 16 + j] = from_f<T>(v);
+    }
+  }
   __device__ __forceinline__ void apply(int vt, int m, const Row& rw, int c, float v, float pv) const {
     const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
     if (vt < tq) put(q + (vt / tph) * hd, 0, vt % tph, rf.inv[8 * (vt % tph) + (c & 7)], m, rw, c, v, pv);
@@ -310,6 +337,22 @@ struct EpiInject {
   __device__ __forceinline__ void apply(const Col& cf, int, const Row& rw, int c, float v, float pv) const {
     const int kind = cf.kind;
     put(cf.p, kind, cf.tt, kind == 0 ? cf.inv[c & 7] : 0.0, rw, c, v, pv);
+  }
+  static constexpr bool kRope = true;
+  __device__ __forceinline__ int rope_pairs() const { return hd / 2; }
+  __device__ __forceinline__ double rope_inv(int j) const { return rf.inv[j]; }
+  __device__ __forceinline__ void apply(const Col& cf, int, const Row& rw, int c, float v, float pv,
+                                        const float2* cs_row) const {
+    const int kind = cf.kind;
+    if (kind < 0 || rw.b < 0) return;
+    const size_t bo = static_cast<size_t>(rw.b) * Hkv * cap * hd;
+    if (kind == 0) {
+      const float2 t = cs_row[8 * cf.tt + (c & 7)];
+      const float r = (c < 8) ? v * t.x - pv * t.y : v * t.x + pv * t.y;
+      cf.p[bo + static_cast<size_t>(rw.pos) * hd + rope_dim(cf.tt, c, hd)] = from_f<T>(r);
+    } else {
+      cf.p[bo + static_cast<size_t>(c) * cap + rw.pos] = from_f<T>(v);
+    }
   }
   __device__ __forceinline__ void apply(int vt, int, const Row& rw, int c, float v, float pv) const {
     const int tk = Hkv * hd / 16, tph = hd / 16;

@@ -47,7 +47,8 @@ __device__ __forceinline__ typename Frag<T>::type load_a(const AS* p) {
 template <class Epi, bool ROWS_READY = false, int NTH = 0>
 __device__ __forceinline__ void epilogue_tile(const Epi& epi, const float* Ct, int ldc, int m_base, int rows,
                                               int vt0, int nvt, int M, const typename Epi::Row* rinfo_in,
-                                              const typename ColOf<Epi>::type* cols = nullptr) {
+                                              const typename ColOf<Epi>::type* cols = nullptr,
+                                              float2* trig = nullptr) {
   // NTH: the work-group size when known at compile time (the element loops then have a known
   // trip count, so their loads can be issued ahead of the stores)
   const int nth = NTH > 0 ? NTH : static_cast<int>(blockDim.x), tid = threadIdx.x;
@@ -57,6 +58,30 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, const float* Ct, i
     __syncthreads();
   }
   const int per = rows * 16;
+  if constexpr (HasRope<Epi>::value && HasCol<Epi>::value) {
+    // rotary epilogue: (cos, sin) of every row and frequency pair once, then the elements
+    if (cols && trig) {
+      const int np = epi.rope_pairs();
+      for (int e = tid; e < rows * np; e += nth) {
+        const int r = e / np, j = e - r * np;
+        float cs, sn;
+        rope_cs(rinfo[r].pos, epi.rope_inv(j), &cs, &sn);
+        trig[e] = make_float2(cs, sn);
+      }
+      __syncthreads();
+      for (int v = 0; v < nvt; ++v) {
+        const bool cm = epi.colmajor(vt0 + v);
+        for (int e = tid; e < per; e += nth) {
+          const int r = cm ? e % rows : e >> 4, c = cm ? e / rows : e & 15;
+          const int m = m_base + r;
+          if (m >= M) continue;
+          const float* row = Ct + r * ldc;
+          epi.apply(cols[v], m, rinfo[r], c, row[v * 16 + c], row[((v ^ Epi::PX) << 4) | (c ^ Epi::PC)], trig + r * np);
+        }
+      }
+      return;
+    }
+  }
   for (int v = 0; v < nvt; ++v) {
     const int vt = vt0 + v;
     const bool cm = epi.colmajor(vt);
@@ -896,8 +921,13 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
     }
     __syncthreads();
     const typename ColOf<Epi>::type* cols = HasCol<Epi>::value ? cols_all : nullptr;
+    // (cos, sin) table of a rotary epilogue in slot 1, free after the main loop
+    float2* trig = nullptr;
+    if constexpr (HasRope<Epi>::value) {
+      if (static_cast<size_t>(EPR) * epi.rope_pairs() * sizeof(float2) <= STAGE * sizeof(T)) trig = reinterpret_cast<float2*>(s1);
+    }
     if constexpr (kRows) {
-      epilogue_tile<Epi, true, 64 * NWV>(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rows_all + h * EPR, cols);
+      epilogue_tile<Epi, true, 64 * NWV>(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rows_all + h * EPR, cols, trig);
     } else {
       __shared__ typename Epi::Row rinfo[EPR];
       epilogue_tile<Epi, false, 64 * NWV>(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rinfo, cols);
@@ -987,7 +1017,12 @@ __global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* 
     for (int e = 0; e < 4; ++e) Ct[r * 65 + cc + e] = v[e];
   }
   __syncthreads();
-  epilogue_tile<Epi, true, 256>(epi, Ct, 65, m0, 16, vt0, nvt, M, rinfo, HasCol<Epi>::value ? cols : nullptr);
+  float2* trig = nullptr;
+  if constexpr (HasRope<Epi>::value) {
+    __shared__ float2 trig_s[16 * 64];
+    if (epi.rope_pairs() <= 64) trig = trig_s;
+  }
+  epilogue_tile<Epi, true, 256>(epi, Ct, 65, m0, 16, vt0, nvt, M, rinfo, HasCol<Epi>::value ? cols : nullptr, trig);
 }
 
 // ---------------------------------------------------------------------------------
