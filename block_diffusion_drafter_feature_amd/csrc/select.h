@@ -362,15 +362,28 @@ __global__ __launch_bounds__(256) void argmax_partial_kernel(const TL* __restric
   int bi = INT_MAX;
   const bool vec = ((reinterpret_cast<uintptr_t>(row) & 15) == 0) && (c0 % EPV == 0);
   if (vec) {
+    // four 16-byte loads per thread in flight at once (the (value, lowest id) maximum does
+    // not depend on the order the elements are visited)
+    constexpr int U = 4;
     const int nvec = (c1 - c0) / EPV;
-    for (int q = threadIdx.x; q < nvec; q += 256) {
-      const u32x4_t u = *reinterpret_cast<const u32x4_t*>(row + c0 + q * EPV);
+    for (int q0 = threadIdx.x; q0 < nvec; q0 += 256 * U) {
+      u32x4_t u[U];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        float f;
-        if constexpr (sizeof(TL) == 2) f = __uint_as_float((e & 1) ? (u[e >> 1] & 0xffff0000u) : (u[e >> 1] << 16));
-        else f = __uint_as_float(u[e]);
-        argmax_step(bv, bi, f, c0 + q * EPV + e);
+      for (int k = 0; k < U; ++k) {
+        const int q = q0 + 256 * k;
+        u[k] = q < nvec ? *reinterpret_cast<const u32x4_t*>(row + c0 + q * EPV) : u32x4_t{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int k = 0; k < U; ++k) {
+        const int q = q0 + 256 * k;
+        if (q >= nvec) break;
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          float f;
+          if constexpr (sizeof(TL) == 2) f = __uint_as_float((e & 1) ? (u[k][e >> 1] & 0xffff0000u) : (u[k][e >> 1] << 16));
+          else f = __uint_as_float(u[k][e]);
+          argmax_step(bv, bi, f, c0 + q * EPV + e);
+        }
       }
     }
     for (int j = c0 + nvec * EPV + threadIdx.x; j < c1; j += 256) argmax_step(bv, bi, to_f<TL>(row[j]), j);
