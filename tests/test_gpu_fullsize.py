@@ -205,3 +205,28 @@ def test_fullsize_step(name, sample, conv_scale, fp8):
     for b in range(B):
         assert (acc_h[b], bon_h[b]) == oracle.verify(draft[b], oracle.decode(T2[b], dims.dtype)), b
     say(f"  accept lengths {acc_h.tolist()[:8]}...")
+
+
+def test_prefill_chunk_large_tiles():
+    """A 4096-row injection at the full model shape: the context-fusion and K/V GEMMs then run
+    256 x 256 tiles in their XCD-grouped order (16 x 16 and 16 x 40 tiles).  One sampled row of
+    every 256-row tile (and the last row), all K/V columns of every layer, against the oracle."""
+    wl, (W, m, dr) = drafter_for("c2", "config")
+    dims = wl.dims
+    rows, cap = 4096, wl.cap
+    assert cap >= rows
+    say(f"prefill chunk: {rows} rows at d {dims.d}, d_cat {dims.d_cat}")
+    cache = D.KVCache(dims, 1, cap, fill=0.0)
+    hid = synth.make_hidden(dims, rows, 900)
+    nb = D.dflash_inject_workspace_bytes(dr.cfg, rows)
+    D.dflash_inject_context(dr.cfg, dr.w, cache.kv, D.to_device(hid, dims), rows, i32([0, rows]), i32([0]),
+                            i32([rows]), 1, ws(nb), nb)
+    torch.cuda.synchronize()
+    sample = np.array([t * 256 + (37 * t) % 256 for t in range(rows // 256)] + [rows - 1])
+    _, Ko, Vo = oracle.inject_rows(m, hid[sample], sample)
+    t = H.tol(dims)
+    for l in range(dims.n_layers):
+        Kg = cache.k[l][0].float().cpu().numpy()
+        Vg = cache.vt[l][0].float().cpu().numpy()
+        H.assert_close_rows(f"prefill K l{l}", Kg[:, sample].transpose(1, 0, 2), Ko[l], t)
+        H.assert_close_rows(f"prefill V l{l}", Vg[:, :, sample].transpose(2, 0, 1), Vo[l], t)
