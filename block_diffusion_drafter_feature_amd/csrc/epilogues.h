@@ -16,7 +16,10 @@
 //                     tile; the staged epilogues then call apply(col, m, row, c, v, partner)
 //   kRope             optional: rotary epilogue; rope_pairs(), rope_inv(j) give the frequencies
 //                     and apply(col, m, row, c, v, partner, cs_row) takes the row's (cos, sin)
-//                     table (Row has pos)
+//                     table (Row has pos); kind8(col) (1 rotated, 0 value, -1 none),
+//                     store8_rot(col, m, row, half, v[8]) (8 consecutive dimensions of a row)
+//                     and store8_val(col, m0, rows, c, v[8], M) (column c of 8 consecutive
+//                     rows) store 8 finished values at once
 #pragma once
 
 #include "common.h"
@@ -117,6 +120,27 @@ template <class Epi, class = void>
 struct HasRope : std::false_type {};
 template <class Epi>
 struct HasRope<Epi, std::void_t<decltype(Epi::kRope)>> : std::integral_constant<bool, Epi::kRope> {};
+
+// 8 consecutive values of T from floats: one 16-byte (bf16) or two (fp32) stores when p is
+// aligned for them, else element by element
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&o)[8]) {
+  if ((reinterpret_cast<uintptr_t>(p) & (8 * sizeof(T) - 1)) == 0) {
+    if constexpr (sizeof(T) == 2) {
+      u32x4_t w;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        w[k] = static_cast<uint32_t>(from_f<T>(o[2 * k])) | (static_cast<uint32_t>(from_f<T>(o[2 * k + 1])) << 16);
+      *reinterpret_cast<u32x4_t*>(p) = w;
+    } else {
+      reinterpret_cast<f32x4_t*>(p)[0] = f32x4_t{o[0], o[1], o[2], o[3]};
+      reinterpret_cast<f32x4_t*>(p)[1] = f32x4_t{o[4], o[5], o[6], o[7]};
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 8; ++k) p[k] = from_f<T>(o[k]);
+  }
+}
 
 template <class Epi>
 struct HasTileMax {
@@ -237,6 +261,24 @@ struct EpiQKV {
       cf.p[static_cast<size_t>(b) * Hkv * hd * 16 + c * 16 + j] = from_f<T>(v);
     }
   }
+  __device__ __forceinline__ int kind8(const Col& cf) const { return cf.kind < 0 ? -1 : (cf.kind < 2 ? 1 : 0); }
+  __device__ __forceinline__ void store8_rot(const Col& cf, int m, const Row&, int h, const float (&o)[8]) const {
+    const int dim0 = rope_dim(cf.tt, 8 * h, hd), b = m >> 4, j = m & 15;
+    if (cf.kind == 0) store8(cf.p + static_cast<size_t>(m) * H * hd + dim0, o);
+    else store8(cf.p + (static_cast<size_t>(b) * Hkv * 16 + j) * hd + dim0, o);
+  }
+  // rows m0 .. m0+7 lie in one 16-row block (m0 % 8 == 0)
+  __device__ __forceinline__ void store8_val(const Col& cf, int m0, const Row*, int c, const float (&o)[8],
+                                             int M) const {
+    T* p = cf.p + static_cast<size_t>(m0 >> 4) * Hkv * hd * 16 + c * 16 + (m0 & 15);
+    if (m0 + 8 <= M) {
+      store8(p, o);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        if (m0 + k < M) p[k] = from_f<T>(o[k]);
+    }
+  }
   __device__ __forceinline__ void apply(int vt, int m, const Row& rw, int c, float v, float pv) const {
     const int tq = H * hd / 16, tk = Hkv * hd / 16, tph = hd / 16;
     if (vt < tq) put(q + (vt / tph) * hd, 0, vt % tph, rf.inv[8 * (vt % tph) + (c & 7)], m, rw, c, v, pv);
@@ -352,6 +394,28 @@ struct EpiInject {
       cf.p[bo + static_cast<size_t>(rw.pos) * hd + rope_dim(cf.tt, c, hd)] = from_f<T>(r);
     } else {
       cf.p[bo + static_cast<size_t>(c) * cap + rw.pos] = from_f<T>(v);
+    }
+  }
+  __device__ __forceinline__ int kind8(const Col& cf) const { return cf.kind < 0 ? -1 : (cf.kind == 0 ? 1 : 0); }
+  __device__ __forceinline__ void store8_rot(const Col& cf, int, const Row& rw, int h, const float (&o)[8]) const {
+    if (rw.b < 0) return;
+    store8(cf.p + static_cast<size_t>(rw.b) * Hkv * cap * hd + static_cast<size_t>(rw.pos) * hd +
+               rope_dim(cf.tt, 8 * h, hd), o);
+  }
+  // column c of rows m0 .. m0+7: one 8-wide store when they are 8 consecutive cache positions of
+  // one sequence, else row by row (rows not stored skipped)
+  __device__ __forceinline__ void store8_val(const Col& cf, int m0, const Row* rows, int c, const float (&o)[8],
+                                             int M) const {
+    const Row r0 = rows[0], r7 = rows[7];
+    if (m0 + 8 <= M && r0.b >= 0 && r7.b == r0.b && r7.pos == r0.pos + 7) {
+      store8(cf.p + static_cast<size_t>(r0.b) * Hkv * cap * hd + static_cast<size_t>(c) * cap + r0.pos, o);
+    } else {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const Row rk = rows[k];
+        if (m0 + k < M && rk.b >= 0)
+          cf.p[static_cast<size_t>(rk.b) * Hkv * cap * hd + static_cast<size_t>(c) * cap + rk.pos] = from_f<T>(o[k]);
+      }
     }
   }
   __device__ __forceinline__ void apply(int vt, int, const Row& rw, int c, float v, float pv) const {

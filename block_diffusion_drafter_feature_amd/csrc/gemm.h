@@ -69,6 +69,38 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, const float* Ct, i
         trig[e] = make_float2(cs, sn);
       }
       __syncthreads();
+      if (rows % 8 == 0) {
+        // 8-wide items, 2 * rows per tile: a rotated tile's row halves (8 consecutive
+        // dimensions, rotated against the other half) or a value tile's columns over 8
+        // consecutive rows; each item is one 16-byte store
+        const int ipt = 2 * rows, nhalf = rows / 8;
+        for (int it = tid; it < nvt * ipt; it += nth) {
+          const int v = it / ipt, sub = it - v * ipt;
+          const typename Epi::Col& cf = cols[v];
+          const int kind = epi.kind8(cf);
+          float o[8];
+          if (kind > 0) {
+            const int r = sub >> 1, h = sub & 1;
+            if (m_base + r >= M) continue;
+            const float* a = Ct + r * ldc + v * 16 + 8 * h;
+            const float* b = Ct + r * ldc + v * 16 + 8 * (1 - h);
+            const float2* t = trig + r * np + 8 * cf.tt;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) {
+              const float2 cs = t[k];
+              o[k] = h == 0 ? a[k] * cs.x - b[k] * cs.y : a[k] * cs.x + b[k] * cs.y;
+            }
+            epi.store8_rot(cf, m_base + r, rinfo[r], h, o);
+          } else if (kind == 0) {
+            const int c = sub / nhalf, r0 = 8 * (sub - c * nhalf);
+            if (m_base + r0 >= M) continue;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) o[k] = Ct[(r0 + k) * ldc + v * 16 + c];
+            epi.store8_val(cf, m_base + r0, rinfo + r0, c, o, M);
+          }
+        }
+        return;
+      }
       for (int v = 0; v < nvt; ++v) {
         const bool cm = epi.colmajor(vt0 + v);
         for (int e = tid; e < per; e += nth) {
