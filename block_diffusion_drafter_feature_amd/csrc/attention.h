@@ -28,7 +28,8 @@
 //     keys 8g..8g+7 of the slab for its query column -- exactly the B-operand layout of
 //   O^T[dim, q] += V^T P^T: A = V^T (8 consecutive keys per lane), B = P^T straight
 //     from the S^T registers.
-// Online softmax in base 2 with per-query running max/sum.  With S == 1 the kernel
+// Online softmax in base 2 with a per-query reference point and running sum; the reference
+// moves only when a score passes it by more than 2^8, so the running output is rarely rescaled.  With S == 1 the kernel
 // writes the normalised output; otherwise each split writes (O, m, l) partials that
 // attn_combine_kernel merges in split order (deterministic).
 #pragma once
@@ -108,6 +109,7 @@ __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
   constexpr int CPR = HD / TL::CE;   // chunks per K row
   constexpr int CPV = TL::TK / TL::CE;
   static_assert(TL::KCH % NT == 0 && TL::VCH % NT == 0, "tile must split evenly over the work-group");
+  constexpr float kSlack = 8.f;     // log2 headroom of the softmax weights over the reference point
   static_assert(KW == 1 || (KW - 1) * G * 16 * (HD + 4) * 4 + KW * G * 16 * 8 <= 2 * TL::STAGE * sizeof(T),
                 "wave merge must fit in the tile buffers");
   __shared__ __align__(16) T lds[2 * TL::STAGE];
@@ -150,35 +152,46 @@ __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) st[t] = F::mma(st[t], kf[t][ks], qf[ks]);
     }
-    float sv[8];
+    if (nvalid < 32) {   // a tail slab (wave-uniform): keys past the end get no weight
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (8 * lg + 4 * t + i >= nvalid) st[t][i] = -INFINITY;
+    }
+    // the raw maximum scaled once: x -> x * scale (scale > 0) preserves the order
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = 8 * lg + 4 * t + i;
-        const float v = key < nvalid ? st[t][i] * a.scale_log2 : -INFINITY;
-        sv[4 * t + i] = v;
-        mx = fmaxf(mx, v);
-      }
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float mnew = fmaxf(mrow, mx);
-    const float corr = exp2f(mrow - mnew);
-    float ps = 0.f;
+    mx *= a.scale_log2;
+    // The softmax's reference point mrow moves only when a score passes it by more than
+    // kSlack (base 2), or on the first slab; any reference gives the same normalised result,
+    // and the weights exp2(s - mrow) stay <= 2^kSlack.  With no lane moving (wave-uniform),
+    // the rescaling of the running sums is skipped altogether.
+    const float mref = mx > mrow + kSlack ? mx : mrow;
+    if (__ballot(mref != mrow)) {
+      const float corr = __builtin_amdgcn_exp2f(mrow - mref);   // 0 on the first slab, 1 where unmoved
+      lsum *= corr;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sv[e] = exp2f(sv[e] - mnew);
-      ps += sv[e];
+      for (int dt = 0; dt < DT; ++dt) o[dt] *= corr;
+      mrow = mref;
     }
-    lsum = lsum * corr + ps;
-    mrow = mnew;
+    float sv[8], ps = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        sv[4 * t + i] = __builtin_amdgcn_exp2f(fmaf(st[t][i], a.scale_log2, -mrow));
+        ps += sv[4 * t + i];
+      }
+    lsum += ps;
     const frag_t pf = F::from_floats(sv);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      o[dt] *= corr;
-      o[dt] = F::mma(o[dt], vf[dt], pf);
-    }
+    for (int dt = 0; dt < DT; ++dt) o[dt] = F::mma(o[dt], vf[dt], pf);
   };
 
   // ---- context tiles through LDS
@@ -212,11 +225,19 @@ __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
       *reinterpret_cast<u32x4_t*>(st + row * TL::KSTR + c * TL::CE) = ck[p];
     }
     T* sv = st + TL::TK * TL::KSTR;
+    if (kb0 + TL::TK <= kend) {   // a whole tile (work-group-uniform)
 #pragma unroll
-    for (int p = 0; p < NV; ++p) {
-      const int e = tid + p * NT, dim = e / CPV, c = e % CPV;
-      const int nv = kend - (kb0 + c * TL::CE);
-      *reinterpret_cast<u32x4_t*>(sv + dim * TL::VSTR + c * TL::CE) = nv >= TL::CE ? cv[p] : keep_first<T>(cv[p], nv);
+      for (int p = 0; p < NV; ++p) {
+        const int e = tid + p * NT, dim = e / CPV, c = e % CPV;
+        *reinterpret_cast<u32x4_t*>(sv + dim * TL::VSTR + c * TL::CE) = cv[p];
+      }
+    } else {
+#pragma unroll
+      for (int p = 0; p < NV; ++p) {
+        const int e = tid + p * NT, dim = e / CPV, c = e % CPV;
+        const int nv = kend - (kb0 + c * TL::CE);
+        *reinterpret_cast<u32x4_t*>(sv + dim * TL::VSTR + c * TL::CE) = nv >= TL::CE ? cv[p] : keep_first<T>(cv[p], nv);
+      }
     }
   };
   auto compute = [&](const T* st, int tile) {
@@ -242,19 +263,23 @@ __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
     T* buf1 = lds + TL::STAGE;
     u32x4_t k0[NK], v0[NV], k1[NK], v1[NV];
     gload(k0, v0, 0);
+    __builtin_amdgcn_sched_barrier(0);   // keep tile 0's loads ahead of tile 1's
     gload(k1, v1, 1);
-    lstore(buf0, k0, v0, 0);
-    __syncthreads();
+    // Each pass stores a landed tile, then fetches the tile two ahead into the same
+    // registers before computing; every tile's loads stay in flight over two compute
+    // phases.  The loop has a single exit at its head, so the loads are issued in the same
+    // order on every path into it (tile 0 before tile 1 here) and only the older tile is
+    // waited for.  A tile past the
+    // end (odd count) reads zeros and computes nothing.
     for (int i = 0; i < ntiles; i += 2) {
+      lstore(buf0, k0, v0, i);
+      __syncthreads();
       gload(k0, v0, i + 2);
       compute(buf0, i);
       lstore(buf1, k1, v1, i + 1);
       __syncthreads();
-      if (i + 1 >= ntiles) break;
       gload(k1, v1, i + 3);
       compute(buf1, i + 1);
-      lstore(buf0, k0, v0, i + 2);
-      __syncthreads();
     }
   }
 

@@ -33,13 +33,16 @@ __device__ __forceinline__ float bf2f(bf16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// float -> bf16, round to nearest, ties to even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7f800000u) == 0x7f800000u && (u & 0x007fffffu)) return static_cast<bf16_t>((u >> 16) | 0x40);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+// float -> bf16, round to nearest, ties to even, by the gfx950 conversion instruction
+// (v_cvt_pk_bf16_f32; NaN stays NaN).  Two values per instruction: pk_bf16 packs a
+// (low half) and b (high half).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  const f32x2_t f = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f, bf16x2_t));
 }
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f)); }
 
 template <typename T> __device__ __forceinline__ float to_f(T v);
 template <> __device__ __forceinline__ float to_f<float>(float v) { return v; }
@@ -94,18 +97,11 @@ template <> struct Frag<bf16_t> {
   __device__ __forceinline__ static type load_f32(const float* p) {
     const f32x4_t a = *reinterpret_cast<const f32x4_t*>(p);
     const f32x4_t b = *reinterpret_cast<const f32x4_t*>(p + 4);
-    u32x4_t r;
-    r[0] = static_cast<uint32_t>(f2bf(a[0])) | (static_cast<uint32_t>(f2bf(a[1])) << 16);
-    r[1] = static_cast<uint32_t>(f2bf(a[2])) | (static_cast<uint32_t>(f2bf(a[3])) << 16);
-    r[2] = static_cast<uint32_t>(f2bf(b[0])) | (static_cast<uint32_t>(f2bf(b[1])) << 16);
-    r[3] = static_cast<uint32_t>(f2bf(b[2])) | (static_cast<uint32_t>(f2bf(b[3])) << 16);
+    const u32x4_t r = {pk_bf16(a[0], a[1]), pk_bf16(a[2], a[3]), pk_bf16(b[0], b[1]), pk_bf16(b[2], b[3])};
     return __builtin_bit_cast(type, r);
   }
   __device__ __forceinline__ static type from_floats(const float* v) {
-    u32x4_t r;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      r[j] = static_cast<uint32_t>(f2bf(v[2 * j])) | (static_cast<uint32_t>(f2bf(v[2 * j + 1])) << 16);
+    const u32x4_t r = {pk_bf16(v[0], v[1]), pk_bf16(v[2], v[3]), pk_bf16(v[4], v[5]), pk_bf16(v[6], v[7])};
     return __builtin_bit_cast(type, r);
   }
   __device__ __forceinline__ static f32x4_t mma(f32x4_t acc, type a, type b) {
