@@ -165,9 +165,7 @@ __global__ __launch_bounds__(256, 2) void block_attn_kernel(AttnArgs<T> a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) mx = fmaxf(mx, st[t][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    mx *= a.scale_log2;
+    mx = max_lane_groups(mx) * a.scale_log2;
     // The softmax's reference point mrow moves only when a score passes it by more than
     // kSlack (base 2), or on the first slab; any reference gives the same normalised result,
     // and the weights exp2(s - mrow) stay <= 2^kSlack.  With no lane moving (wave-uniform),
