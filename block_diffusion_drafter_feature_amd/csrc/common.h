@@ -192,16 +192,31 @@ __device__ __forceinline__ void rope_cs(int pos, double inv, float* c, float* s)
 
 // ------------------------------------------------------------------ wave reductions
 
+// Wave-wide sum and maximum without LDS permutes: two quad permutations, the half-row and
+// row mirrors (DPP), then the gfx950 row swaps across 16 and 32 lanes.  Each step combines a
+// lane with a partner that holds the same partial over a disjoint set of lanes, so the tree
+// is fixed and every lane ends with the same value.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f<0xB1>(v);    // quad_perm [1, 0, 3, 2]
+  v += dpp_f<0x4E>(v);    // quad_perm [2, 3, 0, 1]
+  v += dpp_f<0x141>(v);   // row_half_mirror
+  v += dpp_f<0x140>(v);   // row_mirror
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f<0xB1>(v));
+  v = fmaxf(v, dpp_f<0x4E>(v));
+  v = fmaxf(v, dpp_f<0x141>(v));
+  v = fmaxf(v, dpp_f<0x140>(v));
+  return max_lane_groups(v);
 }
 
 // deterministic block-wide sum (fixed reduction tree); `red` holds >= nwaves floats
