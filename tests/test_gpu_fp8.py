@@ -108,6 +108,42 @@ def test_fp8_draft_parity(name, batch):
         assert e16 > e
 
 
+def test_fp8_draft_wide_vocab_256_rows():
+    """Sixteen drafted blocks (256 rows, the pipelined kernel's 256-row tiles) over a
+    vocabulary of 65552 columns, the last tile holding 16 live columns: logits against the
+    oracle's quantized model, top-16 exactly that of the device's logits."""
+    import dataclasses
+    base = synth.workload("t_batch")
+    dims = dataclasses.replace(base.dims, vocab=65552)
+    B = 16
+    ctx = tuple((23 * i) % 190 for i in range(B))
+    cap = ((max(ctx) + 16 + 31) // 32) * 32
+    say(f"fp8 draft wide vocab: batch {B}, vocab {dims.vocab}")
+    W = synth.make_weights(dims, base.seed + 5)
+    K, V = synth.make_cache(dims, ctx, cap, base.seed + 6)
+    ids = synth.make_block_ids(dims, B, base.seed, 1)
+    dr = D.Drafter(dims, W, fp8=True)
+    cache = D.KVCache(dims, B, cap)
+    cache.load_logical(K, V)
+    ci = torch.zeros((B, 16, 16), dtype=torch.int32, device="cuda")
+    cl = torch.zeros((B, 16, 16), dtype=torch.float32, device="cuda")
+    fh = torch.zeros((B, 16, dims.d), dtype=torch.float32, device="cuda")
+    lg = torch.zeros((B, 16, dims.vocab), dtype=torch.float32, device="cuda")
+    nb = D.dflash_draft_workspace_bytes(dr.cfg, B, cache.cap)
+    D.dflash_draft_block(dr.cfg, dr.w, cache.kv, i32(ctx), i32(ids), B, ci, cl, fh, lg, ws_of(nb), nb)
+    torch.cuda.synchronize()
+    ci, cl, lg = ci.cpu().numpy(), cl.cpu().numpy(), lg.cpu().numpy()
+    for b in range(B):
+        np.testing.assert_array_equal(ci[b], H.exact_topk_of(lg[b]))
+        np.testing.assert_array_equal(cl[b], np.take_along_axis(lg[b], ci[b].astype(np.int64), axis=1))
+    sel = (0, 7, B - 1)
+    outs = H.oracle_draft(oracle.Model(dims, W, fp8=True), K[:, list(sel)], V[:, list(sel)],
+                          tuple(ctx[b] for b in sel), ids[list(sel)])
+    for b, o in zip(sel, outs):
+        e = H.assert_close_rows(f"logits b{b}", lg[b], o["logits"], H.tol(dims))
+        say(f"  b{b}: logits rel err {e:.2e}")
+
+
 @pytest.mark.parametrize("rows", [16, 200])
 def test_fp8_inject_parity(rows):
     say(f"fp8 inject rows={rows}")
