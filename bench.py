@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--sampled-steps", type=int, default=20,
                     help="also time this many steps of the sampling variant (sampled path choice and "
                          "verification by rejection sampling, temperature 0.8) and report them apart")
+    ap.add_argument("--graph-steps", type=int, default=20,
+                    help="also capture the step in a HIP graph and time this many replays (reported apart)")
     ap.add_argument("--fp8-steps", type=int, default=20,
                     help="also time this many steps with the streamed projections in FP8 storage (E4M3 codes, "
                          "a float32 scale per row) and report them apart (bf16 workloads)")
@@ -479,6 +481,33 @@ def main():
         for n in names:
             breakdown[n] = roof(n, avg_ms(pr, n)) if n != "topk" else {"ms": round(avg_ms(pr, n), 4)}
 
+    # the same step captured once in a HIP graph and replayed (what a serving loop that
+    # cannot afford per-kernel launches would run); reported apart, never as the value
+    graph = None
+    if args.graph_steps > 0:
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            step()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.graph_steps):
+            g.replay()
+        stop.record()
+        torch.cuda.synchronize()
+        ms_g = start.elapsed_time(stop) / args.graph_steps
+        log(f"[bench] graph replays: {ms_g:.3f} ms/step, {B * 1000.0 / ms_g:.1f} blocks/s")
+        graph = {"steps": args.graph_steps, "ms_per_step": round(ms_g, 4), "blocks_per_s": round(B * 1000.0 / ms_g, 2),
+                 "what": "inject, draft, greedy path and verify captured once in a HIP graph, replayed"}
+        del g
+
     sampled = None
     if args.sampled_steps > 0:
         temp = 0.8
@@ -662,6 +691,8 @@ def main():
         "breakdown": breakdown,
         "cpu_baseline": cpu,
     }
+    if graph is not None:
+        out["graph"] = graph
     if sampled is not None:
         out["sampled"] = sampled
     if fp8 is not None:
