@@ -1002,8 +1002,22 @@ __global__ __launch_bounds__(256) void gemm_splitk_direct_kernel(const float* __
   const int pcol = ((vt ^ Epi::PX) << 4) | (c ^ Epi::PC);
   const size_t zs = static_cast<size_t>(M) * ldp;
   const float* p = partial + static_cast<size_t>(m) * ldp;
+  // every partial's load issued before the first add (one memory round trip, not ks)
+  float pz[8], qz[8];
+#pragma unroll
+  for (int z = 0; z < 8; ++z) {
+    pz[z] = z < ks ? p[z * zs + col] : 0.f;
+    qz[z] = (Epi::PX || Epi::PC) && z < ks ? p[z * zs + pcol] : 0.f;
+  }
   float v = 0.f, pv = 0.f;
-  for (int z = 0; z < ks; ++z) {
+#pragma unroll
+  for (int z = 0; z < 8; ++z) {
+    if (z < ks) {
+      v += pz[z];
+      pv += qz[z];
+    }
+  }
+  for (int z = 8; z < ks; ++z) {
     v += p[z * zs + col];
     if (Epi::PX || Epi::PC) pv += p[z * zs + pcol];
   }
