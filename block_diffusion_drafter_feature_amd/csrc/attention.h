@@ -29,9 +29,9 @@
 //   O^T[dim, q] += V^T P^T: A = V^T (8 consecutive keys per lane), B = P^T straight
 //     from the S^T registers.
 // Online softmax in base 2 with a per-query reference point and running sum; the reference
-// moves only when a score passes it by more than 2^8, so the running output is rarely rescaled.  With S == 1 the kernel
-// writes the normalised output; otherwise each split writes (O, m, l) partials that
-// attn_combine_kernel merges in split order (deterministic).
+// moves only when a score passes it by more than 2^8, so the running output is rarely
+// rescaled.  With S == 1 the kernel writes the normalised output; otherwise each split
+// writes (O, m, l) partials that attn_combine_kernel merges in split order (deterministic).
 #pragma once
 
 #include "common.h"
