@@ -233,6 +233,34 @@ def test_draft_top16_over_group_maxima(batch, vocab, period):
         H.assert_close_rows(f"logits b{b}", lg[b], outs[b]["logits"], H.tol(dims))
 
 
+def test_draft_parity_256_rows():
+    """Sixteen drafted blocks (256 rows: the pipelined GEMM's 256-row tiles on every
+    projection) with the dynamic short conv and the context gate, ragged contexts including
+    an empty one; every sequence against the oracle."""
+    base = synth.workload("t_conv")
+    dims = base.dims
+    B = 16
+    ctx = tuple((37 * i + 5) % 260 if i else 0 for i in range(B))
+    cap = ((max(ctx) + 16 + 31) // 32) * 32
+    say(f"draft 256 rows (t_conv dims): contexts {list(ctx)}")
+    W = synth.make_weights(dims, base.seed + 3, conv_scale="stress")
+    K, V = synth.make_cache(dims, ctx, cap, base.seed + 4)
+    ids = synth.make_block_ids(dims, B, base.seed + 5, 1)
+    dr = D.Drafter(dims, W)
+    cache = D.KVCache(dims, B, cap)
+    cache.load_logical(K, V)
+    ci, cl, fh, lg = run_draft(dims, dr, cache, ctx, ids)
+    outs = H.oracle_draft(oracle.Model(dims, W), K, V, ctx, ids)
+    t = H.tol(dims)
+    near = 0
+    for b, o in enumerate(outs):
+        H.assert_close_rows(f"logits b{b}", lg[b], o["logits"], t)
+        H.assert_close_rows(f"final hidden b{b}", fh[b], o["xhat"], t)
+        np.testing.assert_array_equal(ci[b], H.exact_topk_of(lg[b]))
+        near += H.topk_with_margin(ci[b], o["logits"], lg[b])
+    say(f"  near-tie top-16 swaps: {near}")
+
+
 def test_draft_long_context():
     """Contexts long enough for many 32-key slabs per attention split (and ragged ends)."""
     say("draft long context t_hd128")
