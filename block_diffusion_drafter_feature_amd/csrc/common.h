@@ -219,6 +219,18 @@ __device__ __forceinline__ float wave_max(float v) {
   return max_lane_groups(v);
 }
 
+// maximum over each aligned group of N lanes (N <= 16, within a DPP row); every lane of a
+// group ends with its group's maximum
+template <int N>
+__device__ __forceinline__ float group_max(float v) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8 || N == 16, "groups of 1..16 lanes");
+  if constexpr (N >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+  if constexpr (N >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+  if constexpr (N >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+  if constexpr (N >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+
 // deterministic block-wide sum (fixed reduction tree); `red` holds >= nwaves floats
 __device__ __forceinline__ float block_sum(float v, float* red) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = (blockDim.x + 63) >> 6;

@@ -958,7 +958,26 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
     if constexpr (HasRope<Epi>::value) {
       if (static_cast<size_t>(EPR) * epi.rope_pairs() * sizeof(float2) <= STAGE * sizeof(T)) trig = reinterpret_cast<float2*>(s1);
     }
-    if constexpr (kRows) {
+    if constexpr (HasTileMax<Epi>::value) {
+      // the LM head's plain fp32 rows: four columns per thread, one 16-byte store each
+      const int ncol = epi.w.off[epi.w.n_seg], n0 = vt0 * 16;
+      const bool vec = epi.ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(epi.out) & 15) == 0;
+      constexpr int C4 = BN / 4;
+#pragma unroll
+      for (int e0 = 0; e0 < EPR * C4; e0 += 64 * NWV) {
+        const int e = e0 + tid, r = e / C4, c = (e % C4) * 4, m = m0 + h * EPR + r, n = n0 + c;
+        if (e >= EPR * C4 || m >= M) continue;
+        const float* sp = Ct + r * (BN + 1) + c;
+        float* o = epi.out + static_cast<size_t>(m) * epi.ldo + n;
+        if (vec && n + 4 <= ncol) {
+          *reinterpret_cast<f32x4_t*>(o) = f32x4_t{sp[0], sp[1], sp[2], sp[3]};
+        } else {
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+            if (n + k < ncol) o[k] = sp[k];
+        }
+      }
+    } else if constexpr (kRows) {
       epilogue_tile<Epi, true, 64 * NWV>(epi, Ct, BN + 1, m0 + h * EPR, EPR, vt0, BN / 16, M, rows_all + h * EPR, cols, trig);
     } else {
       __shared__ typename Epi::Row rinfo[EPR];
@@ -967,7 +986,7 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
     if constexpr (HasTileMax<Epi>::value) {
       // each row's maximum over every 128-column group of the tile (past the vocabulary:
       // excluded; groups wholly past it are not written); 64 * NWV / EPR threads per row,
-      // TPG of them per group, fixed shuffle tree
+      // TPG of them per group (consecutive lanes, reduced by lane permutations)
       constexpr int TPR = 64 * NWV / EPR, CPT = BN / TPR, NGR = BN / 128, TPG = TPR / NGR;
       static_assert(BN % 128 == 0 && TPR <= 64 && (TPR & (TPR - 1)) == 0 && CPT * TPR == BN && TPG * NGR == TPR,
                     "row max layout");
@@ -979,8 +998,12 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
           const int col = q * CPT + k;
           if (vt0 * 16 + col < ncol) mx = fmaxf(mx, Ct[r * (BN + 1) + col]);
         }
+        if constexpr (TPG <= 16) {
+          mx = group_max<TPG>(mx);
+        } else {
 #pragma unroll
-        for (int o = 1; o < TPG; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+          for (int o = 1; o < TPG; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        }
         const int m = m0 + h * EPR + r, grp = vt0 / 8 + q / TPG;
         if (q % TPG == 0 && m < M && grp < ngr) epi.tmax[static_cast<size_t>(m) * ngr + grp] = mx;
       }
