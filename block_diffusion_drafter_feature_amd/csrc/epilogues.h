@@ -90,6 +90,39 @@ struct EpiStore {
     else if (mode == SILU) *o = v / (1.f + expf(-v));
     else *o = v;
   }
+  // four consecutive columns n..n+3 of row m at once (the staged epilogues), the same values
+  // as apply() column by column; ncol = w.off[w.n_seg] and vec (one 16-byte access: the
+  // four columns exist, ldo % 4 == 0, out 16-byte aligned) worked out by the caller
+  static constexpr bool kApply4 = true;
+  __device__ __forceinline__ void apply4(int m, int n, const float* v, bool vec, int ncol) const {
+    float* o = out + static_cast<size_t>(m) * ldo + n;
+    if (mode == STORE) {   // (uniform) the plain store: no transform to evaluate
+      if (vec) {
+        *reinterpret_cast<f32x4_t*>(o) = f32x4_t{v[0], v[1], v[2], v[3]};
+      } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (n + k < ncol) o[k] = v[k];
+      }
+      return;
+    }
+    float r[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (mode == SIGMOID) r[k] = 1.f / (1.f + expf(-v[k]));
+      else if (mode == SILU) r[k] = v[k] / (1.f + expf(-v[k]));
+      else r[k] = v[k];
+    }
+    if (vec) {
+      f32x4_t x = f32x4_t{r[0], r[1], r[2], r[3]};
+      if (mode == ADD) x += *reinterpret_cast<const f32x4_t*>(o);
+      *reinterpret_cast<f32x4_t*>(o) = x;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (n + k < ncol) o[k] = mode == ADD ? o[k] + r[k] : r[k];
+    }
+  }
 };
 
 // LM-head logits: a plain fp32 store, kept as its own type so that the LM-head GEMM is a
@@ -456,6 +489,24 @@ struct EpiSwiGLU {
     if (n >= Fd) return;
     const float s = v / (1.f + expf(-v));
     h[static_cast<size_t>(m) * Fd + n] = from_f<T>(s * pv);
+  }
+  // four consecutive outputs n..n+3 of row m from their gate and up sums (the staged
+  // epilogues): one 8-byte store where the row allows it, the same values as apply()
+  static constexpr bool kPair4 = true;
+  __device__ __forceinline__ void apply_pair4(int m, int n, const float* g, const float* u) const {
+    float o[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) o[k] = g[k] / (1.f + expf(-g[k])) * u[k];
+    T* p = h + static_cast<size_t>(m) * Fd + n;
+    if (sizeof(T) == 2 && n + 4 <= Fd && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+      const uint2 w = {static_cast<uint32_t>(from_f<T>(o[0])) | (static_cast<uint32_t>(from_f<T>(o[1])) << 16),
+                       static_cast<uint32_t>(from_f<T>(o[2])) | (static_cast<uint32_t>(from_f<T>(o[3])) << 16)};
+      *reinterpret_cast<uint2*>(p) = w;
+    } else {
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        if (n + k < Fd) p[k] = from_f<T>(o[k]);
+    }
   }
 };
 

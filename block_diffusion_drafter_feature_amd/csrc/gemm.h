@@ -754,6 +754,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const AS* __restrict__ 
 // position c ^ ((r >> 1) & 7), so the 16 rows of a fragment read hit 16 distinct bank
 // groups.  A wave's direct load writes 1 KB = 8 rows; lane l fetches the chunk that
 // belongs at position l & 7 of row l >> 3.
+// epilogues with a four-column store (plain rows) or a four-output gate/up pair store
+template <class Epi, class = void>
+struct HasApply4 : std::false_type {};
+template <class Epi>
+struct HasApply4<Epi, std::void_t<decltype(Epi::kApply4)>> : std::integral_constant<bool, Epi::kApply4> {};
+template <class Epi, class = void>
+struct HasPair4 : std::false_type {};
+template <class Epi>
+struct HasPair4<Epi, std::void_t<decltype(Epi::kPair4)>> : std::integral_constant<bool, Epi::kPair4> {};
+
 template <typename T, int STAGE, int I>
 __device__ __forceinline__ T* pipe_slot() {
   __shared__ __attribute__((aligned(16))) T s[STAGE];
@@ -975,6 +985,27 @@ __global__ __launch_bounds__(64 * NWV) void gemm_pipe_kernel(const T* __restrict
 #pragma unroll
           for (int k = 0; k < 4; ++k)
             if (n + k < ncol) o[k] = sp[k];
+        }
+      }
+    } else if constexpr (HasApply4<Epi>::value) {
+      // plain fp32 rows (EpiStore): four columns per thread
+      const int ncol = epi.w.off[epi.w.n_seg];
+      const bool v4 = epi.ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(epi.out) & 15) == 0;
+#pragma unroll
+      for (int e0 = 0; e0 < EPR * (BN / 4); e0 += 64 * NWV) {
+        const int e = e0 + tid, r = e / (BN / 4), c = (e % (BN / 4)) * 4, m = m0 + h * EPR + r, n = vt0 * 16 + c;
+        if (e < EPR * (BN / 4) && m < M) epi.apply4(m, n, Ct + r * (BN + 1) + c, v4 && n + 4 <= ncol, ncol);
+      }
+    } else if constexpr (HasPair4<Epi>::value) {
+      // SwiGLU: a tile holds gate/up vtile pairs (columns 32j..32j+15 and 32j+16..32j+31);
+      // four consecutive outputs per thread
+#pragma unroll
+      for (int e0 = 0; e0 < EPR * (BN / 8); e0 += 64 * NWV) {
+        const int e = e0 + tid, r = e / (BN / 8), q = e % (BN / 8), j = q >> 2, c = (q & 3) * 4;
+        const int m = m0 + h * EPR + r;
+        if (e < EPR * (BN / 8) && m < M) {
+          const float* g = Ct + r * (BN + 1) + 32 * j + c;
+          epi.apply_pair4(m, (vt0 >> 1) * 16 + 16 * j + c, g, g + 16);
         }
       }
     } else if constexpr (kRows) {
