@@ -1078,6 +1078,31 @@ __global__ __launch_bounds__(256) void gemm_splitk_direct_kernel(const float* __
   epi.apply(vt, m, epi.row(m), c, v, pv);
 }
 
+// The same for plain rows (Epi::kApply4): four columns per thread, 16-byte partial loads.
+template <class Epi>
+__global__ __launch_bounds__(256) void gemm_splitk_direct4_kernel(const float* __restrict__ partial, int M, int ldp,
+                                                                  int ks, Epi epi) {
+  const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x, l4 = static_cast<size_t>(ldp / 4);
+  if (e >= static_cast<size_t>(M) * l4) return;
+  const int m = static_cast<int>(e / l4), col = static_cast<int>(e % l4) * 4;
+  const int ncol = epi.w.off[epi.w.n_seg];
+  if (col >= ncol) return;
+  const size_t zs = static_cast<size_t>(M) * ldp;
+  const float* p = partial + static_cast<size_t>(m) * ldp + col;
+  f32x4_t pz[8];
+#pragma unroll
+  for (int z = 0; z < 8; ++z)
+    pz[z] = z < ks ? *reinterpret_cast<const f32x4_t*>(p + z * zs) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+  f32x4_t v = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int z = 0; z < 8; ++z)
+    if (z < ks) v += pz[z];
+  for (int z = 8; z < ks; ++z) v += *reinterpret_cast<const f32x4_t*>(p + z * zs);
+  const float vv[4] = {v[0], v[1], v[2], v[3]};
+  const bool vec = epi.ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(epi.out) & 15) == 0 && col + 4 <= ncol;
+  epi.apply4(m, col, vv, vec, ncol);
+}
+
 template <class Epi>
 static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks, int n_vtiles, const Epi& epi,
                                    hipStream_t s);
@@ -1243,7 +1268,10 @@ static hipError_t launch_skinny(const AS* A, int lda, const int32_t* arows, int 
 template <class Epi>
 static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks, int n_vtiles, const Epi& epi,
                                    hipStream_t s) {
-  if (Epi::kDirect) {
+  if constexpr (HasApply4<Epi>::value) {
+    const size_t n = static_cast<size_t>(M) * (ldp / 4);
+    gemm_splitk_direct4_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(partial, M, ldp, ks, epi);
+  } else if (Epi::kDirect) {
     const size_t n = static_cast<size_t>(M) * ldp;
     gemm_splitk_direct_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(partial, M, ldp, ks,
                                                                                         n_vtiles, epi);
