@@ -74,8 +74,20 @@ __device__ __forceinline__ void epilogue_tile(const Epi& epi, const float* Ct, i
         // dimensions, rotated against the other half) or a value tile's columns over 8
         // consecutive rows; each item is one 16-byte store
         const int ipt = 2 * rows, nhalf = rows / 8;
+        // rotated tiles of whole heads (groups of 8 vtiles): items in the order (group, row,
+        // half, vtile of the group), so 16 consecutive lanes write one row's 16 chunks of a
+        // head, 256 contiguous bytes; otherwise vtile by vtile
+        const bool byrow = nvt % 8 == 0 && epi.kind8(cols[0]) > 0;
         for (int it = tid; it < nvt * ipt; it += nth) {
-          const int v = it / ipt, sub = it - v * ipt;
+          int v, sub;
+          if (byrow) {
+            const int g8 = it / (8 * ipt), rem = it - g8 * 8 * ipt;
+            v = 8 * g8 + (rem & 7);
+            sub = rem >> 3;
+          } else {
+            v = it / ipt;
+            sub = it - v * ipt;
+          }
           const typename Epi::Col& cf = cols[v];
           const int kind = epi.kind8(cf);
           float o[8];
