@@ -1093,10 +1093,23 @@ __global__ __launch_bounds__(256) void gemm_splitk_direct_kernel(const float* __
 // The same for plain rows (Epi::kApply4): four columns per thread, 16-byte partial loads.
 template <class Epi>
 __global__ __launch_bounds__(256) void gemm_splitk_direct4_kernel(const float* __restrict__ partial, int M, int ldp,
-                                                                  int ks, Epi epi) {
-  const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x, l4 = static_cast<size_t>(ldp / 4);
-  if (e >= static_cast<size_t>(M) * l4) return;
-  const int m = static_cast<int>(e / l4), col = static_cast<int>(e % l4) * 4;
+                                                                  int ks, Epi epi, int xcd_nb) {
+  const size_t l4 = static_cast<size_t>(ldp / 4);
+  int m, col;
+  if (xcd_nb > 0) {
+    // the partials of 128-column block cb were written on XCD cb % 8: work-group w (XCD w % 8)
+    // takes 8 rows x 128 columns of such a block
+    const int w = blockIdx.x, x8 = w % 8, j = w / 8, per = xcd_nb / 8;
+    const int cb = x8 + 8 * (j % per), rg = j / per;
+    m = rg * 8 + (threadIdx.x >> 5);
+    col = cb * 128 + (threadIdx.x & 31) * 4;
+    if (m >= M) return;
+  } else {
+    const size_t e = static_cast<size_t>(blockIdx.x) * 256 + threadIdx.x;
+    if (e >= static_cast<size_t>(M) * l4) return;
+    m = static_cast<int>(e / l4);
+    col = static_cast<int>(e % l4) * 4;
+  }
   const int ncol = epi.w.off[epi.w.n_seg];
   if (col >= ncol) return;
   const size_t zs = static_cast<size_t>(M) * ldp;
@@ -1117,7 +1130,7 @@ __global__ __launch_bounds__(256) void gemm_splitk_direct4_kernel(const float* _
 
 template <class Epi>
 static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks, int n_vtiles, const Epi& epi,
-                                   hipStream_t s);
+                                   hipStream_t s, int xcd_nb = 0);
 
 // Split-K reduction: sum the partial tiles in z order into an LDS block of 16 rows x 64
 // columns (each thread four consecutive columns of one row: a wave reads four 256-byte row
@@ -1125,10 +1138,19 @@ static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks,
 // grid (ldp / 64, ceil(M / 16)), 256 threads.
 template <class Epi>
 __global__ __launch_bounds__(256) void gemm_splitk_epilogue_kernel(const float* __restrict__ partial, int M,
-                                                                   int ldp, int ks, int n_vtiles, Epi epi) {
+                                                                   int ldp, int ks, int n_vtiles, Epi epi,
+                                                                   int xcd_nb) {
   __shared__ float Ct[16 * 65];
   __shared__ typename Epi::Row rinfo[16];
-  const int c0 = blockIdx.x * 64, m0 = blockIdx.y * 16;
+  int c0 = blockIdx.x * 64, m0 = blockIdx.y * 16;
+  if (xcd_nb > 0) {
+    // the partials of 128-column block cb were written on XCD cb % 8: the work-group of
+    // dispatch index w (XCD w % 8) takes a 64-column half of such a block
+    const int w = blockIdx.y * gridDim.x + blockIdx.x, x8 = w % 8, j = w / 8, per = xcd_nb / 8;
+    const int cb = x8 + 8 * (j % per), half = (j / per) % 2;
+    c0 = (2 * cb + half) * 64;
+    m0 = (j / per / 2) * 16;
+  }
   const int r = threadIdx.x >> 4, cc = (threadIdx.x & 15) * 4;
   // the rows' and tiles' facts first: their loads overlap the partial loads below
   __shared__ typename ColOf<Epi>::type cols[HasCol<Epi>::value ? 4 : 1];
@@ -1279,16 +1301,22 @@ static hipError_t launch_skinny(const AS* A, int lda, const int32_t* arows, int 
 
 template <class Epi>
 static void launch_splitk_epilogue(const float* partial, int M, int ldp, int ks, int n_vtiles, const Epi& epi,
-                                   hipStream_t s) {
+                                   hipStream_t s, int xcd_nb) {
   if constexpr (HasApply4<Epi>::value) {
+    if (xcd_nb > 0) {
+      const unsigned nwg = static_cast<unsigned>(xcd_nb) * ((M + 7) / 8);
+      gemm_splitk_direct4_kernel<Epi><<<nwg, 256, 0, s>>>(partial, M, ldp, ks, epi, xcd_nb);
+      return;
+    }
     const size_t n = static_cast<size_t>(M) * (ldp / 4);
-    gemm_splitk_direct4_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(partial, M, ldp, ks, epi);
+    gemm_splitk_direct4_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(partial, M, ldp, ks, epi, 0);
   } else if (Epi::kDirect) {
     const size_t n = static_cast<size_t>(M) * ldp;
     gemm_splitk_direct_kernel<Epi><<<static_cast<unsigned>((n + 255) / 256), 256, 0, s>>>(partial, M, ldp, ks,
                                                                                         n_vtiles, epi);
   } else {
-    gemm_splitk_epilogue_kernel<Epi><<<dim3(ldp / 64, (M + 15) / 16), 256, 0, s>>>(partial, M, ldp, ks, n_vtiles, epi);
+    gemm_splitk_epilogue_kernel<Epi><<<dim3(ldp / 64, (M + 15) / 16), 256, 0, s>>>(partial, M, ldp, ks, n_vtiles, epi,
+                                                                                  xcd_nb);
   }
 }
 
@@ -1298,7 +1326,9 @@ static hipError_t launch_pipe_shape(const T* A, int lda, const int32_t* arows, i
   const int tm = (M + BM - 1) / BM, tn = (n_vtiles * 16 + BN - 1) / BN, ldp = tn * BN;
   gemm_pipe_kernel<T, BM, BN, NS, Epi, W8, NWV><<<dim3(tm * tn, ks), 64 * NWV, 0, s>>>(
       A, lda, arows, M, K, epi, tm, K / ks, ks > 1 ? scratch : nullptr, ldp);
-  if (ks > 1) launch_splitk_epilogue(scratch, M, ldp, ks, n_vtiles, epi, s);
+  // one row tile of 128-column tiles, dealt to the XCDs round-robin: tile nt's partials on XCD nt % 8
+  const int xcd_nb = BN == 128 && tm == 1 && tn % 8 == 0 ? tn : 0;
+  if (ks > 1) launch_splitk_epilogue(scratch, M, ldp, ks, n_vtiles, epi, s, xcd_nb);
   return hipGetLastError();
 }
 
