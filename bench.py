@@ -453,6 +453,7 @@ def main():
         try:
             import hashlib
             tr = json.load(open(tpath))
+            tr = tr.get(dominant, tr)   # one entry per kernel, or a single kernel's entry
             src = hashlib.sha256(open(os.path.join(ROOT, "block_diffusion_drafter_feature_amd", "csrc",
                                                    tr["source"]), "rb").read()).hexdigest()
             if tr.get("kernel") == dominant and tr.get("source_sha256") == src:
