@@ -151,6 +151,45 @@ def test_inject_row_counts(rows):
         H.assert_close_rows(f"V l{l}", Vg.float().cpu().numpy()[0][:, pos].transpose(1, 0, 2), Vo[l], H.tol(dims))
 
 
+_C2 = {}
+
+
+@pytest.mark.parametrize("rows", [80, 100, 200, 256])
+def test_inject_row_counts_full_width(rows):
+    """The injection at the full model width (d 4096, five 4096-wide target layers): 80 and 100
+    rows take one 128-row tile, 256 rows one 256-row tile, and both GEMMs split K, so their
+    reductions run over one row tile of 128-column tiles (100 rows: a ragged last row group);
+    200 rows take two 128-row tiles."""
+    say(f"inject full width rows={rows}")
+    if not _C2:
+        wl = synth.workload("c2")
+        _C2["wl"] = wl
+        _C2["W"] = synth.make_weights(wl.dims, wl.seed)
+    wl, W = _C2["wl"], _C2["W"]
+    dims = wl.dims
+    m = oracle.Model(dims, W)
+    dr = D.Drafter(dims, W)
+    cap = ((rows + 31) // 32) * 32 + 32
+    hidden = synth.make_hidden(dims, rows, wl.seed + rows)
+    cache = D.KVCache(dims, 1, cap, fill=float("nan"))
+    nb = D.dflash_inject_workspace_bytes(dr.cfg, rows)
+    D.dflash_inject_context(dr.cfg, dr.w, cache.kv, D.to_device(hidden, dims), rows, dev_i32([0, rows]),
+                            dev_i32([7]), dev_i32([rows]), 1, ws_of(nb), nb)
+    torch.cuda.synchronize()
+    pos = 7 + np.arange(rows)
+    _, Ko, Vo = oracle.inject_rows(m, hidden, pos)
+    for l in range(dims.n_layers):
+        Kg, Vg = cache.logical(l)
+        Kg = Kg.float().cpu().numpy()[0]
+        Vg = Vg.float().cpu().numpy()[0]
+        H.assert_close_rows(f"K l{l}", Kg[:, pos].transpose(1, 0, 2), Ko[l], H.tol(dims))
+        H.assert_close_rows(f"V l{l}", Vg[:, pos].transpose(1, 0, 2), Vo[l], H.tol(dims))
+        # rows outside the written range keep the NaN fill
+        keep = np.ones(cap, dtype=bool)
+        keep[pos] = False
+        assert np.isnan(Kg[:, keep]).all() and np.isnan(Vg[:, keep]).all(), f"layer {l}: a row outside was written"
+
+
 # ------------------------------------------------------------------ drafter forward
 
 DRAFT_CASES = ["c1", "t_small", "t_conv", "t_hd128", "t_f32", "t_batch"]
