@@ -3,7 +3,8 @@
 A serving loop captures inject -> draft -> path -> verify once and replays it.  The four
 calls allocate nothing, synchronise nothing and record no memory fills, so the captured
 step must equal the eager one bit for bit on every replay (each replay re-injects the same
-verified rows, so the cache state does not drift).  Replays are interleaved with eager work
+verified rows, so the cache state does not drift; the target logits favour a seeded prefix of
+the drafted path, so the accepted lengths vary).  Replays are interleaved with eager work
 and synchronisations, and every output is cleared between them."""
 import sys
 
@@ -32,7 +33,7 @@ def ws_of(nbytes):
     return torch.empty(max(nbytes, 256), dtype=torch.uint8, device="cuda")
 
 
-@pytest.mark.parametrize("name", ["t_conv", "t_small", "c1"])
+@pytest.mark.parametrize("name", ["t_conv", "t_small", "c1", "c2"])
 def test_step_graph_replays(name):
     wl = synth.workload(name)
     dims = wl.dims
@@ -92,6 +93,12 @@ def test_step_graph_replays(name):
             snap[f"vt{l}"] = cache.vt[l].clone()
         return snap
 
+    step()
+    # the target then favours a seeded prefix of the drafted path, so verification accepts a
+    # seeded number of drafts (the same in every replay: the path does not change)
+    torch.cuda.synchronize()
+    Tp = synth.make_target_logits(dims, B, P, wl.seed, planted="prefix", draft=out["pids"].cpu().numpy(), boost=8.0)
+    T.copy_(D.to_device(Tp, dims))
     step()
     ref = snapshot()
     g = torch.cuda.CUDAGraph()
