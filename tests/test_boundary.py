@@ -3,6 +3,7 @@ arguments before anything reaches the GPU (no compute calls are made here)."""
 import ctypes
 import os
 import re
+import sys
 
 import pytest
 
@@ -244,3 +245,15 @@ def test_calibrate_arguments():
     w.cal_w1 = w.cal_w2 = FAKE
     assert _status(D.dflash_calibrate, cfg, w, FAKE, FAKE, 2, FAKE, FAKE, FAKE, FAKE, nb - 1, 1) == D.DFLASH_E_WORKSPACE
     assert _status(D.dflash_calibrate, cfg, w, FAKE, None, 2, FAKE, FAKE, FAKE, FAKE, nb, 1) == D.DFLASH_E_INVAL
+
+
+def test_bench_refuses_more_than_one_gpu():
+    """The benchmark measures one GPU: any other --gpus value ends with a message and a nonzero
+    status before anything touches a device."""
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for n in (2, 8):
+        p = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", str(n)],
+                           capture_output=True, text=True, timeout=120, cwd=root)
+        assert p.returncode != 0, n
+        assert "one GPU only" in p.stderr and p.stdout.strip() == "", (n, p.stderr, p.stdout)
